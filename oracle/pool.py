@@ -1,0 +1,211 @@
+"""O-B: paged KV pool with block tables — oracle side.
+
+Follows the paged KV managers on the pages:
+  * paurushmuley.com, diagram "PagedAttention virtual memory manager" and the
+    PagedKVCacheManager listing: logical blocks of 16 tokens map to
+    non-contiguous physical blocks; a shared prefix maps the same physical
+    blocks with reference count N; a block with reference count > 1 is copied
+    before a write (copy-on-write); releasing a session drops a reference and
+    frees a block at zero; exhaustion is an error.
+  * innvotechnologies.co, TypeScript PagedKVCacheManager.allocateBlocks:
+    first-fit over the block list; "Memory Exhausted" error.
+  * innvotechnologies.co, pipeline diagram: accepted tokens are committed to
+    the block table, rejected ones discarded (rollback).
+  * futurestack.online, section 2.3 note: the bundle extension is atomic.
+
+Readings where the pages are silent or disagree:
+  * free pages are kept in a set ordered by a rank (the position of the page
+    in a given free order, or its id when none is given); an allocation takes
+    the free page of lowest rank ("first fit" generalised to a shuffled list);
+  * an append is all-or-nothing: it first counts the pages it needs (CoW copy
+    of a shared, partly filled tail page, then one page per new 16-token
+    block) and fails without any change if the pool has fewer free pages;
+  * a shared prefix of n tokens maps ceil(n / S) of the source's pages; a
+    partly valid last shared page is CoW-copied on the first append;
+  * rollback by n truncates the length; pages wholly past the new length lose
+    a reference (freed at zero); no data moves;
+  * FP8 pools quantise on append (see oracle.fp8 for the scale rule).
+
+The model stores page contents in a plain [page][head][slot][dim] array (its
+own layout), so gathering a sequence back to contiguous K/V is a loop over the
+block table.
+"""
+import numpy as np
+
+from . import fp8
+
+
+class OutOfPages(Exception):
+    pass
+
+
+class UnknownSeq(Exception):
+    pass
+
+
+class PoolModel:
+    def __init__(self, num_pages, page_size, num_kv_heads, head_dim, kv_dtype="f64",
+                 free_order=None):
+        self.P, self.S, self.H, self.d = num_pages, page_size, num_kv_heads, head_dim
+        self.fp8 = kv_dtype == "fp8"
+        if free_order is None:
+            free_order = np.arange(num_pages)
+        free_order = [int(p) for p in free_order]
+        assert sorted(free_order) == list(range(num_pages)), "free order must be a permutation"
+        self.rank = {p: r for r, p in enumerate(free_order)}
+        self.free = set(range(num_pages))
+        self.refcount = [0] * num_pages
+        self.tables = {}      # seq -> list of page ids
+        self.lens = {}        # seq -> length in tokens
+        self.cow_copies = 0
+        if self.fp8:
+            self.kc = np.zeros((num_pages, self.H, self.S, self.d), dtype=np.uint8)
+            self.vc = np.zeros_like(self.kc)
+            self.ks = np.ones((num_pages, self.H), dtype=np.float32)
+            self.vs = np.ones((num_pages, self.H), dtype=np.float32)
+        else:
+            self.k = np.full((num_pages, self.H, self.S, self.d), np.nan)
+            self.v = np.full((num_pages, self.H, self.S, self.d), np.nan)
+
+    # -- free set --------------------------------------------------------------
+    def _take(self):
+        p = min(self.free, key=self.rank.__getitem__)
+        self.free.remove(p)
+        self.refcount[p] = 1
+        return p
+
+    def _unref(self, p):
+        self.refcount[p] -= 1
+        assert self.refcount[p] >= 0
+        if self.refcount[p] == 0:
+            self.free.add(p)
+
+    # -- sequence operations ---------------------------------------------------
+    def alloc(self, seq, share_from=None, n_shared=0):
+        if seq in self.tables:
+            raise ValueError("sequence exists")
+        table = []
+        if share_from is not None:
+            if share_from not in self.tables:
+                raise UnknownSeq(share_from)
+            if n_shared > self.lens[share_from]:
+                raise ValueError("shared prefix longer than source")
+            for p in self.tables[share_from][: -(-n_shared // self.S)]:
+                self.refcount[p] += 1
+                table.append(p)
+        else:
+            n_shared = 0
+        self.tables[seq] = table
+        self.lens[seq] = n_shared
+
+    def pages_needed(self, seq, n):
+        L, table = self.lens[seq], self.tables[seq]
+        need = 0
+        if n > 0 and L % self.S and self.refcount[table[L // self.S]] > 1:
+            need += 1                               # copy-on-write of the tail
+        need += -(-(L + n) // self.S) - len(table)   # whole new blocks
+        return need
+
+    def append(self, seq, k_new, v_new):
+        """k_new, v_new: [n, Hkv, d].  Float pools take fp64 values; FP8 pools
+        take the fp32 values to quantise."""
+        if seq not in self.tables:
+            raise UnknownSeq(seq)
+        n = len(k_new)
+        if n == 0:
+            return
+        if self.pages_needed(seq, n) > len(self.free):
+            raise OutOfPages(seq)
+        L, table = self.lens[seq], self.tables[seq]
+        fresh = set()
+        if L % self.S and self.refcount[table[L // self.S]] > 1:
+            old = table[L // self.S]
+            new = self._take()
+            self._copy_page(old, new)
+            self._unref(old)
+            table[L // self.S] = new
+            self.cow_copies += 1
+        while len(table) < -(-(L + n) // self.S):
+            p = self._take()
+            table.append(p)
+            fresh.add(p)
+        # write token by token, grouping per page for the FP8 scale rule
+        for blk in range(L // self.S, -(-(L + n) // self.S)):
+            p = table[blk]
+            t0 = max(L, blk * self.S)
+            t1 = min(L + n, (blk + 1) * self.S)
+            slots = np.arange(t0, t1) - blk * self.S
+            src = slice(t0 - L, t1 - L)
+            if self.fp8:
+                kx = np.asarray(k_new[src], dtype=np.float32)
+                vx = np.asarray(v_new[src], dtype=np.float32)
+                for h in range(self.H):
+                    if p in fresh:
+                        self.ks[p, h] = fp8.page_scale(kx[:, h])
+                        self.vs[p, h] = fp8.page_scale(vx[:, h])
+                    self.kc[p, h, slots] = fp8.quantise(kx[:, h], self.ks[p, h])
+                    self.vc[p, h, slots] = fp8.quantise(vx[:, h], self.vs[p, h])
+            else:
+                for h in range(self.H):
+                    self.k[p, h, slots] = np.asarray(k_new[src, h], dtype=np.float64)
+                    self.v[p, h, slots] = np.asarray(v_new[src, h], dtype=np.float64)
+        self.lens[seq] = L + n
+
+    def _copy_page(self, src, dst):
+        if self.fp8:
+            self.kc[dst] = self.kc[src]
+            self.vc[dst] = self.vc[src]
+            self.ks[dst] = self.ks[src]
+            self.vs[dst] = self.vs[src]
+        else:
+            self.k[dst] = self.k[src]
+            self.v[dst] = self.v[src]
+
+    def rollback(self, seq, n):
+        if seq not in self.tables:
+            raise UnknownSeq(seq)
+        L = self.lens[seq]
+        if n < 0 or n > L:
+            raise ValueError("rollback beyond length")
+        keep = -(-(L - n) // self.S)
+        table = self.tables[seq]
+        for p in table[keep:]:
+            self._unref(p)
+        del table[keep:]
+        self.lens[seq] = L - n
+
+    def release(self, seq):
+        if seq not in self.tables:
+            raise UnknownSeq(seq)
+        for p in self.tables.pop(seq):
+            self._unref(p)
+        del self.lens[seq]
+
+    # -- views -----------------------------------------------------------------
+    def gather(self, seq):
+        """Contiguous fp64 K, V [N, Hkv, d] of a sequence, read through its
+        block table (with FP8 codes decoded and multiplied by their scale)."""
+        L, table = self.lens[seq], self.tables[seq]
+        K = np.empty((L, self.H, self.d))
+        V = np.empty((L, self.H, self.d))
+        for t in range(L):
+            p, o = table[t // self.S], t % self.S
+            if self.fp8:
+                K[t] = fp8.decode(self.kc[p, :, o]) * self.ks[p][:, None].astype(np.float64)
+                V[t] = fp8.decode(self.vc[p, :, o]) * self.vs[p][:, None].astype(np.float64)
+            else:
+                K[t] = self.k[p, :, o]
+                V[t] = self.v[p, :, o]
+        return K, V
+
+    def check_invariants(self):
+        refs = [0] * self.P
+        for table in self.tables.values():
+            for p in table:
+                refs[p] += 1
+        assert refs == self.refcount, "refcount != number of references"
+        used = {p for p in range(self.P) if refs[p] > 0}
+        assert used.isdisjoint(self.free), "page both used and free"
+        assert used | self.free == set(range(self.P)), "page lost"
+        for seq, table in self.tables.items():
+            assert len(table) == -(-self.lens[seq] // self.S), "table length"

@@ -1,0 +1,163 @@
+"""Pins for oracle.pool (O-B): invariants, a contiguous model, worked examples."""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import fp8
+from oracle.pool import OutOfPages, PoolModel
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "fragmentation_worked_example.txt")
+
+
+def _state(p):
+    return (dict((k, list(v)) for k, v in p.tables.items()), dict(p.lens), set(p.free),
+            list(p.refcount))
+
+
+def test_random_ops_match_contiguous_model():
+    rng = np.random.default_rng(0)
+    H, d, S = 2, 4, 4
+    pool = PoolModel(40, S, H, d, free_order=rng.permutation(40))
+    model = {}                     # seq -> list of (k, v) token arrays
+    next_id = 0
+    for step in range(600):
+        op = rng.integers(0, 5)
+        seqs = list(model)
+        try:
+            if op == 0 or not seqs:
+                src = seqs[rng.integers(len(seqs))] if seqs and rng.random() < 0.5 else None
+                n_sh = int(rng.integers(0, len(model[src]) + 1)) if src is not None else 0
+                pool.alloc(next_id, src, n_sh)
+                model[next_id] = list(model[src][:n_sh]) if src is not None else []
+                next_id += 1
+            elif op in (1, 2):
+                s = seqs[rng.integers(len(seqs))]
+                n = int(rng.integers(0, 9))
+                k = rng.standard_normal((n, H, d))
+                v = rng.standard_normal((n, H, d))
+                before = _state(pool)
+                try:
+                    pool.append(s, k, v)
+                    model[s] += [(k[i], v[i]) for i in range(n)]
+                except OutOfPages:
+                    assert _state(pool) == before
+            elif op == 3:
+                s = seqs[rng.integers(len(seqs))]
+                n = int(rng.integers(0, len(model[s]) + 1))
+                pool.rollback(s, n)
+                model[s] = model[s][:len(model[s]) - n]
+            else:
+                s = seqs[rng.integers(len(seqs))]
+                pool.release(s)
+                del model[s]
+        except OutOfPages:
+            pass
+        pool.check_invariants()
+        for s, toks in model.items():
+            K, V = pool.gather(s)
+            assert K.shape[0] == len(toks)
+            for t, (kt, vt) in enumerate(toks):
+                assert np.array_equal(K[t], kt) and np.array_equal(V[t], vt)
+
+
+def test_rollback_equals_never_appended():
+    rng = np.random.default_rng(1)
+    p = PoolModel(30, 16, 1, 4, free_order=rng.permutation(30))
+    p.alloc(0)
+    p.append(0, rng.standard_normal((37, 1, 4)), rng.standard_normal((37, 1, 4)))
+    before = _state(p)
+    K0, V0 = p.gather(0)
+    for m in (1, 5, 11, 12, 27, 40):
+        p.append(0, rng.standard_normal((m, 1, 4)), rng.standard_normal((m, 1, 4)))
+        p.rollback(0, m)
+        assert _state(p) == before
+        K1, V1 = p.gather(0)
+        assert np.array_equal(K0, K1) and np.array_equal(V0, V1)
+
+
+def test_first_fit_by_rank():
+    order = [5, 2, 7, 0, 1, 3, 4, 6]
+    p = PoolModel(8, 4, 1, 1, free_order=order)
+    p.alloc("a")
+    p.append("a", np.zeros((9, 1, 1)), np.zeros((9, 1, 1)))
+    assert p.tables["a"] == [5, 2, 7]
+    p.alloc("b")
+    p.append("b", np.zeros((4, 1, 1)), np.zeros((4, 1, 1)))
+    assert p.tables["b"] == [0]
+    p.release("a")
+    p.append("b", np.zeros((5, 1, 1)), np.zeros((5, 1, 1)))
+    assert p.tables["b"] == [0, 5, 2]          # lowest ranks first again
+
+
+def test_shared_prefix_and_cow():
+    p = PoolModel(64, 16, 1, 2)
+    p.alloc(0)
+    p.append(0, np.ones((800 // 16 * 16, 1, 2)), np.ones((800, 1, 2)))
+    for s in range(1, 6):
+        p.alloc(s, 0, 800)
+    assert len(p.free) == 64 - 50                           # prefix stored once
+    assert all(p.refcount[x] == 6 for x in p.tables[0])
+    # a 40-token partly-valid shared page is copied on the first append
+    p2 = PoolModel(16, 16, 1, 2)
+    p2.alloc(0)
+    p2.append(0, np.arange(48.).reshape(24, 1, 2), np.arange(48.).reshape(24, 1, 2))
+    p2.alloc(1, 0, 20)
+    assert p2.tables[1] == p2.tables[0][:2]
+    p2.append(1, np.full((3, 1, 2), -1.), np.full((3, 1, 2), -1.))
+    assert p2.cow_copies == 1
+    assert p2.tables[1][0] == p2.tables[0][0] and p2.tables[1][1] != p2.tables[0][1]
+    K0, _ = p2.gather(0)
+    K1, _ = p2.gather(1)
+    assert np.array_equal(K1[:20], K0[:20]) and np.all(K1[20:] == -1)
+    assert np.array_equal(K0[20:], np.arange(40., 48.).reshape(4, 1, 2))
+    p2.check_invariants()
+
+
+def test_out_of_pages_is_atomic():
+    p = PoolModel(3, 4, 1, 1)
+    p.alloc(0)
+    p.append(0, np.zeros((10, 1, 1)), np.zeros((10, 1, 1)))
+    before = _state(p)
+    with pytest.raises(OutOfPages):
+        p.append(0, np.zeros((3, 1, 1)), np.zeros((3, 1, 1)))   # needs a 4th page
+    assert _state(p) == before
+    p.append(0, np.zeros((2, 1, 1)), np.zeros((2, 1, 1)))       # fits in the tail
+
+
+def test_fragmentation_worked_example():
+    rows = [l.split() for l in open(GOLDEN) if l.strip() and not l.startswith("#")]
+    reserved, used, used_pct, wasted, wasted_pct = map(float, rows[0])
+    S, bound = int(rows[1][0]), float(rows[1][1])
+    active = [1200, 4500, 800]
+    assert sum(active) == used and 3 * 8000 == reserved
+    assert round(100 * used / reserved, 2) == used_pct
+    assert round(100 * (reserved - used) / reserved, 2) == wasted_pct
+    p = PoolModel(1000, S, 1, 1)
+    for s, n in enumerate(active):
+        p.alloc(s)
+        p.append(s, np.zeros((n, 1, 1)), np.zeros((n, 1, 1)))
+    slots = (1000 - len(p.free)) * S
+    waste = 100 * (slots - used) / slots
+    assert waste < bound
+
+
+def test_fp8_pool_scale_rule_and_gather():
+    rng = np.random.default_rng(2)
+    p = PoolModel(8, 16, 2, 8, kv_dtype="fp8")
+    p.alloc(0)
+    k = rng.standard_normal((20, 2, 8)).astype(np.float32)
+    v = rng.standard_normal((20, 2, 8)).astype(np.float32)
+    p.append(0, k, v)
+    pg0, pg1 = p.tables[0]
+    for h in range(2):
+        assert p.ks[pg0, h] == fp8.page_scale(k[:16, h])
+        assert p.ks[pg1, h] == fp8.page_scale(k[16:, h])
+        assert p.vs[pg1, h] == fp8.page_scale(v[16:, h])
+    s_before = p.ks[pg1].copy()
+    p.append(0, 10 * k[:3], v[:3])                  # into the tail page: scale kept, saturates
+    assert np.array_equal(p.ks[pg1], s_before)
+    K, V = p.gather(0)
+    assert np.all(np.abs(K[20:]) <= 448 * s_before.max() * (1 + 1e-6))
+    rel = np.abs(K[:20] - k) / np.maximum(np.abs(k), 1e-3)
+    assert np.median(rel) < 0.05
