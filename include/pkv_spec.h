@@ -1,0 +1,283 @@
+/*
+ * pkv_spec.h — C ABI of the paged-KV speculative verification library
+ * (libpkvspec.so, HIP for AMD gfx950 / MI355X).
+ *
+ * The library implements one verification step of speculative decoding over a
+ * paged KV cache:
+ *
+ *   paged_kv_alloc / paged_kv_append / paged_kv_rollback / paged_kv_release
+ *       a page pool with block tables, reference-counted shared prefixes,
+ *       copy-on-write and rollback of rejected drafts
+ *       (paurushmuley.com/blog/speculative-decoding-pagedattention-llm-serving-dotnet-10,
+ *        diagram "PagedAttention virtual memory manager" and the
+ *        PagedKVCacheManager listing; innvotechnologies.co/en/blog/low-latency-inference-decoding,
+ *        pipeline diagram "Commit to KV-cache block table / Discard invalid KV blocks");
+ *   spec_verify_attention
+ *       attention of the gamma+1 verification queries over the pages of each
+ *       sequence, with a causal-chain or draft-tree mask, bf16/fp32 or FP8 KV
+ *       (atozofsoftwareengineering.blog, eq. A_speculative and section
+ *        "Custom FP8 Quantized Memory Block Layout");
+ *   spec_accept
+ *       the acceptance rule alpha_i = min(1, P(x_i)/Q(x_i)), the accepted
+ *       length k and the next token (innvotechnologies.co, section
+ *        "Verification Acceptance Probabilities and Speedup Math").
+ *
+ * Conventions for every call
+ *   - Memory: every device buffer (pools, block table, lengths, queries,
+ *     outputs, workspaces) is allocated and owned by the caller.  The library
+ *     never allocates device memory; it owns only the host-side pool handle.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ *     stream).  Device work is enqueued asynchronously on it; host metadata is
+ *     updated synchronously before the call returns.
+ *   - Errors: a call either succeeds or returns a non-zero pkv_status with no
+ *     effect on host metadata and nothing enqueued.  Arguments are validated
+ *     before any work is enqueued; a failed kernel launch returns
+ *     PKV_ERR_DEVICE.  pkv_last_error() returns a message for the calling
+ *     thread's last failure.
+ *   - Threads: a pool handle serialises its calls with an internal mutex.
+ *   - Layout: all arrays are dense row-major; int32 page ids and lengths,
+ *     int64 sequence ids.
+ */
+#ifndef PKV_SPEC_H
+#define PKV_SPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,   /* bad pointer, size, shape or dtype combination   */
+  PKV_ERR_OUT_OF_PAGES = 2,  /* pool exhausted (the pages' OutOfMemory error)    */
+  PKV_ERR_UNKNOWN_SEQ = 3,   /* sequence id not allocated (KeyNotFound)          */
+  PKV_ERR_SEQ_EXISTS = 4,    /* sequence id already allocated                    */
+  PKV_ERR_UNSUPPORTED = 5,   /* valid but not implemented (e.g. head_dim 96)     */
+  PKV_ERR_DEVICE = 6,        /* HIP runtime / launch failure                     */
+  PKV_ERR_WORKSPACE = 7,     /* workspace missing or smaller than required       */
+  PKV_ERR_NO_SLOT = 8,       /* more live sequences than block-table rows        */
+  PKV_ERR_CAPACITY = 9       /* sequence longer than max_pages_per_seq pages     */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
+
+/* ------------------------------------------------------------------------ */
+/* Page pool                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Physical page layout.  A page holds page_size (= 16) tokens of one KV head;
+ * pools are [num_pages][num_kv_heads][page_bytes] for K and for V.  Inside a
+ * page the elements are tiled for the verification kernel's 16-byte loads:
+ *   K, bf16:  element (t, c) at  s*16*32 + t*32 + j*8 + i
+ *             where c = (head_dim/4)*j + 8*s + i,  j<4, i<8
+ *   K, fp8:   element (t, c) at  u*16*64 + t*64 + j*16 + r
+ *             where c = (head_dim/4)*j + 16*u + r, r<16
+ *   V, bf16:  element (t, c) at  ((c/2)*4 + t/4)*8 + (c%2)*4 + t%4
+ *   V, fp8:   element (t, c) at  ((c/4)*4 + t/4)*16 + (c%4)*4 + t%4
+ *   K, V fp32: element (t, c) at t*head_dim + c (plain)
+ * (t = slot in page, c = channel).  pkv_page_bytes() gives page_bytes.
+ * FP8 is OCP E4M3 ("e4m3fn") with one fp32 scale per (page, KV head) for K
+ * and one for V: value = decode(byte) * scale.
+ */
+typedef struct pkv_pool pkv_pool;
+
+typedef struct {
+  int32_t num_pages;          /* physical pages in the pool                      */
+  int32_t page_size;          /* tokens per page; must be 16                     */
+  int32_t num_kv_heads;       /* Hkv >= 1                                        */
+  int32_t head_dim;           /* 64 or 128                                       */
+  pkv_dtype kv_dtype;         /* PKV_F32, PKV_BF16 or PKV_FP8_E4M3               */
+  int32_t max_seqs;           /* rows of the device block table (live sequences) */
+  int32_t max_pages_per_seq;  /* columns of the device block table               */
+  void* k_pages;              /* device [num_pages][Hkv][page_bytes]             */
+  void* v_pages;              /* device, same shape                              */
+  float* k_scale;             /* device [num_pages][Hkv], FP8 only, else NULL    */
+  float* v_scale;             /* device [num_pages][Hkv], FP8 only, else NULL    */
+  int32_t* block_table;       /* device [max_seqs][max_pages_per_seq]            */
+  int32_t* seq_lens;          /* device [max_seqs]; 0 for free rows              */
+  const int32_t* free_order;  /* host [num_pages]: a permutation giving each
+                                 page's allocation rank (first fit takes the free
+                                 page of lowest rank); NULL = rank by page id.
+                                 Copied at creation.                             */
+} pkv_pool_desc;
+
+/* Bytes of one (page, KV head) slab; 0 for unsupported combinations. */
+int64_t pkv_page_bytes(pkv_dtype kv_dtype, int32_t page_size, int32_t head_dim);
+
+/* Create a pool.  When every device pointer of the descriptor is NULL the
+ * pool is metadata-only: all calls below update the host bookkeeping and
+ * enqueue nothing (used for planning and for host-side tests).  Otherwise
+ * k_pages, v_pages, block_table and seq_lens (and the scales for FP8) are
+ * required; they must stay valid for the pool's lifetime and are not
+ * initialised by the library (the library only writes block-table entries
+ * and lengths of sequences it manages). */
+pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out);
+void pkv_pool_destroy(pkv_pool* pool);
+
+/* Register sequence `seq` and give it a block-table row (*slot_out).  If
+ * share_from >= 0 the first n_shared tokens map to share_from's first
+ * ceil(n_shared/16) pages, whose reference counts are incremented
+ * (paurushmuley.com, PagedKVCacheManager.AllocateSessionBlocks: shared
+ * prefix blocks).  The row and its length are written on `stream`. */
+pkv_status paged_kv_alloc(pkv_pool* pool, int64_t seq, int64_t share_from, int32_t n_shared,
+                          int32_t* slot_out, void* stream);
+
+/* Append n_tokens[i] tokens to each of seqs[0..n_seqs) (all-or-nothing over
+ * the whole call; futurestack.online, section 2.3: the bundle extension is
+ * atomic).  Pages are taken at 16-token boundaries; a partly filled tail page
+ * shared with another sequence is copied first (copy-on-write,
+ * PagedKVCacheManager.EnsureCapacityAndAppendToken).  k_src/v_src are device
+ * arrays [sum(n_tokens)][Hkv][head_dim] in src_dtype, sequences in call order.
+ * Allowed src_dtype: the pool dtype for F32/BF16 pools; PKV_F32 for FP8
+ * pools, which quantise with the page's scale (a fresh page gets
+ * scale = amax/448 of the tokens this call writes into it, per KV head; a page
+ * that already holds tokens keeps its scale and values saturate to +-448).
+ * The scatter, the block-table entries and the new lengths are written on
+ * `stream`; the sources must stay valid until the stream reaches the work. */
+pkv_status paged_kv_append(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
+                           const int32_t* n_tokens, const void* k_src, const void* v_src,
+                           pkv_dtype src_dtype, void* stream);
+
+/* Drop the last n_tokens[i] tokens of each sequence (rejected drafts).  Pages
+ * wholly past the new length lose a reference and are freed at zero; no KV
+ * data moves.  New lengths are written on `stream`. */
+pkv_status paged_kv_rollback(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
+                             const int32_t* n_tokens, void* stream);
+
+/* Unregister a sequence: every page loses a reference
+ * (PagedKVCacheManager.ReleaseSession); its row's length is set to 0. */
+pkv_status paged_kv_release(pkv_pool* pool, int64_t seq, void* stream);
+
+/* Host copy of one sequence's block table.  pages_out may be NULL to query
+ * sizes; otherwise it receives min(n_pages, max_pages) page ids. */
+pkv_status paged_kv_block_table(const pkv_pool* pool, int64_t seq, int32_t* pages_out,
+                                int32_t max_pages, int32_t* n_pages_out, int32_t* len_out,
+                                int32_t* slot_out);
+
+typedef struct {
+  int32_t free_pages;         /* pages with reference count 0                    */
+  int32_t used_pages;         /* pages referenced at least once                  */
+  int32_t shared_pages;       /* pages referenced more than once                 */
+  int32_t num_seqs;           /* live sequences                                  */
+  int64_t cow_copies;         /* copy-on-write page copies so far                */
+  int64_t used_token_slots;   /* sum of sequence lengths (tokens stored once per
+                                 reference)                                      */
+} pkv_pool_stats;
+
+pkv_status paged_kv_stats(const pkv_pool* pool, pkv_pool_stats* out);
+pkv_status paged_kv_page_refcount(const pkv_pool* pool, int32_t page, int32_t* refcount_out);
+
+/* ------------------------------------------------------------------------ */
+/* Draft-tree masks                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* Ancestor-or-self bitmasks of a draft tree given by parents[i] (parents[0] =
+ * -1, parents[i] < i, n_nodes <= 64): bit j of masks_out[i] is set iff node j
+ * lies on the path from the root to node i.  Host arrays.  The additive tree
+ * mask M_tree of atozofsoftwareengineering.blog eq. A_speculative is 0 where
+ * the bit is set and -inf elsewhere. */
+pkv_status spec_tree_ancestor_masks(int32_t n_nodes, const int32_t* parents, uint64_t* masks_out);
+
+/* ------------------------------------------------------------------------ */
+/* Verification attention                                                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * For every sequence b (N = seq_lens[row], L = N - n_q), query slot i < n_q
+ * and query head h (KV head g = h / (Hq/Hkv)):
+ *   s_t   = sm_scale * <q[b,i,h,:], K[t,g,:]>      for visible t
+ *   out   = sum_t softmax(s)_t V[t,g,:],  lse = log(sum_t exp(s_t))  (natural log)
+ * where token t < L is always visible and verification slot t - L is visible
+ * iff bit (t - L) of anc_mask[b*n_q + i] is set (anc_mask == NULL: the causal
+ * chain, t - L <= i).  K/V of token t is slot t%16 of page
+ * block_table[row*block_table_stride + t/16], row = batch_slots ? batch_slots[b] : b.
+ * (atozofsoftwareengineering.blog, eq. A_speculative; the verification
+ * tokens' K/V must already be appended, futurestack.online section 2.3.)
+ *
+ * Supported: q_dtype F32 with kv_dtype F32; q_dtype BF16 with kv_dtype BF16
+ * or FP8_E4M3; head_dim 64 or 128; page_size 16; n_q*Hq/Hkv <= 64 rows per KV
+ * head; n_q <= 64; L >= 0 for every sequence.  Long contexts are split over
+ * workgroups and merged by log-sum-exp in a second kernel (workspace below).
+ */
+typedef struct {
+  int32_t batch;
+  int32_t n_q;                /* gamma + 1 (chain) or tree nodes                 */
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  pkv_dtype q_dtype;
+  pkv_dtype kv_dtype;
+  const void* q;              /* device [batch][n_q][Hq][head_dim]               */
+  const void* k_pages;        /* device pool (layout above)                      */
+  const void* v_pages;
+  const float* k_scale;       /* device [num_pages][Hkv], FP8 only               */
+  const float* v_scale;
+  const int32_t* block_table; /* device                                          */
+  int32_t block_table_stride; /* int32 entries per block-table row               */
+  const int32_t* seq_lens;    /* device, total length N incl. the n_q tokens     */
+  const int32_t* batch_slots; /* device [batch] rows to use, or NULL (row = b)   */
+  const uint64_t* anc_mask;   /* device [batch][n_q] or NULL (chain)             */
+  float sm_scale;             /* usually 1/sqrt(head_dim)                        */
+  float* out;                 /* device [batch][n_q][Hq][head_dim] fp32          */
+  float* lse;                 /* device [batch][n_q][Hq] fp32, may be NULL       */
+  void* workspace;            /* device, >= spec_verify_workspace_size bytes     */
+  size_t workspace_bytes;
+  int32_t num_splits;         /* workgroups sharing the work; 0 = one per slot
+                                 the GPU can keep resident                       */
+} pkv_verify_args;
+
+pkv_status spec_verify_workspace_size(const pkv_verify_args* args, size_t* bytes_out);
+pkv_status spec_verify_attention(const pkv_verify_args* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Acceptance                                                                */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * For every sequence b, with P_i = softmax(target_logits[b,i,:]) and
+ * Q_i = softmax(draft_logits[b,i,:]):
+ *   draft token x_i is accepted iff u_i < min(1, P_i(x_i)/Q_i(x_i)), stopping
+ *   at the first rejection; accepted_len[b] = k (0..gamma);
+ *   next_token[b] = if k < gamma: a draw from max(0, P_k - Q_k) normalised
+ *                   (from P_k if that is zero everywhere);
+ *                   else a draw from P_gamma (the bonus token).
+ * Uniforms come from Philox4x32-10 (Salmon et al., SC'11) keyed by `seed`:
+ * u_i uses counter (0, b, step, i | 1<<16), word 0; the draw at position i uses
+ * u_x from counter (x/4, b, step, i | 2<<16), word x%4, and takes
+ * argmax_x log w(x) - log(-log u_x) (Gumbel-max; ties to the smaller x).
+ * u = (floor(word / 2^9) + 0.5) * 2^-23.
+ * (innvotechnologies.co, eq. alpha_i and eq. E[K]; pipeline diagram
+ *  "Rejection Recovery (Resample)".)
+ */
+typedef struct {
+  int32_t batch;
+  int32_t gamma;              /* drafts per sequence, 1..64                      */
+  int32_t vocab;
+  const float* target_logits; /* device [batch][gamma+1][vocab]                  */
+  const float* draft_logits;  /* device [batch][gamma][vocab]                    */
+  const int32_t* draft_tokens;/* device [batch][gamma], values in [0, vocab)     */
+  uint64_t seed;
+  uint32_t step;
+  int32_t* accepted_len;      /* device [batch]                                  */
+  int32_t* next_token;        /* device [batch]                                  */
+  void* workspace;            /* device, >= spec_accept_workspace_size bytes     */
+  size_t workspace_bytes;
+} pkv_accept_args;
+
+pkv_status spec_accept_workspace_size(const pkv_accept_args* args, size_t* bytes_out);
+pkv_status spec_accept(const pkv_accept_args* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
+const char* pkv_status_string(pkv_status status);
+const char* pkv_last_error(void);
+/* Library version string. */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_SPEC_H */

@@ -1,0 +1,254 @@
+"""Python front end over the C ABI (marshalling only)."""
+import ctypes as C
+
+import numpy as np
+import torch
+
+from ._lib import (AcceptArgs, DTYPES, F32, BF16, FP8_E4M3, PoolDesc, PoolStats, VerifyArgs,
+                   check, i32_array, i64_array, lib)
+
+PAGE_SIZE = 16
+_TORCH_SRC = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+def _stream(stream):
+    if stream is None:
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return C.c_void_p(stream.cuda_stream)
+    return C.c_void_p(int(stream))
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def page_bytes(kv_dtype, head_dim, page_size=PAGE_SIZE):
+    return int(lib.pkv_page_bytes(DTYPES[kv_dtype], page_size, head_dim))
+
+
+def tree_ancestor_masks(parents):
+    """Ancestor-or-self bitmask per node (host, via the library)."""
+    n = len(parents)
+    out = (C.c_uint64 * n)()
+    check(lib.spec_tree_ancestor_masks(n, i32_array(parents), out))
+    return [int(x) for x in out]
+
+
+class Pool:
+    """Page pool with device-resident block table and lengths.
+
+    device=None gives a metadata-only pool (host bookkeeping, no kernels)."""
+
+    def __init__(self, num_pages, num_kv_heads, head_dim, kv_dtype="bf16", max_seqs=64,
+                 max_pages_per_seq=256, free_order=None, device=None):
+        self.num_pages, self.num_kv_heads, self.head_dim = num_pages, num_kv_heads, head_dim
+        self.kv_dtype, self.max_seqs, self.max_pages_per_seq = kv_dtype, max_seqs, max_pages_per_seq
+        self.page_bytes = page_bytes(kv_dtype, head_dim)
+        if self.page_bytes == 0:
+            raise ValueError("unsupported kv_dtype/head_dim")
+        self.device = device
+        desc = PoolDesc()
+        desc.num_pages, desc.page_size, desc.num_kv_heads = num_pages, PAGE_SIZE, num_kv_heads
+        desc.head_dim, desc.kv_dtype = head_dim, DTYPES[kv_dtype]
+        desc.max_seqs, desc.max_pages_per_seq = max_seqs, max_pages_per_seq
+        self.k_pages = self.v_pages = self.k_scale = self.v_scale = None
+        self.block_table = self.seq_lens = None
+        if device is not None:
+            shape = (num_pages, num_kv_heads, self.page_bytes)
+            self.k_pages = torch.empty(shape, dtype=torch.uint8, device=device)
+            self.v_pages = torch.empty(shape, dtype=torch.uint8, device=device)
+            if kv_dtype == "fp8":
+                self.k_scale = torch.ones((num_pages, num_kv_heads), dtype=torch.float32, device=device)
+                self.v_scale = torch.ones((num_pages, num_kv_heads), dtype=torch.float32, device=device)
+            self.block_table = torch.zeros((max_seqs, max_pages_per_seq), dtype=torch.int32, device=device)
+            self.seq_lens = torch.zeros(max_seqs, dtype=torch.int32, device=device)
+            desc.k_pages, desc.v_pages = self.k_pages.data_ptr(), self.v_pages.data_ptr()
+            if self.k_scale is not None:
+                desc.k_scale, desc.v_scale = self.k_scale.data_ptr(), self.v_scale.data_ptr()
+            desc.block_table, desc.seq_lens = self.block_table.data_ptr(), self.seq_lens.data_ptr()
+        order = None
+        if free_order is not None:
+            order = i32_array(np.asarray(free_order))
+            desc.free_order = C.cast(order, C.POINTER(C.c_int32))
+        self._h = C.c_void_p()
+        check(lib.pkv_pool_create(C.byref(desc), C.byref(self._h)))
+        self._slots = {}
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            lib.pkv_pool_destroy(h)
+            self._h = None
+
+    def fill_nan(self):
+        """Fill every page with NaN patterns so reads of unwritten slots show."""
+        if self.k_pages is None:
+            return
+        if self.kv_dtype == "fp8":
+            self.k_pages.fill_(0x7F)
+            self.v_pages.fill_(0x7F)
+        elif self.kv_dtype == "bf16":
+            self.k_pages.view(torch.int16).fill_(0x7FC0)
+            self.v_pages.view(torch.int16).fill_(0x7FC0)
+        else:
+            self.k_pages.view(torch.int32).fill_(0x7FC00000)
+            self.v_pages.view(torch.int32).fill_(0x7FC00000)
+
+    # -- sequence operations ---------------------------------------------------
+    def alloc(self, seq, share_from=-1, n_shared=0, stream=None):
+        slot = C.c_int32()
+        st = _stream(stream) if self.device is not None else None
+        check(lib.paged_kv_alloc(self._h, int(seq), int(share_from), int(n_shared), C.byref(slot), st))
+        self._slots[int(seq)] = slot.value
+        return slot.value
+
+    def append(self, seqs, n_tokens, k_src=None, v_src=None, stream=None):
+        seqs, n_tokens = list(seqs), list(n_tokens)
+        src_dtype, kp, vp = F32, None, None
+        if self.device is not None and sum(n_tokens) > 0:
+            assert k_src.is_contiguous() and v_src.is_contiguous() and k_src.dtype == v_src.dtype
+            assert k_src.numel() >= sum(n_tokens) * self.num_kv_heads * self.head_dim
+            src_dtype = _TORCH_SRC[k_src.dtype]
+            kp, vp = _ptr(k_src), _ptr(v_src)
+        st = _stream(stream) if self.device is not None else None
+        check(lib.paged_kv_append(self._h, len(seqs), i64_array(seqs), i32_array(n_tokens),
+                                  kp, vp, src_dtype, st))
+
+    def rollback(self, seqs, n_tokens, stream=None):
+        seqs, n_tokens = list(seqs), list(n_tokens)
+        st = _stream(stream) if self.device is not None else None
+        check(lib.paged_kv_rollback(self._h, len(seqs), i64_array(seqs), i32_array(n_tokens), st))
+
+    def release(self, seq, stream=None):
+        st = _stream(stream) if self.device is not None else None
+        check(lib.paged_kv_release(self._h, int(seq), st))
+        self._slots.pop(int(seq), None)
+
+    def table(self, seq):
+        """(pages, length, slot) of a sequence, from the host bookkeeping."""
+        n, length, slot = C.c_int32(), C.c_int32(), C.c_int32()
+        check(lib.paged_kv_block_table(self._h, int(seq), None, 0, C.byref(n), C.byref(length),
+                                       C.byref(slot)))
+        buf = (C.c_int32 * max(1, n.value))()
+        check(lib.paged_kv_block_table(self._h, int(seq), buf, n.value, C.byref(n), C.byref(length),
+                                       C.byref(slot)))
+        return [buf[i] for i in range(n.value)], length.value, slot.value
+
+    def stats(self):
+        s = PoolStats()
+        check(lib.paged_kv_stats(self._h, C.byref(s)))
+        return {k: getattr(s, k) for k, _ in PoolStats._fields_}
+
+    def refcount(self, page):
+        r = C.c_int32()
+        check(lib.paged_kv_page_refcount(self._h, int(page), C.byref(r)))
+        return r.value
+
+    def slot(self, seq):
+        return self._slots[int(seq)]
+
+    # -- verification over this pool --------------------------------------------
+    def verify(self, q, n_q, slots=None, anc_mask=None, sm_scale=None, buffers=None, num_splits=0,
+               stream=None):
+        return spec_verify_attention(
+            q, self.k_pages, self.v_pages, self.block_table, self.seq_lens, n_q=n_q,
+            num_kv_heads=self.num_kv_heads, kv_dtype=self.kv_dtype, k_scale=self.k_scale,
+            v_scale=self.v_scale, batch_slots=slots, anc_mask=anc_mask, sm_scale=sm_scale,
+            buffers=buffers, num_splits=num_splits, stream=stream)
+
+
+def _verify_args(q, k_pages, v_pages, block_table, seq_lens, n_q, num_kv_heads, kv_dtype, k_scale,
+                 v_scale, batch_slots, anc_mask, sm_scale, num_splits):
+    B, nq, Hq, d = q.shape
+    assert nq == n_q and q.is_contiguous()
+    a = VerifyArgs()
+    a.batch, a.n_q, a.num_q_heads, a.num_kv_heads, a.head_dim = B, n_q, Hq, num_kv_heads, d
+    a.page_size = PAGE_SIZE
+    a.q_dtype = F32 if q.dtype == torch.float32 else BF16
+    a.kv_dtype = DTYPES[kv_dtype]
+    a.q, a.k_pages, a.v_pages = q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr()
+    if k_scale is not None:
+        a.k_scale, a.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+    assert block_table.dtype == torch.int32 and block_table.is_contiguous()
+    a.block_table, a.block_table_stride = block_table.data_ptr(), block_table.shape[-1]
+    assert seq_lens.dtype == torch.int32
+    a.seq_lens = seq_lens.data_ptr()
+    if batch_slots is not None:
+        assert batch_slots.dtype == torch.int32 and batch_slots.numel() == B
+        a.batch_slots = batch_slots.data_ptr()
+    if anc_mask is not None:
+        assert anc_mask.dtype == torch.int64 and anc_mask.shape == (B, n_q)
+        a.anc_mask = anc_mask.data_ptr()
+    a.sm_scale = float(np.float32(1.0 / np.sqrt(d)) if sm_scale is None else sm_scale)
+    a.num_splits = num_splits
+    return a
+
+
+def verify_workspace_size(args):
+    n = C.c_size_t()
+    check(lib.spec_verify_workspace_size(C.byref(args), C.byref(n)))
+    return n.value
+
+
+class VerifyBuffers:
+    """Preallocated outputs and workspace for repeated calls of one shape."""
+
+    def __init__(self, batch, n_q, num_q_heads, head_dim, workspace_bytes, device):
+        self.out = torch.empty((batch, n_q, num_q_heads, head_dim), dtype=torch.float32, device=device)
+        self.lse = torch.empty((batch, n_q, num_q_heads), dtype=torch.float32, device=device)
+        self.workspace = torch.empty(max(1, workspace_bytes), dtype=torch.uint8, device=device)
+
+
+def spec_verify_attention(q, k_pages, v_pages, block_table, seq_lens, *, n_q, num_kv_heads,
+                          kv_dtype, k_scale=None, v_scale=None, batch_slots=None, anc_mask=None,
+                          sm_scale=None, buffers=None, num_splits=0, stream=None):
+    a = _verify_args(q, k_pages, v_pages, block_table, seq_lens, n_q, num_kv_heads, kv_dtype,
+                     k_scale, v_scale, batch_slots, anc_mask, sm_scale, num_splits)
+    ws = verify_workspace_size(a)
+    if buffers is None:
+        B, _, Hq, d = q.shape
+        buffers = VerifyBuffers(B, n_q, Hq, d, ws, q.device)
+    assert buffers.workspace.numel() >= ws
+    a.out, a.lse = buffers.out.data_ptr(), buffers.lse.data_ptr()
+    a.workspace, a.workspace_bytes = buffers.workspace.data_ptr(), buffers.workspace.numel()
+    check(lib.spec_verify_attention(C.byref(a), _stream(stream)))
+    return buffers.out, buffers.lse
+
+
+def _accept_args(target_logits, draft_logits, draft_tokens, seed, step):
+    B, g1, V = target_logits.shape
+    assert draft_logits.shape == (B, g1 - 1, V) and draft_tokens.shape == (B, g1 - 1)
+    assert target_logits.dtype == torch.float32 and draft_logits.dtype == torch.float32
+    assert draft_tokens.dtype == torch.int32
+    assert target_logits.is_contiguous() and draft_logits.is_contiguous() and draft_tokens.is_contiguous()
+    a = AcceptArgs()
+    a.batch, a.gamma, a.vocab = B, g1 - 1, V
+    a.target_logits, a.draft_logits = target_logits.data_ptr(), draft_logits.data_ptr()
+    a.draft_tokens = draft_tokens.data_ptr()
+    a.seed, a.step = int(seed) & 0xFFFFFFFFFFFFFFFF, int(step) & 0xFFFFFFFF
+    return a
+
+
+def accept_workspace_size(args):
+    n = C.c_size_t()
+    check(lib.spec_accept_workspace_size(C.byref(args), C.byref(n)))
+    return n.value
+
+
+class AcceptBuffers:
+    def __init__(self, batch, workspace_bytes, device):
+        self.accepted_len = torch.empty(batch, dtype=torch.int32, device=device)
+        self.next_token = torch.empty(batch, dtype=torch.int32, device=device)
+        self.workspace = torch.empty(max(1, workspace_bytes), dtype=torch.uint8, device=device)
+
+
+def spec_accept(target_logits, draft_logits, draft_tokens, seed, step, buffers=None, stream=None):
+    a = _accept_args(target_logits, draft_logits, draft_tokens, seed, step)
+    ws = accept_workspace_size(a)
+    if buffers is None:
+        buffers = AcceptBuffers(a.batch, ws, target_logits.device)
+    a.accepted_len, a.next_token = buffers.accepted_len.data_ptr(), buffers.next_token.data_ptr()
+    a.workspace, a.workspace_bytes = buffers.workspace.data_ptr(), buffers.workspace.numel()
+    check(lib.spec_accept(C.byref(a), _stream(stream)))
+    return buffers.accepted_len, buffers.next_token

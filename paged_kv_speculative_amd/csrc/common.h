@@ -1,0 +1,70 @@
+// Shared host-side helpers of libpkvspec: status/error reporting and the
+// device-update task format exchanged between the pool bookkeeping
+// (pool.cpp) and the pool-update kernel (kernels/kv_append.hip).
+#pragma once
+
+#include <cstdint>
+#include <string>
+
+#include "../../include/pkv_spec.h"
+
+namespace pkv {
+
+// Thread-local message of the calling thread's last failure.
+void set_error(const std::string& msg);
+pkv_status fail(pkv_status st, const std::string& msg);
+
+constexpr int kPageSize = 16;
+
+// One unit of device work on the pool, applied by one workgroup:
+//   - if cow_src >= 0: copy page cow_src (all heads, K and V, and the FP8
+//     scales) to page `page` before anything else;
+//   - if n > 0: write tokens src_row .. src_row+n-1 of the source arrays into
+//     slots slot_begin .. slot_begin+n-1 of page `page` (FP8: fresh pages get
+//     new scales from these tokens, other pages keep theirs);
+//   - if flags & kWriteTable: block_table[row][logical] = page;
+//   - if flags & kSetLen: seq_lens[row] = new_len.
+enum : int32_t { kFresh = 1, kWriteTable = 2, kSetLen = 4 };
+
+struct PoolTask {
+  int32_t row;
+  int32_t logical;
+  int32_t page;
+  int32_t cow_src;
+  int32_t src_row;
+  int32_t slot_begin;
+  int32_t n;
+  int32_t flags;
+  int32_t new_len;
+  int32_t pad;
+};
+
+constexpr int kTasksPerLaunch = 96;
+
+struct PoolUpdateBatch {
+  int32_t n_tasks;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t kv_dtype;      // pkv_dtype of the pool
+  int32_t src_dtype;     // pkv_dtype of k_src/v_src
+  int32_t bt_stride;     // max_pages_per_seq
+  int64_t page_bytes;    // bytes of one (page, head) slab
+  PoolTask tasks[kTasksPerLaunch];
+};
+static_assert(sizeof(PoolUpdateBatch) <= 4000, "kernel argument block too large");
+
+struct PoolDevice {
+  void* k_pages;
+  void* v_pages;
+  float* k_scale;
+  float* v_scale;
+  int32_t* block_table;
+  int32_t* seq_lens;
+  const void* k_src;
+  const void* v_src;
+};
+
+// Implemented in kernels/kv_append.hip.
+pkv_status launch_pool_update(const PoolDevice& dev, const PoolUpdateBatch& batch, void* stream);
+
+}  // namespace pkv

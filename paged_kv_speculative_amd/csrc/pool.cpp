@@ -1,0 +1,453 @@
+// Page pool bookkeeping of libpkvspec (host side).
+//
+// Semantics follow the paged KV managers on the pages
+// (paurushmuley.com, PagedKVCacheManager: shared-prefix reference counts,
+// allocation at block boundaries, copy-on-write of shared blocks, release at
+// reference count zero, an error on exhaustion; innvotechnologies.co,
+// TypeScript allocateBlocks: first fit; futurestack.online section 2.3: the
+// bundle extension is atomic; innvotechnologies.co pipeline diagram: commit
+// accepted drafts, discard the rest).  Free pages form a set ordered by a
+// caller-given rank; allocation takes the lowest rank, so the free set alone
+// decides future allocations (rollback restores it exactly).
+//
+// All device effects (scatter of new tokens, CoW copies, block-table entries,
+// lengths) are expressed as PoolTask records and applied in-stream by the
+// pool-update kernel; a metadata-only pool skips them.
+
+#include <algorithm>
+#include <cstring>
+#include <mutex>
+#include <set>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "common.h"
+
+namespace pkv {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+pkv_status fail(pkv_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+struct Seq {
+  int32_t row = -1;
+  int32_t len = 0;
+  std::vector<int32_t> pages;
+};
+
+struct pkv_pool {
+  pkv_pool_desc desc{};
+  bool device = false;
+  int64_t page_bytes = 0;
+  std::mutex mu;
+  std::vector<int32_t> rank;          // page -> rank
+  std::vector<int32_t> page_of_rank;  // rank -> page
+  std::set<int32_t> free_ranks;       // ranks of free pages
+  std::vector<int32_t> refcount;
+  std::set<int32_t> free_rows;
+  std::unordered_map<int64_t, Seq> seqs;
+  int64_t cow_copies = 0;
+
+  int32_t take_page() {
+    auto it = free_ranks.begin();
+    int32_t p = page_of_rank[*it];
+    free_ranks.erase(it);
+    refcount[p] = 1;
+    return p;
+  }
+  void unref(int32_t p) {
+    if (--refcount[p] == 0) free_ranks.insert(rank[p]);
+  }
+};
+
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Collects tasks and flushes them to the device in launch-sized batches.
+struct TaskSink {
+  pkv_pool* pool;
+  const void* k_src;
+  const void* v_src;
+  pkv_dtype src_dtype;
+  void* stream;
+  PoolUpdateBatch batch{};
+  pkv_status status = PKV_OK;
+
+  TaskSink(pkv_pool* p, const void* k, const void* v, pkv_dtype sd, void* s)
+      : pool(p), k_src(k), v_src(v), src_dtype(sd), stream(s) {
+    batch.num_kv_heads = p->desc.num_kv_heads;
+    batch.head_dim = p->desc.head_dim;
+    batch.kv_dtype = p->desc.kv_dtype;
+    batch.src_dtype = sd;
+    batch.bt_stride = p->desc.max_pages_per_seq;
+    batch.page_bytes = p->page_bytes;
+  }
+  void add(const PoolTask& t) {
+    if (!pool->device) return;
+    batch.tasks[batch.n_tasks++] = t;
+    if (batch.n_tasks == kTasksPerLaunch) flush();
+  }
+  void flush() {
+    if (!pool->device || batch.n_tasks == 0) return;
+    PoolDevice dev{pool->desc.k_pages, pool->desc.v_pages, pool->desc.k_scale,
+                   pool->desc.v_scale, pool->desc.block_table, pool->desc.seq_lens,
+                   k_src, v_src};
+    pkv_status st = launch_pool_update(dev, batch, stream);
+    if (st != PKV_OK && status == PKV_OK) status = st;
+    batch.n_tasks = 0;
+  }
+};
+
+PoolTask len_task(int32_t row, int32_t len) {
+  PoolTask t{};
+  t.row = row;
+  t.page = -1;
+  t.cow_src = -1;
+  t.flags = kSetLen;
+  t.new_len = len;
+  return t;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t pkv_page_bytes(pkv_dtype kv_dtype, int32_t page_size, int32_t head_dim) {
+  if (page_size != kPageSize || (head_dim != 64 && head_dim != 128)) return 0;
+  switch (kv_dtype) {
+    case PKV_F32: return int64_t(page_size) * head_dim * 4;
+    case PKV_BF16: return int64_t(page_size) * head_dim * 2;
+    case PKV_FP8_E4M3: return int64_t(page_size) * head_dim;
+    default: return 0;
+  }
+}
+
+pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out) {
+  if (!desc || !out) return fail(PKV_ERR_INVALID_ARG, "null descriptor or output");
+  *out = nullptr;
+  const pkv_pool_desc& d = *desc;
+  if (d.num_pages <= 0 || d.num_kv_heads <= 0 || d.max_seqs <= 0 || d.max_pages_per_seq <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "pool sizes must be positive");
+  if (d.kv_dtype != PKV_F32 && d.kv_dtype != PKV_BF16 && d.kv_dtype != PKV_FP8_E4M3)
+    return fail(PKV_ERR_INVALID_ARG, "unknown kv dtype");
+  int64_t pb = pkv_page_bytes(d.kv_dtype, d.page_size, d.head_dim);
+  if (pb == 0) return fail(PKV_ERR_UNSUPPORTED, "page_size must be 16 and head_dim 64 or 128");
+  bool any_dev = d.k_pages || d.v_pages || d.k_scale || d.v_scale || d.block_table || d.seq_lens;
+  if (any_dev) {
+    if (!d.k_pages || !d.v_pages || !d.block_table || !d.seq_lens)
+      return fail(PKV_ERR_INVALID_ARG, "device pool needs k_pages, v_pages, block_table, seq_lens");
+    if (d.kv_dtype == PKV_FP8_E4M3 && (!d.k_scale || !d.v_scale))
+      return fail(PKV_ERR_INVALID_ARG, "FP8 pool needs k_scale and v_scale");
+  }
+  std::vector<int32_t> order(d.num_pages);
+  if (d.free_order) {
+    std::vector<char> seen(d.num_pages, 0);
+    for (int32_t r = 0; r < d.num_pages; ++r) {
+      int32_t p = d.free_order[r];
+      if (p < 0 || p >= d.num_pages || seen[p])
+        return fail(PKV_ERR_INVALID_ARG, "free_order is not a permutation of [0, num_pages)");
+      seen[p] = 1;
+      order[r] = p;
+    }
+  } else {
+    for (int32_t r = 0; r < d.num_pages; ++r) order[r] = r;
+  }
+  auto* pool = new pkv_pool();
+  pool->desc = d;
+  pool->desc.free_order = nullptr;
+  pool->device = any_dev;
+  pool->page_bytes = pb;
+  pool->rank.resize(d.num_pages);
+  pool->page_of_rank = order;
+  pool->refcount.assign(d.num_pages, 0);
+  for (int32_t r = 0; r < d.num_pages; ++r) {
+    pool->rank[order[r]] = r;
+    pool->free_ranks.insert(pool->free_ranks.end(), r);
+  }
+  for (int32_t r = 0; r < d.max_seqs; ++r) pool->free_rows.insert(pool->free_rows.end(), r);
+  *out = pool;
+  return PKV_OK;
+}
+
+void pkv_pool_destroy(pkv_pool* pool) { delete pool; }
+
+pkv_status paged_kv_alloc(pkv_pool* pool, int64_t seq, int64_t share_from, int32_t n_shared,
+                          int32_t* slot_out, void* stream) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "null pool");
+  std::lock_guard<std::mutex> lock(pool->mu);
+  if (pool->seqs.count(seq)) return fail(PKV_ERR_SEQ_EXISTS, "sequence already allocated");
+  const Seq* src = nullptr;
+  if (share_from >= 0) {
+    auto it = pool->seqs.find(share_from);
+    if (it == pool->seqs.end()) return fail(PKV_ERR_UNKNOWN_SEQ, "share_from not allocated");
+    src = &it->second;
+    if (n_shared < 0 || n_shared > src->len)
+      return fail(PKV_ERR_INVALID_ARG, "n_shared outside [0, len(share_from)]");
+  } else if (n_shared != 0) {
+    return fail(PKV_ERR_INVALID_ARG, "n_shared without share_from");
+  }
+  if (pool->free_rows.empty()) return fail(PKV_ERR_NO_SLOT, "no free block-table row");
+  Seq s;
+  s.row = *pool->free_rows.begin();
+  if (src) {
+    int64_t np = ceil_div(n_shared, kPageSize);
+    s.pages.assign(src->pages.begin(), src->pages.begin() + np);
+    s.len = n_shared;
+  }
+  TaskSink sink(pool, nullptr, nullptr, pool->desc.kv_dtype, stream);
+  for (size_t i = 0; i < s.pages.size(); ++i) {
+    PoolTask t = len_task(s.row, s.len);
+    t.flags = kWriteTable | (i + 1 == s.pages.size() ? kSetLen : 0);
+    t.logical = int32_t(i);
+    t.page = s.pages[i];
+    sink.add(t);
+  }
+  if (s.pages.empty()) sink.add(len_task(s.row, 0));
+  sink.flush();
+  if (sink.status != PKV_OK) return sink.status;
+  for (int32_t p : s.pages) pool->refcount[p]++;
+  pool->free_rows.erase(pool->free_rows.begin());
+  if (slot_out) *slot_out = s.row;
+  pool->seqs.emplace(seq, std::move(s));
+  return PKV_OK;
+}
+
+pkv_status paged_kv_append(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
+                           const int32_t* n_tokens, const void* k_src, const void* v_src,
+                           pkv_dtype src_dtype, void* stream) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "null pool");
+  if (n_seqs < 0 || (n_seqs > 0 && (!seqs || !n_tokens)))
+    return fail(PKV_ERR_INVALID_ARG, "bad sequence list");
+  std::lock_guard<std::mutex> lock(pool->mu);
+  const pkv_pool_desc& d = pool->desc;
+  if (pool->device) {
+    bool ok = (d.kv_dtype == PKV_FP8_E4M3) ? src_dtype == PKV_F32 : src_dtype == d.kv_dtype;
+    if (!ok) return fail(PKV_ERR_INVALID_ARG, "source dtype does not match the pool dtype");
+  }
+  // Validate and count pages by simulating the whole call on a copy of the
+  // reference counts of the touched tail pages.
+  std::unordered_set<int64_t> seen;
+  std::unordered_map<int32_t, int32_t> sim_ref;
+  int64_t need = 0, total_tokens = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    auto it = pool->seqs.find(seqs[i]);
+    if (it == pool->seqs.end()) return fail(PKV_ERR_UNKNOWN_SEQ, "append to unknown sequence");
+    if (!seen.insert(seqs[i]).second) return fail(PKV_ERR_INVALID_ARG, "sequence listed twice");
+    int32_t n = n_tokens[i];
+    if (n < 0) return fail(PKV_ERR_INVALID_ARG, "negative token count");
+    const Seq& s = it->second;
+    int64_t new_pages = ceil_div(int64_t(s.len) + n, kPageSize);
+    if (new_pages > d.max_pages_per_seq) return fail(PKV_ERR_CAPACITY, "sequence exceeds max_pages_per_seq");
+    if (int64_t(s.len) + n > INT32_MAX) return fail(PKV_ERR_CAPACITY, "sequence too long");
+    total_tokens += n;
+    if (n == 0) continue;
+    if (s.len % kPageSize) {
+      int32_t tail = s.pages[s.len / kPageSize];
+      auto r = sim_ref.emplace(tail, pool->refcount[tail]).first;
+      if (r->second > 1) {
+        need += 1;
+        r->second -= 1;
+      }
+    }
+    need += new_pages - int64_t(s.pages.size());
+  }
+  if (pool->device && total_tokens > 0 && (!k_src || !v_src))
+    return fail(PKV_ERR_INVALID_ARG, "null source arrays");
+  if (need > int64_t(pool->free_ranks.size()))
+    return fail(PKV_ERR_OUT_OF_PAGES, "page pool exhausted");
+
+  // Copy-on-write copies go to the device before any token write of this
+  // call: a write may land in a page that another sequence just stopped
+  // sharing, and the copy must see that page's old contents.
+  std::vector<PoolTask> copies, writes;
+  int64_t src_row = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    Seq& s = pool->seqs[seqs[i]];
+    int32_t n = n_tokens[i];
+    if (n == 0) continue;
+    int32_t L = s.len;
+    int32_t cow_src = -1;
+    if (L % kPageSize) {
+      int32_t tail = s.pages[L / kPageSize];
+      if (pool->refcount[tail] > 1) {
+        int32_t np = pool->take_page();
+        pool->unref(tail);
+        s.pages[L / kPageSize] = np;
+        cow_src = tail;
+        pool->cow_copies++;
+        PoolTask c{};
+        c.row = s.row;
+        c.page = np;
+        c.cow_src = tail;
+        copies.push_back(c);
+      }
+    }
+    std::vector<char> fresh(ceil_div(int64_t(L) + n, kPageSize), 0);
+    while (int64_t(s.pages.size()) < ceil_div(int64_t(L) + n, kPageSize)) {
+      fresh[s.pages.size()] = 1;
+      s.pages.push_back(pool->take_page());
+    }
+    int32_t first_blk = L / kPageSize;
+    int32_t last_blk = int32_t(ceil_div(int64_t(L) + n, kPageSize)) - 1;
+    for (int32_t blk = first_blk; blk <= last_blk; ++blk) {
+      int32_t t0 = std::max(L, blk * kPageSize);
+      int32_t t1 = std::min(L + n, (blk + 1) * kPageSize);
+      PoolTask t{};
+      t.row = s.row;
+      t.logical = blk;
+      t.page = s.pages[blk];
+      t.cow_src = -1;
+      t.src_row = int32_t(src_row + (t0 - L));
+      t.slot_begin = t0 - blk * kPageSize;
+      t.n = t1 - t0;
+      t.flags = (fresh[blk] ? kFresh : 0) |
+                ((fresh[blk] || (blk == first_blk && cow_src >= 0)) ? kWriteTable : 0) |
+                (blk == last_blk ? kSetLen : 0);
+      t.new_len = L + n;
+      writes.push_back(t);
+    }
+    s.len = L + n;
+    src_row += n;
+  }
+  TaskSink sink(pool, k_src, v_src, src_dtype, stream);
+  for (const PoolTask& t : copies) sink.add(t);
+  sink.flush();
+  for (const PoolTask& t : writes) sink.add(t);
+  sink.flush();
+  return sink.status;
+}
+
+pkv_status paged_kv_rollback(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
+                             const int32_t* n_tokens, void* stream) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "null pool");
+  if (n_seqs < 0 || (n_seqs > 0 && (!seqs || !n_tokens)))
+    return fail(PKV_ERR_INVALID_ARG, "bad sequence list");
+  std::lock_guard<std::mutex> lock(pool->mu);
+  std::unordered_set<int64_t> seen;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    auto it = pool->seqs.find(seqs[i]);
+    if (it == pool->seqs.end()) return fail(PKV_ERR_UNKNOWN_SEQ, "rollback of unknown sequence");
+    if (!seen.insert(seqs[i]).second) return fail(PKV_ERR_INVALID_ARG, "sequence listed twice");
+    if (n_tokens[i] < 0 || n_tokens[i] > it->second.len)
+      return fail(PKV_ERR_INVALID_ARG, "rollback outside [0, len]");
+  }
+  TaskSink sink(pool, nullptr, nullptr, pool->desc.kv_dtype, stream);
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    Seq& s = pool->seqs[seqs[i]];
+    if (n_tokens[i] == 0) continue;
+    s.len -= n_tokens[i];
+    size_t keep = size_t(ceil_div(s.len, kPageSize));
+    for (size_t j = keep; j < s.pages.size(); ++j) pool->unref(s.pages[j]);
+    s.pages.resize(keep);
+    sink.add(len_task(s.row, s.len));
+  }
+  sink.flush();
+  return sink.status;
+}
+
+pkv_status paged_kv_release(pkv_pool* pool, int64_t seq, void* stream) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "null pool");
+  std::lock_guard<std::mutex> lock(pool->mu);
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PKV_ERR_UNKNOWN_SEQ, "release of unknown sequence");
+  TaskSink sink(pool, nullptr, nullptr, pool->desc.kv_dtype, stream);
+  sink.add(len_task(it->second.row, 0));
+  sink.flush();
+  if (sink.status != PKV_OK) return sink.status;
+  for (int32_t p : it->second.pages) pool->unref(p);
+  pool->free_rows.insert(it->second.row);
+  pool->seqs.erase(it);
+  return PKV_OK;
+}
+
+pkv_status paged_kv_block_table(const pkv_pool* cpool, int64_t seq, int32_t* pages_out,
+                                int32_t max_pages, int32_t* n_pages_out, int32_t* len_out,
+                                int32_t* slot_out) {
+  if (!cpool) return fail(PKV_ERR_INVALID_ARG, "null pool");
+  auto* pool = const_cast<pkv_pool*>(cpool);
+  std::lock_guard<std::mutex> lock(pool->mu);
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence");
+  const Seq& s = it->second;
+  if (pages_out) {
+    if (max_pages < 0) return fail(PKV_ERR_INVALID_ARG, "negative max_pages");
+    size_t n = std::min<size_t>(size_t(max_pages), s.pages.size());
+    std::memcpy(pages_out, s.pages.data(), n * sizeof(int32_t));
+  }
+  if (n_pages_out) *n_pages_out = int32_t(s.pages.size());
+  if (len_out) *len_out = s.len;
+  if (slot_out) *slot_out = s.row;
+  return PKV_OK;
+}
+
+pkv_status paged_kv_stats(const pkv_pool* cpool, pkv_pool_stats* out) {
+  if (!cpool || !out) return fail(PKV_ERR_INVALID_ARG, "null argument");
+  auto* pool = const_cast<pkv_pool*>(cpool);
+  std::lock_guard<std::mutex> lock(pool->mu);
+  pkv_pool_stats st{};
+  for (int32_t r : pool->refcount) {
+    if (r > 0) st.used_pages++;
+    if (r > 1) st.shared_pages++;
+  }
+  st.free_pages = int32_t(pool->free_ranks.size());
+  st.num_seqs = int32_t(pool->seqs.size());
+  st.cow_copies = pool->cow_copies;
+  for (auto& kv : pool->seqs) st.used_token_slots += kv.second.len;
+  *out = st;
+  return PKV_OK;
+}
+
+pkv_status paged_kv_page_refcount(const pkv_pool* cpool, int32_t page, int32_t* refcount_out) {
+  if (!cpool || !refcount_out) return fail(PKV_ERR_INVALID_ARG, "null argument");
+  auto* pool = const_cast<pkv_pool*>(cpool);
+  std::lock_guard<std::mutex> lock(pool->mu);
+  if (page < 0 || page >= pool->desc.num_pages) return fail(PKV_ERR_INVALID_ARG, "page out of range");
+  *refcount_out = pool->refcount[page];
+  return PKV_OK;
+}
+
+pkv_status spec_tree_ancestor_masks(int32_t n_nodes, const int32_t* parents, uint64_t* masks_out) {
+  if (n_nodes < 1 || n_nodes > 64 || !parents || !masks_out)
+    return fail(PKV_ERR_INVALID_ARG, "need 1..64 nodes and non-null arrays");
+  if (parents[0] != -1) return fail(PKV_ERR_INVALID_ARG, "node 0 must be the root (parent -1)");
+  for (int32_t i = 1; i < n_nodes; ++i)
+    if (parents[i] < 0 || parents[i] >= i)
+      return fail(PKV_ERR_INVALID_ARG, "parents[i] must lie in [0, i)");
+  // parents precede children, so each node's mask extends its parent's
+  for (int32_t i = 0; i < n_nodes; ++i)
+    masks_out[i] = (uint64_t(1) << i) | (i ? masks_out[parents[i]] : 0);
+  return PKV_OK;
+}
+
+const char* pkv_status_string(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_OUT_OF_PAGES: return "out of pages";
+    case PKV_ERR_UNKNOWN_SEQ: return "unknown sequence";
+    case PKV_ERR_SEQ_EXISTS: return "sequence exists";
+    case PKV_ERR_UNSUPPORTED: return "unsupported";
+    case PKV_ERR_DEVICE: return "device error";
+    case PKV_ERR_WORKSPACE: return "workspace too small";
+    case PKV_ERR_NO_SLOT: return "no free block-table row";
+    case PKV_ERR_CAPACITY: return "sequence exceeds block-table capacity";
+  }
+  return "unknown status";
+}
+
+const char* pkv_last_error(void) { return pkv::g_last_error.c_str(); }
+
+const char* pkv_version(void) { return "pkvspec 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,235 @@
+"""GPU parity of spec_verify_attention and the pool kernels against the oracle.
+
+Every comparison takes the oracle's values from its own replay of the
+generator's arrays (tests/harness.py); tolerances are the accuracy targets:
+max |dO| <= tau * rms(O_ref) and max |dLSE| <= tau nats, tau = 2e-3 for
+bf16/fp32 KV and 2e-2 for FP8 KV (1e-4 for the fp32 VALU path)."""
+import numpy as np
+import pytest
+import torch
+
+import harness as H
+from oracle import fp8 as ofp8
+from paged_kv_speculative_amd import workloads as wl
+from layout_ref import detile_k, detile_v, tile_v
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, **kw):
+    g = H.GpuSide(w)
+    O, L = g.verify(**kw)
+    torch.cuda.synchronize()
+    return g, O.cpu().numpy(), L.cpu().numpy()
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_config_small_full_parity(cfg):
+    w = wl.make(cfg, small=True)
+    print(f"cfg {cfg} small: B={w.batch} lens={list(w.seq_lens)}", flush=True)
+    g, O, L = _run(w)
+    O_ref, L_ref = H.oracle_verify(w, range(w.batch))
+    tol = 1e-4 if w.kv_dtype == "f32" else H.TOL[w.kv_dtype]
+    H.compare(O, L, O_ref, L_ref, tol)
+    # block tables are integer state: exact
+    ref = H.oracle_block_tables(w)
+    for b in range(w.batch):
+        assert g.pool.table(b)[0] == ref[b]
+    bt = g.pool.block_table.cpu().numpy()
+    lens = g.pool.seq_lens.cpu().numpy()
+    for b in range(w.batch):
+        assert list(bt[b, :len(ref[b])]) == ref[b] and lens[b] == w.seq_lens[b]
+
+
+@pytest.mark.parametrize("cfg", [2, 4, 5, 3])
+def test_config_full_size_sampled(cfg):
+    """Full-size workload in the launch configuration the benchmark times;
+    the oracle checks a sample of sequences (all their heads and rows)."""
+    w = wl.make(cfg)
+    print(f"cfg {cfg} full: B={w.batch} pages={w.num_pages}", flush=True)
+    g, O, L = _run(w)
+    rng = np.random.default_rng(cfg)
+    longest = int(np.argmax(w.seq_lens))
+    sample = sorted(set([0, w.batch - 1, longest] + list(rng.choice(w.batch, 2, replace=False))))
+    O_ref, L_ref = H.oracle_verify(w, sample)
+    H.compare(O[sample], L[sample], O_ref, L_ref, H.TOL[w.kv_dtype])
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+    ref = H.oracle_block_tables(w)
+    for b in sample:
+        assert g.pool.table(b)[0] == ref[b]
+
+
+def test_permutation_invariance_bitwise():
+    w = wl.make(2, small=True, batch=6)
+    _, O1, L1 = _run(w)
+    perm = np.random.default_rng(5).permutation(w.num_pages).astype(np.int32)
+    g2 = H.GpuSide(w, free_order=perm)
+    O2, L2 = g2.verify()
+    assert g2.pool.table(0)[0] != H.oracle_block_tables(w)[0]
+    assert np.array_equal(O1, O2.cpu().numpy()) and np.array_equal(L1, L2.cpu().numpy())
+
+
+@pytest.mark.parametrize("splits", [1, 3, 17, 64, 1000])
+def test_split_counts_agree(splits):
+    """The stream-K split and the merge give the oracle's result for any
+    number of workgroups (1 = no split, 1000 = many empty ranges)."""
+    w = wl.make(3, small=True)
+    g = H.GpuSide(w)
+    O, L = g.verify(num_splits=splits)
+    O_ref, L_ref = H.oracle_verify(w, range(w.batch))
+    H.compare(O.cpu().numpy(), L.cpu().numpy(), O_ref, L_ref, H.TOL["bf16"])
+
+
+def test_rollback_equals_never_appended():
+    w = wl.make(2, small=True, batch=5)
+    g = H.GpuSide(w)
+    O0, L0 = (x.clone() for x in g.verify())
+    before = [g.pool.table(b) for b in range(w.batch)], g.pool.stats()
+    rng = np.random.default_rng(3)
+    for m in (1, 7, 16, 33):
+        k = torch.randn((w.batch * m, w.num_kv_heads, w.head_dim)).to(torch.bfloat16).cuda()
+        g.pool.append(range(w.batch), [m] * w.batch, k, k.clone())
+        g.pool.rollback(range(w.batch), [m] * w.batch)
+        assert ([g.pool.table(b) for b in range(w.batch)], g.pool.stats()) == before
+        O1, L1 = g.verify()
+        assert torch.equal(O0, O1) and torch.equal(L0, L1)
+
+
+def test_commit_after_partial_accept():
+    """Appending gamma+1 tokens and keeping 1+k of them equals appending
+    only those 1+k (the committed prefix), as seen by later queries."""
+    w = wl.make(2, small=True, batch=4)
+    ks = [0, 2, 4, 1]
+    g = H.GpuSide(w)
+    n_new = 5
+    rng = np.random.default_rng(4)
+    newk = rng.standard_normal((w.batch, n_new, w.num_kv_heads, w.head_dim)).astype(np.float32)
+    newk = wl.bf16_to_f32(wl.bf16_bits(newk))
+    kt = torch.from_numpy(newk.reshape(-1, w.num_kv_heads, w.head_dim)).to(torch.bfloat16).cuda()
+    g.pool.append(range(w.batch), [n_new] * w.batch, kt, kt.clone())
+    g.pool.rollback(range(w.batch), [n_new - 1 - k for k in ks])
+    g2 = H.GpuSide(w)
+    keep = [torch.from_numpy(newk[b, :1 + ks[b]]) for b in range(w.batch)]
+    kk = torch.cat(keep).to(torch.bfloat16).cuda().contiguous()
+    g2.pool.append(range(w.batch), [1 + k for k in ks], kk, kk.clone())
+    # fresh queries over the committed state (n_q = 1: plain decode over everything)
+    q = torch.randn((w.batch, 1, w.num_q_heads, w.head_dim)).to(torch.bfloat16).cuda()
+    O1, L1 = g.pool.verify(q, 1)
+    O1, L1 = O1.clone(), L1.clone()
+    O2, L2 = g2.pool.verify(q, 1)
+    assert [g.pool.table(b)[1] for b in range(w.batch)] == [g2.pool.table(b)[1] for b in range(w.batch)]
+    torch.testing.assert_close(O1, O2, rtol=0, atol=0)
+    torch.testing.assert_close(L1, L2, rtol=0, atol=0)
+
+
+def test_append_layout_bf16_exact():
+    w = wl.make(2, small=True, batch=3)
+    g = H.GpuSide(w)
+    kp = g.pool.k_pages.cpu().numpy().view(np.uint16)
+    vp = g.pool.v_pages.cpu().numpy().view(np.uint16)
+    for b in range(w.batch):
+        pages, n, _ = g.pool.table(b)
+        K = np.concatenate([np.stack([detile_k(kp[p, h], "bf16", w.head_dim)
+                                      for h in range(w.num_kv_heads)], 1) for p in pages])[:n]
+        V = np.concatenate([np.stack([detile_v(vp[p, h], "bf16", w.head_dim)
+                                      for h in range(w.num_kv_heads)], 1) for p in pages])[:n]
+        k, v = w.seq_kv(b)
+        assert np.array_equal(K, wl.bf16_bits(k)) and np.array_equal(V, wl.bf16_bits(v))
+
+
+def test_append_fp8_quantiser_bit_exact():
+    """GPU FP8 codes and per page-head scales equal the oracle quantiser's."""
+    w = wl.make(4, small=True, batch=2)
+    g = H.GpuSide(w)
+    kp = g.pool.k_pages.cpu().numpy()
+    vp = g.pool.v_pages.cpu().numpy()
+    ks = g.pool.k_scale.cpu().numpy()
+    vs = g.pool.v_scale.cpu().numpy()
+    for b in range(w.batch):
+        pages, n, _ = g.pool.table(b)
+        pm = H.opool.PoolModel(len(pages) + 1, 16, w.num_kv_heads, w.head_dim, kv_dtype="fp8")
+        pm.alloc(0)
+        k, v = w.private_kv(b)
+        ctx = int(w.cached_lens[b])
+        pm.append(0, k[:ctx], v[:ctx])
+        pm.append(0, k[ctx:], v[ctx:])
+        for j, p in enumerate(pages):
+            q = pm.tables[0][j]
+            valid = min(16, n - 16 * j)
+            assert np.array_equal(ks[p], pm.ks[q]) and np.array_equal(vs[p], pm.vs[q])
+            for h in range(w.num_kv_heads):
+                Kc = detile_k(kp[p, h], "fp8", w.head_dim)[:valid]
+                Vc = detile_v(vp[p, h], "fp8", w.head_dim)[:valid]
+                assert np.array_equal(Kc, pm.kc[q][h, :valid]), (b, j, h)
+                assert np.array_equal(Vc, pm.vc[q][h, :valid]), (b, j, h)
+
+
+def test_fp8_decode_all_codes():
+    """Every E4M3 code through the verify kernel's decode: one page holding a
+    single visible token whose channels cover all codes; the output equals
+    V = decode(code) * scale exactly (one visible token -> O = V)."""
+    d, Hkv = 128, 1
+    pool = H.Pool(4, Hkv, d, "fp8", max_seqs=1, max_pages_per_seq=2, device="cuda")
+    pool.fill_nan()
+    pool.alloc(0)
+    src = np.zeros((1, Hkv, d), dtype=np.float32)
+    pool.append([0], [1], torch.from_numpy(src).cuda(), torch.from_numpy(src).cuda())
+    codes = np.arange(256, dtype=np.uint8)
+    codes = codes[(codes != 0x7F) & (codes != 0xFF)]
+    page = pool.table(0)[0][0]
+    for part in range(0, len(codes), d):
+        chunk = codes[part:part + d]
+        chunk = np.pad(chunk, (0, d - len(chunk)))
+        vrow = np.zeros((16, d), dtype=np.uint8)
+        vrow[0] = chunk
+        pool.v_pages[page, 0] = torch.from_numpy(tile_v(vrow, "fp8", d)).cuda()
+        pool.v_scale[page, 0] = 1.0
+        q = torch.zeros((1, 1, 1, d), dtype=torch.bfloat16, device="cuda")
+        O, _ = pool.verify(q, 1)
+        assert np.array_equal(O[0, 0, 0].cpu().numpy().astype(np.float64), ofp8.decode(chunk))
+
+
+def test_edge_cases():
+    rng = np.random.default_rng(9)
+    d, Hkv, Hq = 128, 2, 8
+    cases = [  # (cached lengths, n_q)
+        ([0, 0], 5),             # nothing cached: verification slots only
+        ([11, 16], 5),           # page-exact and ragged
+        ([1, 31, 32], 1),        # n_q = 1: plain paged decode
+        ([3, 250], 16),          # 16 queries x G=4 = 64 rows
+        ([2000], 2),
+    ]
+    for lens, n_q in cases:
+        B = len(lens)
+        pool = H.Pool(600, Hkv, d, "bf16", max_seqs=B, max_pages_per_seq=200,
+                      free_order=rng.permutation(600), device="cuda")
+        pool.fill_nan()
+        Ks, Vs = [], []
+        for b, L in enumerate(lens):
+            pool.alloc(b)
+            k = wl.bf16_to_f32(wl.bf16_bits(rng.standard_normal((L + n_q, Hkv, d)).astype(np.float32)))
+            v = wl.bf16_to_f32(wl.bf16_bits(rng.standard_normal((L + n_q, Hkv, d)).astype(np.float32)))
+            pool.append([b], [L + n_q], torch.from_numpy(k).to(torch.bfloat16).cuda(),
+                        torch.from_numpy(v).to(torch.bfloat16).cuda())
+            Ks.append(k.astype(np.float64))
+            Vs.append(v.astype(np.float64))
+        q = wl.bf16_to_f32(wl.bf16_bits(rng.standard_normal((B, n_q, Hq, d)).astype(np.float32)))
+        qt = torch.from_numpy(q).to(torch.bfloat16).cuda()
+        scale = np.float32(1 / np.sqrt(d))
+        for splits in (0, 1, 5):
+            O, L = pool.verify(qt, n_q, sm_scale=scale, num_splits=splits)
+            O_ref, L_ref = H.oa.verify_attention(q.astype(np.float64), Ks, Vs, n_q, None, float(scale))
+            H.compare(O.cpu().numpy(), L.cpu().numpy(), O_ref, L_ref, H.TOL["bf16"])
+
+
+def test_batch_slots():
+    w = wl.make(2, small=True, batch=4)
+    g = H.GpuSide(w)
+    O_all, L_all = (x.clone() for x in g.verify())
+    slots = torch.tensor([3, 1], dtype=torch.int32, device="cuda")
+    q = g.q[[3, 1]].contiguous()
+    from paged_kv_speculative_amd import spec_verify_attention
+    O, L = spec_verify_attention(q, g.pool.k_pages, g.pool.v_pages, g.pool.block_table,
+                                 g.pool.seq_lens, n_q=w.n_q, num_kv_heads=w.num_kv_heads,
+                                 kv_dtype="bf16", batch_slots=slots)
+    assert torch.equal(O, O_all[[3, 1]]) and torch.equal(L, L_all[[3, 1]])

@@ -1,0 +1,199 @@
+"""Host-side tests of libpkvspec.so (no GPU): exports, allocator bookkeeping
+against the oracle pool model, error paths, tree masks."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle.attention import tree_masks
+from oracle.pool import OutOfPages as OracleOOP
+from oracle.pool import PoolModel
+from paged_kv_speculative_amd import OutOfPages, PkvError, Pool, tree_ancestor_masks
+from paged_kv_speculative_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "pkv_spec.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"typedef struct \{.*?\}\s*\w+;", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names) - {"defined"})
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 17
+    lib = C.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_status_strings_and_version():
+    assert _lib.lib.pkv_status_string(0) == b"ok"
+    assert _lib.lib.pkv_status_string(2) == b"out of pages"
+    assert b"gfx950" in _lib.lib.pkv_version()
+    assert _lib.lib.pkv_page_bytes(1, 16, 128) == 4096
+    assert _lib.lib.pkv_page_bytes(2, 16, 128) == 2048
+    assert _lib.lib.pkv_page_bytes(0, 16, 64) == 4096
+    assert _lib.lib.pkv_page_bytes(1, 8, 128) == 0
+
+
+def test_tree_masks_match_oracle():
+    rng = np.random.default_rng(0)
+    for _ in range(50):
+        n = int(rng.integers(1, 65))
+        parents = [-1] + [int(rng.integers(0, i)) for i in range(1, n)]
+        assert tree_ancestor_masks(parents) == tree_masks(parents)
+    with pytest.raises(PkvError):
+        tree_ancestor_masks([0, 0])
+    with pytest.raises(PkvError):
+        tree_ancestor_masks([-1, 2, 0])
+
+
+def _tables_equal(lib_pool, model):
+    for seq in model.tables:
+        pages, length, _ = lib_pool.table(seq)
+        assert pages == model.tables[seq] and length == model.lens[seq], seq
+    st = lib_pool.stats()
+    assert st["free_pages"] == len(model.free)
+    assert st["num_seqs"] == len(model.tables)
+    assert st["cow_copies"] == model.cow_copies
+    for p in range(model.P):
+        assert lib_pool.refcount(p) == model.refcount[p]
+
+
+def test_random_ops_match_oracle_pool():
+    rng = np.random.default_rng(1)
+    P, S = 48, 16
+    order = rng.permutation(P)
+    lib_pool = Pool(P, 1, 64, "bf16", max_seqs=64, max_pages_per_seq=64, free_order=order)
+    model = PoolModel(P, S, 1, 1, free_order=order)
+    live, nid = [], 0
+    for step in range(1500):
+        op = int(rng.integers(0, 6))
+        if op == 0 or not live:
+            src = live[int(rng.integers(len(live)))] if live and rng.random() < 0.6 else None
+            n_sh = int(rng.integers(0, model.lens[src] + 1)) if src is not None else 0
+            model.alloc(nid, src, n_sh)
+            lib_pool.alloc(nid, -1 if src is None else src, n_sh)
+            live.append(nid)
+            nid += 1
+        elif op in (1, 2, 3):
+            k = int(rng.integers(1, min(4, len(live)) + 1))
+            seqs = list(rng.choice(live, size=k, replace=False))
+            ns = [int(rng.integers(0, 40)) for _ in seqs]
+            # the library call is atomic over the batch; mirror it on a copy
+            import copy
+            trial = copy.deepcopy(model)
+            try:
+                for s, n in zip(seqs, ns):
+                    trial.append(s, np.zeros((n, 1, 1)), np.zeros((n, 1, 1)))
+                ok = True
+            except OracleOOP:
+                ok = False
+            if ok:
+                lib_pool.append(seqs, ns)
+                model = trial
+            else:
+                with pytest.raises(OutOfPages):
+                    lib_pool.append(seqs, ns)
+        elif op == 4:
+            s = live[int(rng.integers(len(live)))]
+            n = int(rng.integers(0, model.lens[s] + 1))
+            model.rollback(s, n)
+            lib_pool.rollback([s], [n])
+        else:
+            s = live.pop(int(rng.integers(len(live))))
+            model.release(s)
+            lib_pool.release(s)
+        if step % 10 == 0:
+            _tables_equal(lib_pool, model)
+    _tables_equal(lib_pool, model)
+
+
+def test_rollback_restores_free_set_and_tables():
+    order = np.random.default_rng(2).permutation(40)
+    p = Pool(40, 2, 128, "bf16", free_order=order)
+    p.alloc(7)
+    p.append([7], [37])
+    before = (p.table(7), p.stats())
+    for m in (1, 5, 11, 27):
+        p.append([7], [m])
+        p.rollback([7], [m])
+        assert (p.table(7), p.stats()) == before
+
+
+def test_errors_leave_state_unchanged():
+    p = Pool(4, 1, 64, "bf16", max_seqs=2, max_pages_per_seq=3)
+    p.alloc(1)
+    p.append([1], [20])
+    before = (p.table(1), p.stats())
+    with pytest.raises(OutOfPages):
+        p.alloc(2)
+        p.append([2], [40])           # needs 3 pages, 2 free
+    after_alloc = p.stats()
+    with pytest.raises(PkvError) as e:
+        p.append([1], [40])           # 60 tokens > 3 pages of capacity
+    assert e.value.status == 9
+    with pytest.raises(PkvError) as e:
+        p.append([99], [1])
+    assert e.value.status == 3
+    with pytest.raises(PkvError) as e:
+        p.append([1, 1], [1, 1])
+    assert e.value.status == 1
+    with pytest.raises(PkvError) as e:
+        p.rollback([1], [21])
+    assert e.value.status == 1
+    with pytest.raises(PkvError) as e:
+        p.alloc(1)
+    assert e.value.status == 4
+    with pytest.raises(PkvError) as e:
+        p.alloc(3)                    # both block-table rows in use
+    assert e.value.status == 8
+    with pytest.raises(PkvError) as e:
+        p.alloc(4, 1, 21)             # shared prefix longer than the source
+    assert p.table(1) == before[0]
+    assert p.stats() == after_alloc
+    # a whole-call failure (second sequence does not fit) changes nothing
+    p.release(2)
+    p.alloc(2)
+    snap = (p.table(1), p.table(2), p.stats())
+    with pytest.raises(OutOfPages):
+        p.append([1, 2], [10, 40])
+    assert (p.table(1), p.table(2), p.stats()) == snap
+
+
+def test_shared_prefix_cow_accounting():
+    p = Pool(64, 8, 128, "bf16")
+    p.alloc(0)
+    p.append([0], [800])
+    for s in range(1, 6):
+        p.alloc(s, 0, 800)
+    st = p.stats()
+    assert st["used_pages"] == 50 and st["shared_pages"] == 50
+    # partial shared page -> copy on first append
+    q = Pool(8, 1, 64, "bf16")
+    q.alloc(0)
+    q.append([0], [24])
+    q.alloc(1, 0, 20)
+    q.append([1], [3])
+    assert q.stats()["cow_copies"] == 1
+    assert q.table(1)[0][0] == q.table(0)[0][0] and q.table(1)[0][1] != q.table(0)[0][1]
+
+
+def test_layout_maps_are_bijections():
+    """The documented page layouts place every (token, channel) at a distinct
+    offset inside one slab."""
+    from layout_ref import k_index, v_index
+    for D in (64, 128):
+        t = np.arange(16)[:, None]
+        c = np.arange(D)[None, :]
+        for dt in ("bf16", "fp8"):
+            for f in (lambda: k_index(t, c, dt, D), lambda: v_index(t, c, dt)):
+                idx = f().reshape(-1)
+                assert sorted(idx.tolist()) == list(range(16 * D))
