@@ -1,0 +1,292 @@
+"""Benchmark: one speculative verification step over a paged KV cache on one GPU.
+
+A step is one pass of the whole path over the batch, as a serving loop runs it:
+  1. paged_kv_append       the gamma+1 verification tokens' K/V of every sequence
+  2. spec_verify_attention verification queries over each sequence's pages
+  3. spec_accept           acceptance rule, accepted length, next token
+  4. paged_kv_rollback     commit 1+k tokens, drop the rejected gamma-k
+(the accepted lengths are read back to the host each step, as a serving loop
+must to emit tokens).  Inputs are resident in HBM before the timed region.
+Several independent pool instances are used round-robin so that no step finds
+its KV in the 256 MB last-level cache.
+
+Output: one JSON line.  `value` is whole-step throughput in query tokens per
+second (batch * (gamma+1) / step time); `roofline` is measured on the
+verification attention launch (partial + merge kernels) with HIP events on
+the launch stream.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "verify-attn KV GB/s & % of HBM peak; query-tokens/s at γ=4, 1 GPU"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--instances", type=int, default=0, help="pool copies used round-robin (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM counter scaling)")
+    return ap.parse_args()
+
+
+def kv_bytes(lens, w):
+    """Algorithmic KV bytes of one verification call: every K and V element of
+    every token of every sequence once (the shared prefix counted once), plus
+    the FP8 scales of the pages read."""
+    elem = {"bf16": 2, "f32": 4, "fp8": 1}[w.kv_dtype]
+    per_tok = w.num_kv_heads * 2 * w.head_dim * elem
+    toks = int(np.sum(lens)) - (len(lens) - 1) * w.prefix_len if w.prefix_len else int(np.sum(lens))
+    total = toks * per_tok
+    if w.kv_dtype == "fp8":
+        total += int(np.sum((np.asarray(lens) + 15) // 16)) * w.num_kv_heads * 2 * 4
+    return total
+
+
+class Instance:
+    """One copy of the workload: pool filled with every sequence's context."""
+
+    def __init__(self, w, steps, torch, api, seed_offset):
+        B, S = w.batch, 16
+        self.w = w
+        grow = steps * w.n_q
+        pages = w.num_pages + B * (-(-grow // S) + 2)
+        maxp = int(max(-(-int(n) // S) for n in w.seq_lens)) + -(-grow // S) + 4
+        self.pool = api.Pool(pages, w.num_kv_heads, w.head_dim, w.kv_dtype, max_seqs=B,
+                             max_pages_per_seq=maxp, free_order=np.random.default_rng(
+                                 w.seed + seed_offset).permutation(pages), device="cuda")
+        dt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+        if w.prefix_len:
+            self.pool.alloc(0)
+            pk, pv = w.prefix_kv()
+            self.pool.append([0], [w.prefix_len], torch.from_numpy(pk).to(dt).cuda(),
+                             torch.from_numpy(pv).to(dt).cuda())
+            for b in range(1, B):
+                self.pool.alloc(b, 0, w.prefix_len)
+        else:
+            for b in range(B):
+                self.pool.alloc(b)
+        for b in range(B):
+            k, v = w.private_kv(b)
+            ctx = int(w.cached_lens[b]) - w.prefix_len
+            self.pool.append([b], [ctx], torch.from_numpy(np.ascontiguousarray(k[:ctx])).to(dt).cuda(),
+                             torch.from_numpy(np.ascontiguousarray(v[:ctx])).to(dt).cuda())
+        self.lens = np.asarray(w.cached_lens, dtype=np.int64).copy()
+        # per-step inputs: new K/V of the n_q verification tokens, queries, logits
+        g = torch.Generator(device="cuda")
+        g.manual_seed(w.seed * 7 + seed_offset)
+        n = B * w.n_q
+        self.knew = torch.randn((n, w.num_kv_heads, w.head_dim), generator=g, device="cuda").to(dt)
+        self.vnew = torch.randn((n, w.num_kv_heads, w.head_dim), generator=g, device="cuda").to(dt)
+        self.q = torch.randn((B, w.n_q, w.num_q_heads, w.head_dim), generator=g,
+                             device="cuda").to(torch.bfloat16)
+        self.anc = None
+        if w.tree_parents is not None:
+            m = [api.tree_ancestor_masks(p) for p in w.tree_parents]
+            self.anc = torch.tensor(np.array(m, dtype=np.uint64).view(np.int64), device="cuda")
+        V, gam = w.accept_vocab, w.gamma
+        self.accept = V > 0 and w.tree_parents is None
+        if self.accept:
+            self.T = torch.randn((B, gam + 1, V), generator=g, device="cuda") * w.accept_std
+            self.D = torch.randn((B, gam, V), generator=g, device="cuda") * w.accept_std
+            probs = torch.softmax(self.D.reshape(-1, V), -1)
+            self.x = torch.multinomial(probs, 1, generator=g).reshape(B, gam).to(torch.int32)
+            del probs
+            self.abuf = None
+        self.vbuf = None
+
+
+def run_gpu(args, w, torch, api):
+    B, nq, gam = w.batch, w.n_q, w.gamma
+    total_steps = args.steps + args.warmup
+    one = kv_bytes(w.seq_lens, w)
+    R = args.instances or max(2, int(np.ceil(1.2e9 / max(one, 1))))
+    R = min(R, 8)
+    insts = [Instance(w, -(-total_steps // R) + 1, torch, api, r) for r in range(R)]
+    for I in insts:
+        a = api.api._verify_args(I.q, I.pool.k_pages, I.pool.v_pages, I.pool.block_table,
+                                 I.pool.seq_lens, nq, w.num_kv_heads, w.kv_dtype, I.pool.k_scale,
+                                 I.pool.v_scale, None, I.anc, w.sm_scale, 0)
+        I.vbuf = api.VerifyBuffers(B, nq, w.num_q_heads, w.head_dim, api.verify_workspace_size(a), "cuda")
+        if I.accept:
+            aa = api.api._accept_args(I.T, I.D, I.x, 1, 0)
+            I.abuf = api.AcceptBuffers(B, api.accept_workspace_size(aa), "cuda")
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(total_steps)]
+    acc_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(total_steps)]
+    step_bytes, accepted = [], []
+
+    def step(s):
+        I = insts[s % R]
+        I.pool.append(range(B), [nq] * B, I.knew, I.vnew)
+        I.lens += nq
+        step_bytes.append(kv_bytes(I.lens, w))
+        ev[s][0].record()
+        I.pool.verify(I.q, nq, anc_mask=I.anc, sm_scale=w.sm_scale, buffers=I.vbuf)
+        ev[s][1].record()
+        if I.accept:
+            acc_ev[s][0].record()
+            k, _ = api.spec_accept(I.T, I.D, I.x, seed=12345, step=s, buffers=I.abuf)
+            acc_ev[s][1].record()
+            k = k.cpu().numpy()                       # host needs k (and the tokens) every step
+        else:
+            k = np.full(B, gam, dtype=np.int64)       # tree: commit policy outside this path
+            torch.cuda.synchronize()
+        accepted.append(k.copy())
+        drop = (nq - 1 - k).astype(np.int64)
+        I.pool.rollback(range(B), drop)
+        I.lens -= drop
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, total_steps):
+        step(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timed = range(args.warmup, total_steps)
+    attn_ms = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in timed])
+    attn_bytes = np.array([step_bytes[s] for s in timed], dtype=np.float64)
+    acc_ms = np.array([acc_ev[s][0].elapsed_time(acc_ev[s][1]) for s in timed]) if insts[0].accept else None
+    res = {
+        "wall_s": wall, "steps": args.steps, "instances": R,
+        "attn_ms": attn_ms, "attn_bytes": attn_bytes, "acc_ms": acc_ms,
+        "mean_k": float(np.mean([a.mean() for a in accepted[args.warmup:]])),
+    }
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    return res
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same step: for each
+    sampled sequence its pool replay and gather, verification attention and
+    acceptance.  Single-threaded (BLAS limited to one thread)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import accept as oacc
+    from oracle import attention as oatt
+    from oracle import pool as opool
+    rng = np.random.default_rng(0)
+    done, t_used = 0, 0.0
+    q = w.q_f32().astype(np.float64)
+    T = D = x = None
+    with threadpool_limits(limits=1):
+        for b in range(w.batch):
+            if t_used >= budget_s:
+                break
+            if w.accept_vocab and w.tree_parents is None and T is None:
+                T, D, x = w.accept_inputs(step=0, batch=min(w.batch, 8))
+            t0 = time.perf_counter()
+            n = int(w.seq_lens[b])
+            pm = opool.PoolModel(-(-n // 16) + 2, 16, w.num_kv_heads, w.head_dim,
+                                 kv_dtype="fp8" if w.kv_dtype == "fp8" else "f64")
+            pm.alloc(0)
+            k, v = w.seq_kv(b)
+            ctx = int(w.cached_lens[b])
+            pm.append(0, k[:ctx], v[:ctx])
+            pm.append(0, k[ctx:], v[ctx:])
+            K, V = pm.gather(0)
+            anc = None if w.tree_parents is None else [oatt.tree_masks(w.tree_parents[b])]
+            oatt.verify_attention(q[b:b + 1], [K], [V], w.n_q, anc, float(w.sm_scale))
+            if T is not None:
+                j = b % T.shape[0]
+                oacc.accept_one(T[j], D[j], x[j], 12345, 0, j)
+            t_used += time.perf_counter() - t0
+            done += 1
+    return {"value": done * w.n_q / t_used, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {w.batch} sequences of the same workload (pool replay + gather, "
+                      f"verification attention, acceptance over vocab {w.accept_vocab}), fp64 NumPy, "
+                      f"{t_used:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the verification step shards by sequence or KV head with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import paged_kv_speculative_amd as api
+    from paged_kv_speculative_amd import workloads
+    w = workloads.make(args.config)
+    r = run_gpu(args, w, torch, api)
+    B, nq = w.batch, w.n_q
+    ms_step = 1e3 * r["wall_s"] / args.steps
+    attn_s = r["attn_ms"] / 1e3
+    gbps = r["attn_bytes"] / attn_s / 1e9
+    achieved = float(np.sum(r["attn_bytes"]) / np.sum(attn_s) / 1e9)
+    out = {
+        "metric": METRIC,
+        "value": B * nq / (r["wall_s"] / args.steps),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype != "fp8" else "fp8-kv/bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{workloads.CONFIG_NAMES[args.config]}: batch {B}, {w.num_q_heads} q / "
+                        f"{w.num_kv_heads} KV heads, head_dim {w.head_dim}, {w.kv_dtype} KV, page 16, "
+                        f"cached context {int(w.cached_lens.min())}..{int(w.cached_lens.max())}, "
+                        f"n_q {nq} ({'tree' if w.tree_parents else 'chain'})"
+                        + (f", acceptance over vocab {w.accept_vocab}" if w.accept_vocab else ""),
+            "batch": B, "n_q": nq, "gamma": w.gamma, "instances": r["instances"],
+        },
+        "verify_attn": {
+            "kv_gbps": achieved,
+            "hbm_frac": achieved / HBM_PEAK_GBPS,
+            "us_median": float(np.median(r["attn_ms"]) * 1e3),
+            "us_p10": float(np.percentile(r["attn_ms"], 10) * 1e3),
+            "us_p90": float(np.percentile(r["attn_ms"], 90) * 1e3),
+            "kv_gbps_median": float(np.median(gbps)),
+            "kv_bytes_per_call": float(np.mean(r["attn_bytes"])),
+            "query_tokens_per_s": float(B * nq / np.median(attn_s)),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": None,
+        },
+    }
+    if r["acc_ms"] is not None:
+        lb = B * (2 * w.gamma + 1) * w.accept_vocab * 4
+        out["spec_accept"] = {"us_median": float(np.median(r["acc_ms"]) * 1e3),
+                              "logit_gbps": lb / (np.median(r["acc_ms"]) / 1e3) / 1e9,
+                              "mean_accepted": r["mean_k"]}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -224,10 +224,13 @@ typedef struct {
   float sm_scale;             /* usually 1/sqrt(head_dim)                        */
   float* out;                 /* device [batch][n_q][Hq][head_dim] fp32          */
   float* lse;                 /* device [batch][n_q][Hq] fp32, may be NULL       */
-  void* workspace;            /* device, >= spec_verify_workspace_size bytes     */
+  void* workspace;            /* device, >= spec_verify_workspace_size bytes;
+                                 scratch for partial results of contexts split
+                                 over workgroups; calls that share a workspace
+                                 must not overlap in time                        */
   size_t workspace_bytes;
-  int32_t num_splits;         /* workgroups sharing the work; 0 = one per slot
-                                 the GPU can keep resident                       */
+  int32_t num_splits;         /* workgroups sharing the work; 0 = as many as the
+                                 GPU keeps resident                              */
 } pkv_verify_args;
 
 pkv_status spec_verify_workspace_size(const pkv_verify_args* args, size_t* bytes_out);

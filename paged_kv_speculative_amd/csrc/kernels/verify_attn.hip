@@ -40,6 +40,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "../common.h"
 
 namespace pkv {
@@ -68,10 +72,11 @@ struct VerifyParams {
   const unsigned long long* anc;
   float* out;
   float* lse;
-  float* part;           // [n_wg][2][slot_floats]
-  int* cum_ws;           // [batch + 1] page prefix sums, written by workgroup 0
+  float* part;           // [n_wg][2][slot_floats] partial (O, max, sum) of split units
+  int* cum;              // [batch + 1] page prefix sums (written by workgroup 0)
   long slab_bytes;       // bytes of one (page, KV head) slab
   int batch, n_q, Hq, Hkv, G, rows, bt_stride, n_wg;
+  int min_range;         // fewest page-heads per workgroup range
   float scale_log2;      // sm_scale * log2(e)
 };
 
@@ -106,18 +111,70 @@ __device__ inline Dw2 fp8x4_to_bf16x4(unsigned w) {
 
 __device__ inline u32x4 load16(const void* p) { return *static_cast<const u32x4*>(p); }
 
-template <int D, bool FP8>
-struct PageRegs {
-  static constexpr int KS = D / 32;                    // k-steps of the score MFMA
-  static constexpr int KL = FP8 ? KS / 2 : KS;         // 16-byte K loads per page
-  static constexpr int VL = FP8 ? D / 64 : D / 32;     // 16-byte V loads per page
-  u32x4 k[2][KL];
-  u32x4 v[2][VL];
-  int id[2];
-  bool has_y;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Scalar (SMEM) buffer load of one dword.  Block-table entries and FP8 scales
+// are read through the scalar unit so that waiting for them never waits for
+// the vector loads of K/V in flight (vector-memory counters retire in order).
+__device__ int s_buffer_load_dword(i32x4 rsrc, int offset, int cachepolicy)
+    __asm("llvm.amdgcn.s.buffer.load.i32");
+
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format,
+// no swizzle): with stride 0, num_records counts bytes.
+constexpr int kBufferFlags = 0x00020000;
+
+__device__ inline i32x4 scalar_rsrc(const void* base, unsigned bytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  return i32x4{int(unsigned(a)), int(unsigned(a >> 32) & 0xFFFFu), int(bytes), kBufferFlags};
+}
+
+// Maximum over the four lanes {l, l^16, l^32, l^48} of a wave: the lanes that
+// hold one score row.  v_permlane32_swap / v_permlane16_swap exchange halves
+// and 16-lane rows between two registers in the VALU.
+__device__ inline float row_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ inline f32x4 mfma_bf16_k16(unsigned a0, unsigned a1, unsigned b0, unsigned b1, const f32x4& c) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, u32x2{a0, a1}),
+                                                   __builtin_bit_cast(s16x4, u32x2{b0, b1}), c, 0, 0, 0);
+}
+
+// Compile-time shape of the streaming kernel for one (head_dim, row tiles, KV type).
+template <int D, int NT, bool FP8>
+struct Shape {
+  static constexpr int KS = D / 32;                  // k-steps of the score MFMA (32 channels)
+  static constexpr int DT = D / 16;                  // 16-channel tiles of the output
+  static constexpr int KL = FP8 ? KS / 2 : KS;       // 16-byte K loads per page
+  static constexpr int VL = FP8 ? D / 64 : D / 32;   // 16-byte V loads per page
+  // pages in flight per wave while one page is computed
+  static constexpr int PF = FP8 ? (NT <= 2 ? 8 : (NT == 3 ? 5 : 3)) : (NT <= 2 ? 5 : (NT == 3 ? 3 : 2));
 };
 
-// Inclusive-exclusive prefix of pages per sequence into s_cum[0..batch].
+template <int D, bool FP8>
+struct PageRegs {
+  static constexpr int KL = Shape<D, 1, FP8>::KL, VL = Shape<D, 1, FP8>::VL;
+  u32x4 k[KL];
+  u32x4 v[VL];
+};
+
+// Where a ring slot's page sits: sequence, KV head, page, and the
+// sequence's length (all wave-uniform).
+struct PageMeta {
+  int b, g, page, np, n, valid, ks_bits, vs_bits;
+};
+
+// Values every lane of the wave holds alike (read from LDS or computed from
+// such reads): moved to scalar registers so addresses built from them stay
+// scalar.
+__device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Exclusive prefix of pages per sequence into s_cum[0..batch].
 __device__ void page_prefix(const VerifyParams& P, int* s_cum, int* s_tmp) {
   const int tid = threadIdx.x;
   const int per = (P.batch + kThreads - 1) / kThreads;
@@ -145,350 +202,10 @@ __device__ void page_prefix(const VerifyParams& P, int* s_cum, int* s_tmp) {
   __syncthreads();
 }
 
+// Work range of worker w out of n over W positions: [lo(w), lo(w+1)).
 __device__ inline long range_lo(long w, long W, long n) { return w * W / n; }
 
-template <int D, int NT, bool FP8, bool TREE>
-__device__ void process_segment(const VerifyParams& P, int b, int g, int p0, int p1, bool full,
-                                int slot, float* s_red, float* s_m, float* s_l) {
-  using Regs = PageRegs<D, FP8>;
-  constexpr int KS = Regs::KS;
-  constexpr int DT = D / 16;
-  constexpr int RP = D + 4;                       // padded LDS row
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int m16 = lane & 15, jg = lane >> 4;
-  const int row_b = P.batch_slots ? P.batch_slots[b] : b;
-  const int N = P.seq_lens[row_b];
-  const int L = N - P.n_q;
-  const int* bt = P.block_table + long(row_b) * P.bt_stride;
-  const unsigned lane_off = unsigned(m16 * 64 + jg * 16);
-
-  // Q fragments (B operand of S^T = K Q^T): row 16nt+m16, channels (D/4)jg + 8s .. +7.
-  u32x4 qf[NT][KS];
-  int qi[NT];                      // verification slot of the row (padding rows: 64)
-  unsigned long long anc[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = nt * 16 + m16;
-    qi[nt] = 64;
-    anc[nt] = ~0ull;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[nt][s] = u32x4{0, 0, 0, 0};
-    if (r < P.rows) {
-      const int i = r / P.G, h = g * P.G + r % P.G;
-      qi[nt] = i;
-      const unsigned short* qp = static_cast<const unsigned short*>(P.q) +
-                                 (long(b * P.n_q + i) * P.Hq + h) * D + (D / 4) * jg;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) qf[nt][s] = load16(qp + 8 * s);
-      if (TREE) anc[nt] = P.anc[long(b) * P.n_q + i];
-    }
-  }
-
-  float m_run[NT], l_run[NT];
-  f32x4 acc[DT][NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m_run[nt] = kNegInf;
-    l_run[nt] = 0.0f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt][nt] = f32x4{0, 0, 0, 0};
-  }
-
-  const char* kbase = P.k_pages + long(g) * P.slab_bytes;
-  const char* vbase = P.v_pages + long(g) * P.slab_bytes;
-  const long page_stride = long(P.Hkv) * P.slab_bytes;
-  const int npairs = (p1 - p0 + 1) >> 1;
-
-  auto load_pair = [&](Regs& R, int q) {
-    const int px = p0 + 2 * q;
-    R.has_y = px + 1 < p1;
-    R.id[0] = bt[px];
-    R.id[1] = R.has_y ? bt[px + 1] : R.id[0];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const char* kp = kbase + R.id[x] * page_stride + lane_off;
-      const char* vp = vbase + R.id[x] * page_stride + lane_off;
-      if (x == 1 && !R.has_y) {
-#pragma unroll
-        for (int u = 0; u < Regs::KL; ++u) R.k[1][u] = u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int c = 0; c < Regs::VL; ++c) R.v[1][c] = u32x4{0, 0, 0, 0};
-      } else {
-#pragma unroll
-        for (int u = 0; u < Regs::KL; ++u) R.k[x][u] = load16(kp + u * 1024);
-#pragma unroll
-        for (int c = 0; c < Regs::VL; ++c) R.v[x][c] = load16(vp + c * 1024);
-      }
-    }
-  };
-
-  auto compute_pair = [&](Regs& R, int q) {
-    const int px = p0 + 2 * q;
-    const int tok0 = px * 16;                   // first token of page X
-    const bool need_mask = tok0 + 32 > L;       // pair reaches the verification slots or the end
-
-    // scores S^T (lane: row 16nt+m16, tokens 4jg..4jg+3 of each page)
-    f32x4 sc[2][NT];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        f32x4 a = f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          u32x4 kf;
-          if (FP8) {
-            const u32x4 w = R.k[x][s >> 1];
-            const int o = (s & 1) * 2;
-            const Dw2 a0 = fp8x4_to_bf16x4(w[o]), a1 = fp8x4_to_bf16x4(w[o + 1]);
-            kf = u32x4{a0.lo, a0.hi, a1.lo, a1.hi};
-          } else {
-            kf = R.k[x][s];
-          }
-          a = mfma_bf16(kf, qf[nt][s], a);
-        }
-        sc[x][nt] = a;
-      }
-    }
-    float ksc[2] = {P.scale_log2, P.scale_log2};
-    float vsc[2] = {1.0f, 1.0f};
-    if (FP8) {
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        ksc[x] *= P.k_scale[long(R.id[x]) * P.Hkv + g];
-        vsc[x] = P.v_scale[long(R.id[x]) * P.Hkv + g];
-      }
-    }
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sc[x][nt][e] *= ksc[x];
-
-    if (need_mask || !R.has_y) {
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = tok0 + 16 * x + 4 * jg + e;
-          const int j = t - L;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            bool vis;
-            if (TREE) vis = (t < L) || (t < N && ((anc[nt] >> (j & 63)) & 1ull));
-            else vis = (t < L) || (t < N && j <= qi[nt]);
-            if (x == 1 && !R.has_y) vis = false;
-            sc[x][nt][e] = vis ? sc[x][nt][e] : kNegInf;
-          }
-        }
-      }
-      // zero V of tokens at or past N (stale slots may hold anything)
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int valid = (x == 1 && !R.has_y) ? 0 : min(4, max(0, N - (tok0 + 16 * x + 4 * jg)));
-        if (FP8) {
-          const unsigned keep = valid >= 4 ? 0xFFFFFFFFu : ((1u << (8 * valid)) - 1u);
-#pragma unroll
-          for (int c = 0; c < Regs::VL; ++c)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) R.v[x][c][w] &= keep;
-        } else {
-          const unsigned keep0 = valid >= 2 ? 0xFFFFFFFFu : (valid == 1 ? 0xFFFFu : 0u);
-          const unsigned keep1 = valid >= 4 ? 0xFFFFFFFFu : (valid == 3 ? 0xFFFFu : 0u);
-#pragma unroll
-          for (int c = 0; c < Regs::VL; ++c) {
-            R.v[x][c][0] &= keep0;
-            R.v[x][c][1] &= keep1;
-            R.v[x][c][2] &= keep0;
-            R.v[x][c][3] &= keep1;
-          }
-        }
-      }
-    }
-
-    // online softmax (base 2) and P^T operands
-    u32x4 phi[NT], plo[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float mx = fmaxf(fmaxf(fmaxf(sc[0][nt][0], sc[0][nt][1]), fmaxf(sc[0][nt][2], sc[0][nt][3])),
-                       fmaxf(fmaxf(sc[1][nt][0], sc[1][nt][1]), fmaxf(sc[1][nt][2], sc[1][nt][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[nt], mx);
-      const float m_ref = m_new == kNegInf ? 0.0f : m_new;
-      const float alpha = exp2_fast(m_run[nt] - m_ref);
-      m_run[nt] = m_new;
-      float p[2][4];
-      float psum = 0.0f;
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[x][e] = exp2_fast(sc[x][nt][e] - m_ref);
-          psum += p[x][e];
-        }
-      l_run[nt] = l_run[nt] * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt][nt] *= alpha;
-      if (FP8) {
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) p[x][e] *= vsc[x];
-      }
-      float hi[2][4], lo[2][4];
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          hi[x][e] = __uint_as_float(__float_as_uint(p[x][e]) & 0xFFFF0000u);
-          lo[x][e] = __uint_as_float(rne_bf16_bits(p[x][e] - hi[x][e]));
-        }
-      phi[nt] = u32x4{pack_hi16(hi[0][0], hi[0][1]), pack_hi16(hi[0][2], hi[0][3]),
-                      pack_hi16(hi[1][0], hi[1][1]), pack_hi16(hi[1][2], hi[1][3])};
-      plo[nt] = u32x4{pack_hi16(lo[0][0], lo[0][1]), pack_hi16(lo[0][2], lo[0][3]),
-                      pack_hi16(lo[1][0], lo[1][1]), pack_hi16(lo[1][2], lo[1][3])};
-    }
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      u32x4 vf;
-      if (FP8) {
-        const int c = dt >> 2, w = dt & 3;
-        const Dw2 a0 = fp8x4_to_bf16x4(R.v[0][c][w]), a1 = fp8x4_to_bf16x4(R.v[1][c][w]);
-        vf = u32x4{a0.lo, a0.hi, a1.lo, a1.hi};
-      } else {
-        const int c = dt >> 1, w = (dt & 1) * 2;
-        vf = u32x4{R.v[0][c][w], R.v[0][c][w + 1], R.v[1][c][w], R.v[1][c][w + 1]};
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        acc[dt][nt] = mfma_bf16(vf, phi[nt], acc[dt][nt]);
-        acc[dt][nt] = mfma_bf16(vf, plo[nt], acc[dt][nt]);
-      }
-    }
-  };
-
-  // software pipeline: the next pair's loads are in flight while a pair is
-  // computed; two register sets alternate so nothing is copied
-  int q = wave;
-  Regs ra, rb;
-  if (q < npairs) load_pair(ra, q);
-  while (q < npairs) {
-    if (q + kWaves < npairs) load_pair(rb, q + kWaves);
-    compute_pair(ra, q);
-    q += kWaves;
-    if (q >= npairs) break;
-    if (q + kWaves < npairs) load_pair(ra, q + kWaves);
-    compute_pair(rb, q);
-    q += kWaves;
-  }
-
-  // ---- combine the four waves ---------------------------------------------
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    l_run[nt] += __shfl_xor(l_run[nt], 16, 64);
-    l_run[nt] += __shfl_xor(l_run[nt], 32, 64);
-  }
-  __syncthreads();                              // previous segment's LDS readers are done
-  if (jg == 0) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      s_m[wave * 64 + nt * 16 + m16] = m_run[nt];
-      s_l[wave * 64 + nt * 16 + m16] = l_run[nt];
-    }
-  }
-  __syncthreads();
-  const long slot_floats = long(NT) * 16 * (D + 2);
-  float* part = P.part + (long(blockIdx.x) * 2 + slot) * slot_floats;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = nt * 16 + m16;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w * 64 + r]);
-    const float Mref = M == kNegInf ? 0.0f : M;
-    const float f = exp2_fast(m_run[nt] - Mref);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int ch = FP8 ? (dt >> 2) * 64 + 16 * jg + 4 * e + (dt & 3)
-                           : (dt >> 1) * 32 + 8 * jg + 2 * e + (dt & 1);
-        s_red[(wave * 16 + m16) * RP + ch] = acc[dt][nt][e] * f;
-      }
-    __syncthreads();
-    for (int idx = tid; idx < 16 * D; idx += kThreads) {
-      const int rr = idx / D, ch = idx % D, rw = nt * 16 + rr;
-      if (rw < P.rows) {
-        float Mr = kNegInf;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) Mr = fmaxf(Mr, s_m[w * 64 + rw]);
-        const float Mrr = Mr == kNegInf ? 0.0f : Mr;
-        float Lr = 0.0f, o = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          Lr += s_l[w * 64 + rw] * exp2_fast(s_m[w * 64 + rw] - Mrr);
-          o += s_red[(w * 16 + rr) * RP + ch];
-        }
-        if (full) {
-          const int i = rw / P.G, h = g * P.G + rw % P.G;
-          const long oi = long(b * P.n_q + i) * P.Hq + h;
-          P.out[oi * D + ch] = o / Lr;
-          if (ch == 0 && P.lse) P.lse[oi] = (Mr + __log2f(Lr)) * kLn2;
-        } else {
-          part[rw * D + ch] = o;
-          if (ch == 0) {
-            part[NT * 16 * D + rw] = Mr;
-            part[NT * 16 * D + NT * 16 + rw] = Lr;
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
-}
-
-template <int D, int NT, bool FP8, bool TREE>
-__global__ __launch_bounds__(kThreads) void verify_partial_kernel(VerifyParams P) {
-  extern __shared__ float smem[];
-  int* s_cum = reinterpret_cast<int*>(smem);
-  const int cum_words = (P.batch + 1 + 3) & ~3;
-  float* s_red = smem + cum_words;
-  float* s_m = s_red + kWaves * 16 * (D + 4);
-  float* s_l = s_m + kWaves * 64;
-
-  page_prefix(P, s_cum, reinterpret_cast<int*>(s_red));
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i <= P.batch; i += kThreads) P.cum_ws[i] = s_cum[i];
-
-  const long W = long(P.Hkv) * s_cum[P.batch];
-  const long lo = range_lo(blockIdx.x, W, P.n_wg), hi = range_lo(blockIdx.x + 1, W, P.n_wg);
-  long pos = lo;
-  while (pos < hi) {
-    // sequence b: last b with Hkv * cum[b] <= pos
-    int a = 0, z = P.batch - 1;
-    while (a < z) {
-      const int mid = (a + z + 1) >> 1;
-      if (long(P.Hkv) * s_cum[mid] <= pos) a = mid;
-      else z = mid - 1;
-    }
-    const int b = a;
-    const int np = s_cum[b + 1] - s_cum[b];
-    const long base = long(P.Hkv) * s_cum[b];
-    const int g = int((pos - base) / np);
-    const int p0 = int((pos - base) % np);
-    const long seg_end = min(hi, base + long(g + 1) * np);
-    const int p1 = p0 + int(seg_end - pos);
-    process_segment<D, NT, FP8, TREE>(P, b, g, p0, p1, p0 == 0 && p1 == np, pos == lo ? 0 : 1,
-                                      s_red, s_m, s_l);
-    pos = seg_end;
-  }
-}
-
-// Workgroup whose range holds work position p (lo(w) <= p < lo(w+1)).
+// Worker whose range holds position p (all ranges are non-empty: n <= W).
 __device__ inline int owner_of(long p, long W, int n) {
   int w = int(p * n / W);
   while (w + 1 < n && range_lo(w + 1, W, n) <= p) ++w;
@@ -496,42 +213,458 @@ __device__ inline int owner_of(long p, long W, int n) {
   return w;
 }
 
-template <int D, int NT>
-__global__ __launch_bounds__(256) void verify_merge_kernel(VerifyParams P) {
+// The running maximum of a row is only moved when the block maximum exceeds
+// it by more than this (log2 units), so P <= 2^8 and the O rescale is rare.
+constexpr float kRescaleSlack = 8.0f;
+
+// Pieces of one split unit whose slots and weights are kept in LDS by the merge.
+constexpr int kMaxPieces = 64;
+
+// Floats of one partial slot: O [rows][D], then max [rows], then sum [rows].
+__device__ __host__ inline long slot_floats(int rows, int D) { return long(rows) * (D + 2); }
+
+// Cursor over work positions (sequence b, KV head g, page) in that order.
+struct Cursor {
+  int b, g, page, np, row, n;
+};
+
+template <int D, int NT, bool FP8, bool TREE>
+__device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, int hi, int worker) {
+  using SH = Shape<D, NT, FP8>;
+  using Regs = PageRegs<D, FP8>;
+  constexpr int KS = SH::KS, DT = SH::DT, PF = SH::PF;
+  const int lane = threadIdx.x & 63;
+  const int m16 = lane & 15, jg = lane >> 4;
+  const unsigned lane_off = unsigned(m16 * 64 + jg * 16);
+  const long page_stride = long(P.Hkv) * P.slab_bytes;
+  const i32x4 ks_rsrc = scalar_rsrc(P.k_scale, 0xFFFFFFFFu);
+  const i32x4 vs_rsrc = scalar_rsrc(P.v_scale, 0xFFFFFFFFu);
+  const i32x4 len_rsrc = scalar_rsrc(P.seq_lens, 0xFFFFFFFFu);
+  const i32x4 slot_rsrc = scalar_rsrc(P.batch_slots, P.batch_slots ? unsigned(P.batch) * 4u : 0u);
+
+  // ---- cursor helpers (all scalar) -----------------------------------------
+  auto seq_info = [&](Cursor& c) {
+    c.np = uni(s_cum[c.b + 1]) - uni(s_cum[c.b]);
+    c.row = P.batch_slots ? s_buffer_load_dword(slot_rsrc, c.b * 4, 0) : c.b;
+    c.n = s_buffer_load_dword(len_rsrc, c.row * 4, 0);
+  };
+  auto locate = [&](int pos) {
+    int a = 0, z = P.batch - 1;
+    while (a < z) {
+      const int mid = (a + z + 1) >> 1;
+      if (P.Hkv * uni(s_cum[mid]) <= pos) a = mid;
+      else z = mid - 1;
+    }
+    Cursor c;
+    c.b = a;
+    seq_info(c);
+    const int off = pos - P.Hkv * uni(s_cum[a]);
+    c.g = off / c.np;
+    c.page = off - c.g * c.np;
+    return c;
+  };
+  auto advance = [&](Cursor& c) {
+    if (++c.page < c.np) return;
+    c.page = 0;
+    if (++c.g < P.Hkv) return;
+    c.g = 0;
+    do {
+      ++c.b;
+    } while (c.b < P.batch - 1 && uni(s_cum[c.b + 1]) == uni(s_cum[c.b]));
+    if (c.b >= P.batch) c.b = P.batch - 1;    // past the end: only null loads follow
+    seq_info(c);
+  };
+  auto bt_rsrc = [&](const Cursor& c) {
+    return scalar_rsrc(P.block_table + long(c.row) * P.bt_stride, unsigned(c.np) * 4u);
+  };
+
+  // ---- loads ---------------------------------------------------------------
+  // Bounds-checked buffer loads of one page: a position outside the range
+  // gets num_records = 0, which returns zeros without touching memory.
+  auto load_page = [&](Regs& R, PageMeta& M, const Cursor& c, int id, bool valid) {
+    const int nrec = valid ? int(P.slab_bytes) : 0;
+    const char* kb = P.k_pages + long(id) * page_stride + long(c.g) * P.slab_bytes;
+    const char* vb = P.v_pages + long(id) * page_stride + long(c.g) * P.slab_bytes;
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kb), 0, nrec, kBufferFlags);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vb), 0, nrec, kBufferFlags);
+#pragma unroll
+    for (int u = 0; u < SH::KL; ++u)
+      R.k[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off + u * 1024, 0, 0));
+#pragma unroll
+    for (int cc = 0; cc < SH::VL; ++cc)
+      R.v[cc] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off + cc * 1024, 0, 0));
+    M.b = c.b;
+    M.g = c.g;
+    M.page = c.page;
+    M.np = c.np;
+    M.n = c.n;
+    M.valid = valid;
+    if (FP8) {
+      M.ks_bits = s_buffer_load_dword(ks_rsrc, (id * P.Hkv + c.g) * 4, 0);
+      M.vs_bits = s_buffer_load_dword(vs_rsrc, (id * P.Hkv + c.g) * 4, 0);
+    }
+  };
+  // Q fragments (B operand of S^T = K Q^T) of unit (b, g): row 16nt+m16,
+  // channels (D/4)jg + 8s .. +7; rows past n_q*G read row 0 (never output).
+  auto load_q = [&](u32x4 (&q)[NT][KS], unsigned long long (&an)[NT], int b, int g) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int r = nt * 16 + m16 < P.rows ? nt * 16 + m16 : 0;
+      const int i = r / P.G, h = g * P.G + r % P.G;
+      const unsigned short* qp = static_cast<const unsigned short*>(P.q) +
+                                 (long(b * P.n_q + i) * P.Hq + h) * D + (D / 4) * jg;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) q[nt][s] = load16(qp + 8 * s);
+      if (TREE) an[nt] = P.anc[long(b) * P.n_q + i];
+    }
+  };
+
+  // ---- per-unit state --------------------------------------------------------
+  int qi[NT];                     // verification slot of the row (padding rows: 64)
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) qi[nt] = nt * 16 + m16 < P.rows ? (nt * 16 + m16) / P.G : 64;
+  u32x4 qf[NT][KS], qn[NT][KS];
+  unsigned long long anc[NT], ancn[NT];
+  int qn_tag = -1;                // unit whose Q is in qn
+  float m_run[NT], l_run[NT];
+  f32x4 acc[DT][NT];
+  int u_b = -1, u_g = 0, u_first = 0, u_last = 0, u_np = 0, u_n = 0, units_done = 0;
+
+  auto finalize = [&]() {
+    const bool full = u_first == 0 && u_last == u_np - 1;
+    const int slot = units_done == 0 ? 0 : 1;
+    float* part = P.part + (long(worker) * 2 + slot) * slot_floats(P.rows, D);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float l = l_run[nt];
+      l += __shfl_xor(l, 16, 64);
+      l += __shfl_xor(l, 32, 64);
+      const int r = nt * 16 + m16;
+      if (r < P.rows) {
+        const float inv = full ? 1.0f / l : 1.0f;
+        const int i = r / P.G, h = u_g * P.G + r % P.G;
+        const long oi = long(u_b * P.n_q + i) * P.Hq + h;
+        float* dst = full ? P.out + oi * D : part + long(r) * D;
+        if (FP8) {
+#pragma unroll
+          for (int c = 0; c < D / 64; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int ch = c * 64 + 16 * jg + 4 * e;
+              *reinterpret_cast<float4*>(dst + ch) =
+                  make_float4(acc[4 * c][nt][e] * inv, acc[4 * c + 1][nt][e] * inv,
+                              acc[4 * c + 2][nt][e] * inv, acc[4 * c + 3][nt][e] * inv);
+            }
+        } else {
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c) {
+            const int ch = c * 32 + 8 * jg;
+            *reinterpret_cast<float4*>(dst + ch) =
+                make_float4(acc[2 * c][nt][0] * inv, acc[2 * c + 1][nt][0] * inv,
+                            acc[2 * c][nt][1] * inv, acc[2 * c + 1][nt][1] * inv);
+            *reinterpret_cast<float4*>(dst + ch + 4) =
+                make_float4(acc[2 * c][nt][2] * inv, acc[2 * c + 1][nt][2] * inv,
+                            acc[2 * c][nt][3] * inv, acc[2 * c + 1][nt][3] * inv);
+          }
+        }
+        if (jg == 0) {
+          if (full) {
+            if (P.lse) P.lse[oi] = (m_run[nt] + __log2f(l)) * kLn2;
+          } else {
+            part[long(P.rows) * D + r] = m_run[nt];
+            part[long(P.rows) * D + P.rows + r] = l;
+          }
+        }
+      }
+    }
+    ++units_done;
+  };
+
+  auto compute_page = [&](Regs& R, const PageMeta& M) {
+    const int tok0 = M.page * 16;
+    const int L = M.n - P.n_q;
+    // scores S^T (lane: row 16nt+m16, tokens tok0 + 4jg .. +3)
+    f32x4 sc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 a = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        u32x4 kf;
+        if (FP8) {
+          const u32x4 w = R.k[s >> 1];
+          const int o = (s & 1) * 2;
+          const Dw2 a0 = fp8x4_to_bf16x4(w[o]), a1 = fp8x4_to_bf16x4(w[o + 1]);
+          kf = u32x4{a0.lo, a0.hi, a1.lo, a1.hi};
+        } else {
+          kf = R.k[s];
+        }
+        a = mfma_bf16(kf, qf[nt][s], a);
+      }
+      sc[nt] = a;
+    }
+    float ksc = P.scale_log2, vsc = 1.0f;
+    if (FP8) {
+      ksc *= __int_as_float(M.ks_bits);
+      vsc = __int_as_float(M.vs_bits);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[nt][e] *= ksc;
+
+    if (tok0 + 16 > L) {                         // page reaches the verification slots or the end
+      const int N = M.n;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = tok0 + 4 * jg + e;
+        const int j = t - L;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          bool vis;
+          if (TREE) vis = (t < L) || (t < N && ((anc[nt] >> (j & 63)) & 1ull));
+          else vis = (t < L) || (t < N && j <= qi[nt]);
+          sc[nt][e] = vis ? sc[nt][e] : kNegInf;
+        }
+      }
+      // zero V of tokens at or past N (stale slots may hold anything)
+      const int valid = min(4, max(0, N - (tok0 + 4 * jg)));
+      if (FP8) {
+        const unsigned keep = valid >= 4 ? 0xFFFFFFFFu : ((1u << (8 * valid)) - 1u);
+#pragma unroll
+        for (int c = 0; c < SH::VL; ++c)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) R.v[c][w] &= keep;
+      } else {
+        const unsigned keep0 = valid >= 2 ? 0xFFFFFFFFu : (valid == 1 ? 0xFFFFu : 0u);
+        const unsigned keep1 = valid >= 4 ? 0xFFFFFFFFu : (valid == 3 ? 0xFFFFu : 0u);
+#pragma unroll
+        for (int c = 0; c < SH::VL; ++c) {
+          R.v[c][0] &= keep0;
+          R.v[c][1] &= keep1;
+          R.v[c][2] &= keep0;
+          R.v[c][3] &= keep1;
+        }
+      }
+    }
+
+    // online softmax (base 2, lazy rescale) and the P^T operands
+    unsigned ph[NT][2], pl[NT][2];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float mx = row_max4(fmaxf(fmaxf(sc[nt][0], sc[nt][1]), fmaxf(sc[nt][2], sc[nt][3])));
+      const bool grow = mx > m_run[nt] + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mx : m_run[nt];
+        const float alpha = grow ? exp2_fast(m_run[nt] - m_new) : 1.0f;
+        l_run[nt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt][nt] *= alpha;
+        m_run[nt] = m_new;
+      }
+      const float m_ref = m_run[nt] == kNegInf ? 0.0f : m_run[nt];
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = exp2_fast(sc[nt][e] - m_ref);
+      l_run[nt] += (p[0] + p[1]) + (p[2] + p[3]);
+      if (FP8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] *= vsc;
+      }
+      float hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = __uint_as_float(__float_as_uint(p[e]) & 0xFFFF0000u);
+        lo[e] = __uint_as_float(rne_bf16_bits(p[e] - hi[e]));
+      }
+      ph[nt][0] = pack_hi16(hi[0], hi[1]);
+      ph[nt][1] = pack_hi16(hi[2], hi[3]);
+      pl[nt][0] = pack_hi16(lo[0], lo[1]);
+      pl[nt][1] = pack_hi16(lo[2], lo[3]);
+    }
+
+    // O^T += V^T P^T  (16 tokens of the page per MFMA)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      unsigned v0, v1;
+      if (FP8) {
+        const Dw2 a = fp8x4_to_bf16x4(R.v[dt >> 2][dt & 3]);
+        v0 = a.lo;
+        v1 = a.hi;
+      } else {
+        const int w = (dt & 1) * 2;
+        v0 = R.v[dt >> 1][w];
+        v1 = R.v[dt >> 1][w + 1];
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[dt][nt] = mfma_bf16_k16(v0, v1, ph[nt][0], ph[nt][1], acc[dt][nt]);
+        acc[dt][nt] = mfma_bf16_k16(v0, v1, pl[nt][0], pl[nt][1], acc[dt][nt]);
+      }
+    }
+  };
+
+  // ---- the stream ---------------------------------------------------------------
+  // Positions lo..hi-1 are computed in order; the loads of position i + PF are
+  // issued while position i is computed, continuing across unit and sequence
+  // boundaries, and the page id of position i + PF + 1 is fetched one step
+  // ahead through the scalar unit.  The loop body is straight-line (positions
+  // past hi are null loads, and their compute is skipped by a uniform branch),
+  // so the compiler's wait counts keep all PF pages in flight.
+  Regs ring[PF + 1];
+  PageMeta meta[PF + 1];
+  Cursor c = locate(lo);
+  const int len = hi - lo;
+  int id_pend = s_buffer_load_dword(bt_rsrc(c), c.page * 4, 0);
+  auto prefetch = [&](Regs& R, PageMeta& M, int rel) {
+    const bool valid = rel < len;
+    if (valid && (c.page == 0 || rel == 0)) {  // a new unit enters the ring: fetch its Q
+      load_q(qn, ancn, c.b, c.g);
+      qn_tag = c.b * P.Hkv + c.g;
+    }
+    load_page(R, M, c, id_pend, valid);
+    if (rel + 1 < len) {
+      advance(c);
+      id_pend = s_buffer_load_dword(bt_rsrc(c), c.page * 4, 0);
+    }
+  };
+#pragma unroll
+  for (int r = 0; r < PF; ++r) prefetch(ring[r], meta[r], r);
+  for (int i0 = 0; i0 < len; i0 += PF + 1) {
+#pragma unroll
+    for (int r = 0; r <= PF; ++r) {
+      const int i = i0 + r;
+      prefetch(ring[(r + PF) % (PF + 1)], meta[(r + PF) % (PF + 1)], i + PF);
+      const PageMeta& M = meta[r];
+      if (M.valid) {
+        if (M.b != u_b || M.g != u_g) {          // a new unit starts at this position
+          if (u_b >= 0) finalize();
+          const int unit = M.b * P.Hkv + M.g;
+          if (qn_tag == unit) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              anc[nt] = ancn[nt];
+#pragma unroll
+              for (int s = 0; s < KS; ++s) qf[nt][s] = qn[nt][s];
+            }
+          } else {
+            load_q(qf, anc, M.b, M.g);           // its Q was overwritten in the ring window
+          }
+          u_b = M.b;
+          u_g = M.g;
+          u_first = M.page;
+          u_np = M.np;
+          u_n = M.n;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            m_run[nt] = kNegInf;
+            l_run[nt] = 0.0f;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt][nt] = f32x4{0, 0, 0, 0};
+          }
+        }
+        u_last = M.page;
+        compute_page(ring[r], M);
+      }
+    }
+  }
+  if (u_b >= 0) finalize();
+}
+
+// Merge of the units split over workers: one workgroup per (sequence, KV
+// head); a unit finished in place by one worker is skipped.  The pieces are
+// combined with the log-sum-exp rule.  Each thread finds the pieces of its
+// unit itself and issues every load it needs (the pieces' maxima, sums and
+// float4s of O) before using any, so the kernel waits for memory once.
+template <int D>
+__global__ __launch_bounds__(kThreads) void verify_merge_kernel(VerifyParams P) {
+  extern __shared__ int s_lo[];                 // [n_eff + 1] worker range starts
   const int b = blockIdx.x / P.Hkv, g = blockIdx.x % P.Hkv;
-  const int* cum = P.cum_ws;
+  const int tid = threadIdx.x;
+  const int* __restrict__ cum = P.cum;
   const long W = long(P.Hkv) * cum[P.batch];
+  if (W == 0) return;
   const int np = cum[b + 1] - cum[b];
-  if (np == 0 || W == 0) return;
+  if (np == 0) return;
+  const int n_eff = int(min(long(P.n_wg) * kWaves, max(1L, W / P.min_range)));
   const long u0 = long(P.Hkv) * cum[b] + long(g) * np, u1 = u0 + np;
-  const int wf = owner_of(u0, W, P.n_wg), wl = owner_of(u1 - 1, W, P.n_wg);
-  if (wf == wl) return;                       // finished in place by one workgroup
-  const long slot_floats = long(NT) * 16 * (D + 2);
-  const int RW = NT * 16;
-  for (int idx = threadIdx.x; idx < P.rows * D; idx += blockDim.x) {
-    const int r = idx / D, ch = idx % D;
-    float M = kNegInf;
-    for (int w = wf; w <= wl; ++w) {
-      if (range_lo(w + 1, W, P.n_wg) == range_lo(w, W, P.n_wg)) continue;   // empty range
-      const int slot = (w == wf && range_lo(w, W, P.n_wg) != u0) ? 1 : 0;
-      const float* pt = P.part + (long(w) * 2 + slot) * slot_floats;
-      M = fmaxf(M, pt[RW * D + r]);
+  for (int w = tid; w <= n_eff; w += kThreads) s_lo[w] = int(range_lo(w, W, n_eff));
+  __syncthreads();
+  auto owner = [&](long p) {
+    int a = 0, z = n_eff - 1;
+    while (a < z) {
+      const int mid = (a + z + 1) >> 1;
+      if (s_lo[mid] <= p) a = mid;
+      else z = mid - 1;
     }
-    const float Mref = M == kNegInf ? 0.0f : M;
-    float Ls = 0.0f, o = 0.0f;
-    for (int w = wf; w <= wl; ++w) {
-      if (range_lo(w + 1, W, P.n_wg) == range_lo(w, W, P.n_wg)) continue;
-      const int slot = (w == wf && range_lo(w, W, P.n_wg) != u0) ? 1 : 0;
-      const float* pt = P.part + (long(w) * 2 + slot) * slot_floats;
-      const float f = exp2_fast(pt[RW * D + r] - Mref);
-      Ls += pt[RW * D + RW + r] * f;
-      o += pt[r * D + ch] * f;
+    return a;
+  };
+  const int wf = owner(u0), wl = owner(u1 - 1);
+  if (wf == wl) return;                         // finished in place
+  const long sf = slot_floats(P.rows, D);
+  const int R = P.rows;
+  const float* __restrict__ part = P.part;
+  constexpr int KB = 8;                          // pieces handled per batch of loads
+  for (int x = tid; x < R * (D / 4); x += kThreads) {
+    const int r = x / (D / 4), c4 = x % (D / 4);
+    float M = kNegInf, Ls = 0.0f;
+    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int w0 = wf; w0 <= wl; w0 += KB) {
+      float mk[KB], lk[KB];
+      float4 v[KB];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int w = min(w0 + u, wl);
+        const long base = (2L * w + ((w == wf && s_lo[w] != u0) ? 1 : 0)) * sf;
+        mk[u] = part[base + long(R) * D + r];
+        lk[u] = part[base + long(R) * D + R + r];
+        v[u] = *reinterpret_cast<const float4*>(part + base + long(r) * D + 4 * c4);
+      }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        if (w0 + u > wl) break;
+        // online log-sum-exp combine of piece u into (M, Ls, o)
+        const float mn = fmaxf(M, mk[u]);
+        const float ref = mn == kNegInf ? 0.0f : mn;
+        const float a = exp2_fast(M - ref), c = exp2_fast(mk[u] - ref);
+        Ls = Ls * a + lk[u] * c;
+        o.x = o.x * a + v[u].x * c;
+        o.y = o.y * a + v[u].y * c;
+        o.z = o.z * a + v[u].z * c;
+        o.w = o.w * a + v[u].w * c;
+        M = mn;
+      }
     }
+    const float inv = 1.0f / Ls;
     const int i = r / P.G, h = g * P.G + r % P.G;
     const long oi = long(b * P.n_q + i) * P.Hq + h;
-    P.out[oi * D + ch] = o / Ls;
-    if (ch == 0 && P.lse) P.lse[oi] = (M + __log2f(Ls)) * kLn2;
+    *reinterpret_cast<float4*>(P.out + oi * D + 4 * c4) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+    if (c4 == 0 && P.lse) P.lse[oi] = (M + __log2f(Ls)) * kLn2;
   }
+}
+
+template <int D>
+size_t split_smem(int batch) {
+  const int cum_words = (batch + 1 + 3) & ~3;
+  return size_t(cum_words + kThreads) * sizeof(int);
+}
+
+// Each wave is one worker streaming an equal contiguous range of the
+// (sequence, KV head, page) positions.
+template <int D, int NT, bool FP8, bool TREE>
+__global__ __launch_bounds__(kThreads) void verify_stream_kernel(VerifyParams P) {
+  extern __shared__ int s_cum[];
+  const int cum_words = (P.batch + 1 + 3) & ~3;
+  page_prefix(P, s_cum, s_cum + cum_words);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= P.batch; i += kThreads) P.cum[i] = s_cum[i];
+  const int W = P.Hkv * uni(s_cum[P.batch]);
+  if (W == 0) return;
+  const int worker = blockIdx.x * kWaves + uni(threadIdx.x >> 6);
+  const int n_eff = int(min(long(P.n_wg) * kWaves, max(1L, long(W) / P.min_range)));
+  if (worker >= n_eff) return;
+  const int lo = int(range_lo(worker, W, n_eff)), hi = int(range_lo(worker + 1, W, n_eff));
+  stream_range<D, NT, FP8, TREE>(P, s_cum, lo, hi, worker);
 }
 
 // fp32 K/V (plain [token][channel] pages): one workgroup per (query head,
@@ -608,38 +741,13 @@ __global__ __launch_bounds__(128) void verify_f32_kernel(VerifyParams P) {
   }
 }
 
-struct DeviceInfo {
-  int cus = 0;
-};
-
-DeviceInfo device_info() {
-  static thread_local int cached_dev = -1;
-  static thread_local DeviceInfo info;
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  if (dev != cached_dev) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    info.cus = cus;
-    cached_dev = dev;
-  }
-  return info;
-}
-
-template <int D, int NT>
-size_t partial_smem(int batch) {
-  const int cum_words = (batch + 1 + 3) & ~3;
-  return size_t(cum_words + kWaves * 16 * (D + 4) + 2 * kWaves * 64) * sizeof(float);
-}
-
 struct Plan {
   int D, NT, rows, n_wg;
   bool fp8, tree, f32;
   size_t cum_bytes, part_bytes;
 };
 
-pkv_status make_plan(const pkv_verify_args* a, Plan* pl) {
+pkv_status check_args(const pkv_verify_args* a, Plan* pl) {
   if (!a) return fail(PKV_ERR_INVALID_ARG, "null args");
   if (a->batch < 1 || a->batch > 4096) return fail(PKV_ERR_INVALID_ARG, "batch must be in [1, 4096]");
   if (a->n_q < 1 || a->n_q > 64) return fail(PKV_ERR_INVALID_ARG, "n_q must be in [1, 64]");
@@ -650,6 +758,8 @@ pkv_status make_plan(const pkv_verify_args* a, Plan* pl) {
   if (a->block_table_stride < 1) return fail(PKV_ERR_INVALID_ARG, "block_table_stride must be >= 1");
   if (!a->q || !a->k_pages || !a->v_pages || !a->block_table || !a->seq_lens)
     return fail(PKV_ERR_INVALID_ARG, "null device pointer");
+  if (a->num_splits < 0 || a->num_splits > 1024)
+    return fail(PKV_ERR_INVALID_ARG, "num_splits must be in [0, 1024]");
   const int G = a->num_q_heads / a->num_kv_heads;
   pl->D = a->head_dim;
   pl->rows = a->n_q * G;
@@ -668,27 +778,82 @@ pkv_status make_plan(const pkv_verify_args* a, Plan* pl) {
     return fail(PKV_ERR_INVALID_ARG, "unknown dtype");
   }
   pl->NT = (pl->rows + 15) / 16;
-  if (a->num_splits < 0) return fail(PKV_ERR_INVALID_ARG, "num_splits must be >= 0");
+  return PKV_OK;
+}
+
+// Resident workgroups of one kernel instance per GPU (cached per device,
+// instance and LDS size).
+int resident_workgroups(const void* fn, size_t smem) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, size_t>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  std::lock_guard<std::mutex> lock(mu);
+  auto key = std::make_tuple(dev, fn, smem);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, smem) != hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  (void)hipGetLastError();
+  const int n = cus * per_cu;
+  cache[key] = n;
+  return n;
+}
+
+template <int D, int NT, bool FP8, bool TREE>
+const void* split_fn() {
+  return reinterpret_cast<const void*>(&verify_stream_kernel<D, NT, FP8, TREE>);
+}
+
+template <int D, int NT>
+const void* pick_fn(bool fp8, bool tree) {
+  if (fp8) return tree ? split_fn<D, NT, true, true>() : split_fn<D, NT, true, false>();
+  return tree ? split_fn<D, NT, false, true>() : split_fn<D, NT, false, false>();
+}
+
+template <int D>
+const void* pick_fn(int NT, bool fp8, bool tree) {
+  switch (NT) {
+    case 1: return pick_fn<D, 1>(fp8, tree);
+    case 2: return pick_fn<D, 2>(fp8, tree);
+    case 3: return pick_fn<D, 3>(fp8, tree);
+    default: return pick_fn<D, 4>(fp8, tree);
+  }
+}
+
+pkv_status make_plan(const pkv_verify_args* a, Plan* pl) {
+  pkv_status st = check_args(a, pl);
+  if (st != PKV_OK) return st;
   pl->cum_bytes = 0;
   pl->part_bytes = 0;
   pl->n_wg = 0;
   if (!pl->f32) {
     int n = a->num_splits;
-    if (n == 0) n = device_info().cus * 2;
+    if (n == 0) {
+      const size_t smem = pl->D == 64 ? split_smem<64>(a->batch) : split_smem<128>(a->batch);
+      const void* fn = pl->D == 64 ? pick_fn<64>(pl->NT, pl->fp8, pl->tree)
+                                   : pick_fn<128>(pl->NT, pl->fp8, pl->tree);
+      n = resident_workgroups(fn, smem);
+    }
     pl->n_wg = n;
     pl->cum_bytes = ((size_t(a->batch) + 1) * sizeof(int) + 255) & ~size_t(255);
-    pl->part_bytes = size_t(n) * 2 * pl->NT * 16 * (pl->D + 2) * sizeof(float);
+    pl->part_bytes = size_t(n) * kWaves * 2 * size_t(pl->rows) * (pl->D + 2) * sizeof(float);
   }
   return PKV_OK;
 }
 
 template <int D, int NT, bool FP8, bool TREE>
 hipError_t launch_split(const VerifyParams& p, hipStream_t st) {
-  const size_t smem = partial_smem<D, NT>(p.batch);
-  hipLaunchKernelGGL((verify_partial_kernel<D, NT, FP8, TREE>), dim3(p.n_wg), dim3(kThreads), smem, st, p);
+  hipLaunchKernelGGL((verify_stream_kernel<D, NT, FP8, TREE>), dim3(p.n_wg), dim3(kThreads),
+                     split_smem<D>(p.batch), st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((verify_merge_kernel<D, NT>), dim3(p.batch * p.Hkv), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((verify_merge_kernel<D>), dim3(p.batch * p.Hkv), dim3(kThreads),
+                     size_t(p.n_wg * kWaves + 1) * sizeof(int), st, p);
   return hipGetLastError();
 }
 
@@ -743,8 +908,9 @@ extern "C" pkv_status spec_verify_attention(const pkv_verify_args* a, void* stre
   p.anc = reinterpret_cast<const unsigned long long*>(a->anc_mask);
   p.out = a->out;
   p.lse = a->lse;
-  p.cum_ws = static_cast<int*>(a->workspace);
+  p.cum = static_cast<int*>(a->workspace);
   p.part = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + pl.cum_bytes);
+  p.min_range = a->num_splits == 0 ? 8 : 1;
   p.slab_bytes = pkv_page_bytes(a->kv_dtype, a->page_size, a->head_dim);
   p.batch = a->batch;
   p.n_q = a->n_q;
