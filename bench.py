@@ -105,8 +105,7 @@ class Instance:
             probs = torch.softmax(self.D.reshape(-1, V), -1)
             self.x = torch.multinomial(probs, 1, generator=g).reshape(B, gam).to(torch.int32)
             del probs
-            self.abuf = None
-        self.vbuf = None
+        self.verify = self.accept_call = None
 
 
 def run_gpu(args, w, torch, api):
@@ -117,39 +116,40 @@ def run_gpu(args, w, torch, api):
     R = min(R, 8)
     insts = [Instance(w, -(-total_steps // R) + 1, torch, api, r) for r in range(R)]
     for I in insts:
-        a = api.api._verify_args(I.q, I.pool.k_pages, I.pool.v_pages, I.pool.block_table,
-                                 I.pool.seq_lens, nq, w.num_kv_heads, w.kv_dtype, I.pool.k_scale,
-                                 I.pool.v_scale, None, I.anc, w.sm_scale, 0)
-        I.vbuf = api.VerifyBuffers(B, nq, w.num_q_heads, w.head_dim, api.verify_workspace_size(a), "cuda")
+        I.verify = I.pool.prepare_verify(I.q, nq, anc_mask=I.anc, sm_scale=w.sm_scale)
         if I.accept:
-            aa = api.api._accept_args(I.T, I.D, I.x, 1, 0)
-            I.abuf = api.AcceptBuffers(B, api.accept_workspace_size(aa), "cuda")
+            I.accept_call = api.PreparedAccept(I.T, I.D, I.x, seed=12345)
+    seq_ids = np.arange(B, dtype=np.int64)
+    n_new = np.full(B, nq, dtype=np.int32)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(total_steps)]
     acc_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(total_steps)]
-    step_bytes, accepted = [], []
+    step_lens, accepted = [], []
+    k_host = torch.empty(B, dtype=torch.int32, pin_memory=True)
 
     def step(s):
         I = insts[s % R]
-        I.pool.append(range(B), [nq] * B, I.knew, I.vnew)
+        I.pool.append(seq_ids, n_new, I.knew, I.vnew)
         I.lens += nq
-        step_bytes.append(kv_bytes(I.lens, w))
+        step_lens.append(I.lens.copy())
         ev[s][0].record()
-        I.pool.verify(I.q, nq, anc_mask=I.anc, sm_scale=w.sm_scale, buffers=I.vbuf)
+        I.verify()
         ev[s][1].record()
         if I.accept:
             acc_ev[s][0].record()
-            k, _ = api.spec_accept(I.T, I.D, I.x, seed=12345, step=s, buffers=I.abuf)
+            k, _ = I.accept_call(step=s)
             acc_ev[s][1].record()
-            k = k.cpu().numpy()                       # host needs k (and the tokens) every step
+            k_host.copy_(k, non_blocking=True)        # host needs k (and the tokens) every step
+            torch.cuda.current_stream().synchronize()
+            k = k_host.numpy()
         else:
-            k = np.full(B, gam, dtype=np.int64)       # tree: commit policy outside this path
+            k = np.full(B, gam, dtype=np.int32)       # tree: commit policy outside this path
             torch.cuda.synchronize()
         accepted.append(k.copy())
-        drop = (nq - 1 - k).astype(np.int64)
-        I.pool.rollback(range(B), drop)
+        drop = (nq - 1) - k
+        I.pool.rollback(seq_ids, drop)
         I.lens -= drop
 
     for s in range(args.warmup):
@@ -162,7 +162,7 @@ def run_gpu(args, w, torch, api):
     wall = time.perf_counter() - t0
     timed = range(args.warmup, total_steps)
     attn_ms = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in timed])
-    attn_bytes = np.array([step_bytes[s] for s in timed], dtype=np.float64)
+    attn_bytes = np.array([kv_bytes(step_lens[s], w) for s in timed], dtype=np.float64)
     acc_ms = np.array([acc_ev[s][0].elapsed_time(acc_ev[s][1]) for s in timed]) if insts[0].accept else None
     res = {
         "wall_s": wall, "steps": args.steps, "instances": R,

@@ -130,7 +130,8 @@ pkv_status paged_kv_alloc(pkv_pool* pool, int64_t seq, int64_t share_from, int32
  * atomic).  Pages are taken at 16-token boundaries; a partly filled tail page
  * shared with another sequence is copied first (copy-on-write,
  * PagedKVCacheManager.EnsureCapacityAndAppendToken).  k_src/v_src are device
- * arrays [sum(n_tokens)][Hkv][head_dim] in src_dtype, sequences in call order.
+ * arrays [sum(n_tokens)][Hkv][head_dim] in src_dtype, sequences in call order,
+ * 16-byte aligned.
  * Allowed src_dtype: the pool dtype for F32/BF16 pools; PKV_F32 for FP8
  * pools, which quantise with the page's scale (a fresh page gets
  * scale = amax/448 of the tokens this call writes into it, per KV head; a page
@@ -259,7 +260,7 @@ pkv_status spec_verify_attention(const pkv_verify_args* args, void* stream);
 typedef struct {
   int32_t batch;
   int32_t gamma;              /* drafts per sequence, 1..64                      */
-  int32_t vocab;
+  int32_t vocab;              /* 1..2^26                                         */
   const float* target_logits; /* device [batch][gamma+1][vocab]                  */
   const float* draft_logits;  /* device [batch][gamma][vocab]                    */
   const int32_t* draft_tokens;/* device [batch][gamma], values in [0, vocab)     */
@@ -267,7 +268,10 @@ typedef struct {
   uint32_t step;
   int32_t* accepted_len;      /* device [batch]                                  */
   int32_t* next_token;        /* device [batch]                                  */
-  void* workspace;            /* device, >= spec_accept_workspace_size bytes     */
+  void* workspace;            /* device, >= spec_accept_workspace_size bytes,
+                                 16-byte aligned; scratch for per-chunk partial
+                                 results; calls that share a workspace must not
+                                 overlap in time                                 */
   size_t workspace_bytes;
 } pkv_accept_args;
 

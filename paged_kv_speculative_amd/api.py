@@ -23,6 +23,15 @@ def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
 
 
+def _ints(values, dtype):
+    """A C array view of a sequence of integers (list, range or ndarray)."""
+    a = np.ascontiguousarray(np.asarray(values, dtype=dtype))
+    if a.ndim != 1:
+        a = a.reshape(-1)
+    ctype = C.c_int64 if dtype == np.int64 else C.c_int32
+    return a, a.ctypes.data_as(C.POINTER(ctype))
+
+
 def page_bytes(kv_dtype, head_dim, page_size=PAGE_SIZE):
     return int(lib.pkv_page_bytes(DTYPES[kv_dtype], page_size, head_dim))
 
@@ -104,21 +113,28 @@ class Pool:
         return slot.value
 
     def append(self, seqs, n_tokens, k_src=None, v_src=None, stream=None):
-        seqs, n_tokens = list(seqs), list(n_tokens)
+        sa, sp = _ints(seqs, np.int64)
+        na, np_ = _ints(n_tokens, np.int32)
+        assert sa.size == na.size
         src_dtype, kp, vp = F32, None, None
-        if self.device is not None and sum(n_tokens) > 0:
+        if self.device is not None and int(na.sum()) > 0:
             assert k_src.is_contiguous() and v_src.is_contiguous() and k_src.dtype == v_src.dtype
-            assert k_src.numel() >= sum(n_tokens) * self.num_kv_heads * self.head_dim
+            assert k_src.numel() >= int(na.sum()) * self.num_kv_heads * self.head_dim
             src_dtype = _TORCH_SRC[k_src.dtype]
+            if k_src.data_ptr() % 16:
+                k_src = k_src.clone()
+            if v_src.data_ptr() % 16:
+                v_src = v_src.clone()
             kp, vp = _ptr(k_src), _ptr(v_src)
         st = _stream(stream) if self.device is not None else None
-        check(lib.paged_kv_append(self._h, len(seqs), i64_array(seqs), i32_array(n_tokens),
-                                  kp, vp, src_dtype, st))
+        check(lib.paged_kv_append(self._h, sa.size, sp, np_, kp, vp, src_dtype, st))
 
     def rollback(self, seqs, n_tokens, stream=None):
-        seqs, n_tokens = list(seqs), list(n_tokens)
+        sa, sp = _ints(seqs, np.int64)
+        na, np_ = _ints(n_tokens, np.int32)
+        assert sa.size == na.size
         st = _stream(stream) if self.device is not None else None
-        check(lib.paged_kv_rollback(self._h, len(seqs), i64_array(seqs), i32_array(n_tokens), st))
+        check(lib.paged_kv_rollback(self._h, sa.size, sp, np_, st))
 
     def release(self, seq, stream=None):
         st = _stream(stream) if self.device is not None else None
@@ -149,6 +165,14 @@ class Pool:
         return self._slots[int(seq)]
 
     # -- verification over this pool --------------------------------------------
+    def prepare_verify(self, q, n_q, slots=None, anc_mask=None, sm_scale=None, buffers=None,
+                       num_splits=0):
+        return PreparedVerify(q, self.k_pages, self.v_pages, self.block_table, self.seq_lens,
+                              n_q=n_q, num_kv_heads=self.num_kv_heads, kv_dtype=self.kv_dtype,
+                              k_scale=self.k_scale, v_scale=self.v_scale, batch_slots=slots,
+                              anc_mask=anc_mask, sm_scale=sm_scale, buffers=buffers,
+                              num_splits=num_splits)
+
     def verify(self, q, n_q, slots=None, anc_mask=None, sm_scale=None, buffers=None, num_splits=0,
                stream=None):
         return spec_verify_attention(
@@ -216,6 +240,33 @@ def spec_verify_attention(q, k_pages, v_pages, block_table, seq_lens, *, n_q, nu
     return buffers.out, buffers.lse
 
 
+class PreparedVerify:
+    """spec_verify_attention with its arguments marshalled once.  The launch
+    reads the tensors given here (queries, pages, block table, lengths) at
+    call time, so a serving loop that updates them in place calls this once
+    per step; returns (out, lse) from the buffers it owns."""
+
+    def __init__(self, q, k_pages, v_pages, block_table, seq_lens, *, n_q, num_kv_heads, kv_dtype,
+                 k_scale=None, v_scale=None, batch_slots=None, anc_mask=None, sm_scale=None,
+                 buffers=None, num_splits=0):
+        a = _verify_args(q, k_pages, v_pages, block_table, seq_lens, n_q, num_kv_heads, kv_dtype,
+                         k_scale, v_scale, batch_slots, anc_mask, sm_scale, num_splits)
+        ws = verify_workspace_size(a)
+        if buffers is None:
+            B, _, Hq, d = q.shape
+            buffers = VerifyBuffers(B, n_q, Hq, d, ws, q.device)
+        assert buffers.workspace.numel() >= ws
+        a.out, a.lse = buffers.out.data_ptr(), buffers.lse.data_ptr()
+        a.workspace, a.workspace_bytes = buffers.workspace.data_ptr(), buffers.workspace.numel()
+        self.args, self.buffers = a, buffers
+        self._keep = (q, k_pages, v_pages, block_table, seq_lens, k_scale, v_scale, batch_slots,
+                      anc_mask)
+
+    def __call__(self, stream=None):
+        check(lib.spec_verify_attention(C.byref(self.args), _stream(stream)))
+        return self.buffers.out, self.buffers.lse
+
+
 def _accept_args(target_logits, draft_logits, draft_tokens, seed, step):
     B, g1, V = target_logits.shape
     assert draft_logits.shape == (B, g1 - 1, V) and draft_tokens.shape == (B, g1 - 1)
@@ -252,3 +303,27 @@ def spec_accept(target_logits, draft_logits, draft_tokens, seed, step, buffers=N
     a.workspace, a.workspace_bytes = buffers.workspace.data_ptr(), buffers.workspace.numel()
     check(lib.spec_accept(C.byref(a), _stream(stream)))
     return buffers.accepted_len, buffers.next_token
+
+
+class PreparedAccept:
+    """spec_accept with its arguments marshalled once; each call takes the
+    step counter (and optionally a new seed) and reads the logits and draft
+    tokens in place.  Returns (accepted_len, next_token) buffers it owns."""
+
+    def __init__(self, target_logits, draft_logits, draft_tokens, seed, buffers=None):
+        a = _accept_args(target_logits, draft_logits, draft_tokens, seed, 0)
+        ws = accept_workspace_size(a)
+        if buffers is None:
+            buffers = AcceptBuffers(a.batch, ws, target_logits.device)
+        assert buffers.workspace.numel() >= ws
+        a.accepted_len, a.next_token = buffers.accepted_len.data_ptr(), buffers.next_token.data_ptr()
+        a.workspace, a.workspace_bytes = buffers.workspace.data_ptr(), buffers.workspace.numel()
+        self.args, self.buffers = a, buffers
+        self._keep = (target_logits, draft_logits, draft_tokens)
+
+    def __call__(self, step, seed=None, stream=None):
+        self.args.step = int(step) & 0xFFFFFFFF
+        if seed is not None:
+            self.args.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+        check(lib.spec_accept(C.byref(self.args), _stream(stream)))
+        return self.buffers.accepted_len, self.buffers.next_token

@@ -8,18 +8,23 @@
 // keeps the target distribution exact); after gamma accepts it is drawn from
 // P_gamma (the bonus token).
 //
-// Two kernels:
-//  1. row statistics: one workgroup per logit row (gamma+1 target rows and
-//     gamma draft rows per sequence) streams the row once with 16-byte loads
-//     and reduces max and sum(exp) to the log-normaliser; the workgroup of
-//     target row gamma also draws the bonus token by Gumbel-max;
-//  2. decision: one workgroup per sequence computes all gamma acceptance
-//     tests, finds k, and if k < gamma streams rows k of target and draft to
-//     draw the residual token by Gumbel-max.
+// The work is one pass over every logit row (the normalisers) and one pass
+// over the row pair the draw needs, each cut into chunks of logits so
+// that a launch holds thousands of workgroups with every load of a thread in
+// flight at once:
+//  1. stats: workgroup (row, chunk) reduces max and sum(exp) of its chunk
+//     (8192 logits, eight 16-byte loads per thread, all in flight);
+//  2. draw: workgroup (sequence, chunk of 2048) combines the row partials into log
+//     normalisers, runs the gamma acceptance tests in one wave (lane i tests
+//     draft i), and computes its chunk's Gumbel-max candidate for the token
+//     drawn at position k (residual, or bonus when k = gamma);
+//  3. finish: one wave per sequence takes the best candidate.
 // Uniforms are Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) keyed by the
 // 64-bit seed; counters are documented in pkv_spec.h.  Drawing by argmax of
 // Gumbel-perturbed log weights needs no prefix sum over the vocabulary and its
-// outcome is an argmax, stable under rounding differences.
+// outcome is an argmax, stable under rounding differences.  Keys are kept in
+// base-2 units (every key of one draw scaled by 1/ln 2 and shifted by one
+// constant), which leaves the argmax unchanged.
 
 #include <hip/hip_runtime.h>
 
@@ -30,7 +35,16 @@ namespace pkv {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kStatsQuads = 8;                            // 16-byte loads per thread
+constexpr int kStatsChunk = kThreads * kStatsQuads * 4;   // logits per stats workgroup
+constexpr int kDrawQuads = 2;
+constexpr int kDrawChunk = kThreads * kDrawQuads * 4;     // logits per draw workgroup
+constexpr int kMaxVocab = 1 << 26;
+constexpr int kMaxBatch = 1 << 20;
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr unsigned kPurposeAccept = 1u, kPurposeSample = 2u;
 
 struct Philox4 {
@@ -39,9 +53,11 @@ struct Philox4 {
 
 __device__ inline Philox4 philox4x32_10(unsigned c0, unsigned c1, unsigned c2, unsigned c3,
                                         unsigned k0, unsigned k1) {
+#pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const unsigned lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
-    const unsigned lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    const unsigned long long p0 = 0xD2511F53ull * c0, p1 = 0xCD9E8D57ull * c2;
+    const unsigned lo0 = unsigned(p0), hi0 = unsigned(p0 >> 32);
+    const unsigned lo1 = unsigned(p1), hi1 = unsigned(p1 >> 32);
     const unsigned n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0;
     c1 = lo1;
@@ -58,7 +74,23 @@ __device__ inline float uniform01(unsigned w) {
   return (float(w >> 9) + 0.5f) * 1.1920928955078125e-7f;
 }
 
-__device__ inline float gumbel(float u) { return -logf(-logf(u)); }
+__device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// Gumbel noise -ln(-ln u) in base-2 units, less the constant log2(ln 2):
+// -log2(-log2 u).  u is at least 2^-24 and at most 1 - 2^-24, so both
+// logarithms see normal arguments.
+__device__ inline float gumbel2(float u) { return -log2_hw(-log2_hw(u)); }
+
+// log2(1 - 2^d) for d < 0.  Near 0 the difference 1 - 2^d cancels, so it is
+// taken from the Taylor series of 1 - e^t (t = d ln 2), whose truncation error
+// for |t| <= 0.35 is below 1e-7 relative.
+__device__ inline float log2_one_minus_exp2(float d) {
+  const float t = d * kLn2;
+  // 1 - e^t = -t (1 + t/2 + t^2/6 + t^3/24 + t^4/120 + t^5/720)
+  const float p = 1.0f + t * (0.5f + t * (1.0f / 6 + t * (1.0f / 24 + t * (1.0f / 120 + t * (1.0f / 720)))));
+  return log2_hw(t > -0.35f ? -t * p : 1.0f - exp2_hw(d));
+}
 
 struct AcceptParams {
   const float* T;
@@ -66,22 +98,13 @@ struct AcceptParams {
   const int* tokens;
   int* accepted_len;
   int* next_token;
-  float* lse;          // [batch][2*gamma+1]: target rows 0..gamma, then draft rows
-  float* bonus_key;    // [batch]
-  int* bonus_tok;      // [batch]
-  int batch, gamma, vocab;
+  float2* stats;       // [batch][2*gamma+1][schunks] (max, sum exp) in base 2
+  int4* cand;          // [batch][dchunks] (residual key bits, index, fallback key bits, index)
+  int batch, gamma, vocab, schunks, dchunks;
   unsigned k0, k1, step;
 };
 
-// Block-wide combine of (max, sum) pairs; result valid in all threads.
-__device__ inline void combine_ms(float& m, float& s, float m2, float s2) {
-  const float mn = fmaxf(m, m2);
-  if (mn == kNegInf) return;
-  s = s * expf(m - mn) + s2 * expf(m2 - mn);
-  m = mn;
-}
-
-// Block-wide argmax of (key, index): larger key wins, ties to smaller index.
+// Argmax of (key, index): larger key wins, ties to the smaller index.
 __device__ inline void better(float& k, int& i, float k2, int i2) {
   if (k2 > k || (k2 == k && i2 < i)) {
     k = k2;
@@ -89,66 +112,72 @@ __device__ inline void better(float& k, int& i, float k2, int i2) {
   }
 }
 
-__device__ void block_argmax(float& key, int& idx, float* sk, int* si) {
-  for (int o = 32; o > 0; o >>= 1) {
-    const float k2 = __shfl_xor(key, o, 64);
-    const int i2 = __shfl_xor(idx, o, 64);
-    better(key, idx, k2, i2);
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) {
-    sk[wave] = key;
-    si[wave] = idx;
-  }
-  __syncthreads();
-  key = sk[0];
-  idx = si[0];
-  for (int w = 1; w < kThreads / 64; ++w) better(key, idx, sk[w], si[w]);
+// (max, sum 2^(v - max)) pairs in base 2.
+__device__ inline void combine_ms(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == kNegInf) return;
+  s = s * exp2_hw(m - mn) + s2 * exp2_hw(m2 - mn);
+  m = mn;
 }
 
-__global__ __launch_bounds__(kThreads) void accept_rowstats_kernel(AcceptParams P) {
-  const int rows_per_seq = 2 * P.gamma + 1;
-  const int b = blockIdx.x / rows_per_seq, j = blockIdx.x % rows_per_seq;
-  const float* row = j <= P.gamma ? P.T + (long(b) * (P.gamma + 1) + j) * P.vocab
-                                  : P.Dl + (long(b) * P.gamma + (j - P.gamma - 1)) * P.vocab;
-  const bool bonus = j == P.gamma;
-  const bool aligned = (P.vocab & 3) == 0;
-  float m = kNegInf, s = 0.0f, bk = kNegInf;
-  int bi = 0x7FFFFFFF;
-  const int nq = (P.vocab + 3) >> 2;
-  for (int qd = threadIdx.x; qd < nq; qd += kThreads) {
-    float v[4];
-    const int x0 = qd * 4;
-    if (aligned) {
-      const float4 f = reinterpret_cast<const float4*>(row)[qd];
-      v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
-    } else {
+// Loads NQ quads per thread of one row, quad q at logits 4q..4q+3, thread t
+// taking quads q0 + u * kThreads + t.  Past the row's end: -inf.
+template <bool kAligned, int NQ>
+__device__ inline void load_chunk(const float* row, int vocab, int q0, float (&v)[NQ][4]) {
+  if (kAligned) {
+    const int nq = vocab >> 2;
+    float4 f[NQ];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = x0 + e < P.vocab ? row[x0 + e] : kNegInf;
+    for (int u = 0; u < NQ; ++u) {
+      const int q = q0 + u * kThreads + int(threadIdx.x);
+      f[u] = q < nq ? reinterpret_cast<const float4*>(row)[q]
+                    : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
     }
-    const float mv = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-    if (mv > m) {
-      s *= expf(m - mv);
-      m = mv;
-    }
-    if (m > kNegInf) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s += expf(v[e] - m);
+    for (int u = 0; u < NQ; ++u) {
+      v[u][0] = f[u].x;
+      v[u][1] = f[u].y;
+      v[u][2] = f[u].z;
+      v[u][3] = f[u].w;
     }
-    if (bonus) {
-      const Philox4 r = philox4x32_10(unsigned(qd), unsigned(b), P.step,
-                                      unsigned(P.gamma) | (kPurposeSample << 16), P.k0, P.k1);
+  } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (x0 + e < P.vocab) better(bk, bi, v[e] + gumbel(uniform01(r.x[e])), x0 + e);
+    for (int u = 0; u < NQ; ++u) {
+      const int x0 = (q0 + u * kThreads + int(threadIdx.x)) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[u][e] = x0 + e < vocab ? row[x0 + e] : kNegInf;
     }
   }
-  // combine (m, s) across the block
+}
+
+__device__ inline const float* row_ptr(const AcceptParams& P, int b, int j) {
+  return j <= P.gamma ? P.T + (long(b) * (P.gamma + 1) + j) * P.vocab
+                      : P.Dl + (long(b) * P.gamma + (j - P.gamma - 1)) * P.vocab;
+}
+
+template <bool kAligned>
+__global__ __launch_bounds__(kThreads) void accept_stats_kernel(AcceptParams P) {
+  const int chunk = blockIdx.x % P.schunks;
+  const int r = blockIdx.x / P.schunks;  // b * (2 gamma + 1) + j
+  const int rows_per_seq = 2 * P.gamma + 1;
+  const float* row = row_ptr(P, r / rows_per_seq, r % rows_per_seq);
+  float v[kStatsQuads][4];
+  load_chunk<kAligned, kStatsQuads>(row, P.vocab, chunk * (kStatsChunk / 4), v);
+  float m = kNegInf;
+#pragma unroll
+  for (int u = 0; u < kStatsQuads; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = fmaxf(m, v[u][e]);
+  m *= kLog2e;
+  float s = 0.0f;
+  if (m > kNegInf) {
+#pragma unroll
+    for (int u = 0; u < kStatsQuads; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s += exp2_hw(__builtin_fmaf(v[u][e], kLog2e, -m));
+  }
   for (int o = 32; o > 0; o >>= 1) combine_ms(m, s, __shfl_xor(m, o, 64), __shfl_xor(s, o, 64));
-  __shared__ float sm[kThreads / 64], ss[kThreads / 64];
-  __shared__ float sk[kThreads / 64];
-  __shared__ int si[kThreads / 64];
+  __shared__ float sm[kWaves], ss[kWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) {
     sm[wave] = m;
@@ -156,112 +185,187 @@ __global__ __launch_bounds__(kThreads) void accept_rowstats_kernel(AcceptParams 
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    float M = sm[0], S = ss[0];
-    for (int w = 1; w < kThreads / 64; ++w) combine_ms(M, S, sm[w], ss[w]);
-    P.lse[long(b) * rows_per_seq + j] = M + logf(S);
+    for (int w = 1; w < kWaves; ++w) combine_ms(m, s, sm[w], ss[w]);
+    P.stats[long(r) * P.schunks + chunk] = make_float2(m, s);
   }
-  if (bonus) {
-    block_argmax(bk, bi, sk, si);
-    if (threadIdx.x == 0) {
-      P.bonus_key[b] = bk;
-      P.bonus_tok[b] = bi;
+}
+
+// Gumbel-max candidate of this thread over its quads of row k: the fallback
+// (bonus) key log2 P_k(x) + g(x) and, with kResidual, the residual key
+// log2 max(0, P_k - Q_k)(x) + g(x).  Branch-free per logit.
+template <bool kResidual>
+__device__ inline void draw_quads(const float (&tv)[kDrawQuads][4], const float (&dv)[kDrawQuads][4],
+                                  int q0, int b, unsigned c3, float lt, float ld, const AcceptParams& P,
+                                  float& rk, int& ri, float& fk, int& fi) {
+#pragma unroll
+  for (int u = 0; u < kDrawQuads; ++u) {
+    const int q = q0 + u * kThreads + int(threadIdx.x);
+    const Philox4 r = philox4x32_10(unsigned(q), unsigned(b), P.step, c3, P.k0, P.k1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int x = q * 4 + e;
+      const float g = gumbel2(uniform01(r.x[e]));
+      const float a = __builtin_fmaf(tv[u][e], kLog2e, -lt);  // log2 P_k(x); -inf past the row
+      better(fk, fi, a + g, x);
+      if (kResidual) {
+        const float c = __builtin_fmaf(dv[u][e], kLog2e, -ld);  // log2 Q_k(x)
+        // log2 max(0, P - Q) = a + log2(1 - 2^(c - a)) where P > Q
+        const float key = a > c ? a + log2_one_minus_exp2(c - a) + g : kNegInf;
+        better(rk, ri, key, x);
+      }
     }
   }
 }
 
-__global__ __launch_bounds__(kThreads) void accept_decide_kernel(AcceptParams P) {
-  const int b = blockIdx.x;
+template <bool kAligned>
+__global__ __launch_bounds__(kThreads) void accept_draw_kernel(AcceptParams P) {
+  const int chunk = blockIdx.x % P.dchunks;
+  const int b = blockIdx.x / P.dchunks;
   const int rows_per_seq = 2 * P.gamma + 1;
-  const float* lse = P.lse + long(b) * rows_per_seq;
+  __shared__ float s_lse[2 * 64 + 1];  // base-2 log normaliser per row
   __shared__ int s_k;
-  __shared__ float sk[kThreads / 64];
-  __shared__ int si[kThreads / 64];
-  if (threadIdx.x == 0) {
-    int k = P.gamma;
-    for (int i = 0; i < P.gamma; ++i) {
-      const int x = P.tokens[long(b) * P.gamma + i];
-      if (x < 0 || x >= P.vocab) {       // invalid draft token: reject
-        k = i;
-        break;
+  __shared__ float sk[2][kWaves];
+  __shared__ int si[2][kWaves];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // wave 0, lane i < gamma: the logits of draft token x_i (independent of the
+  // normalisers, so issued first)
+  int x = -1;
+  float tx = 0.0f, dx = 0.0f;
+  if (t < P.gamma) {
+    x = P.tokens[long(b) * P.gamma + t];
+    if (x >= 0 && x < P.vocab) {
+      tx = P.T[(long(b) * (P.gamma + 1) + t) * P.vocab + x];
+      dx = P.Dl[(long(b) * P.gamma + t) * P.vocab + x];
+    }
+  }
+  // log normalisers of the sequence's rows from the chunk partials: wave w
+  // takes rows w, w + 4, ... four at a time, lane c chunks c, c + 64, ...
+  const float2* st = P.stats + long(b) * rows_per_seq * P.schunks;
+  for (int r0 = wave; r0 < rows_per_seq; r0 += 4 * kWaves) {
+    float m[4], sm[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m[j] = kNegInf;
+      sm[j] = 0.0f;
+    }
+    for (int c = lane; c < P.schunks; c += 64) {
+      float2 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = r0 + j * kWaves;
+        v[j] = r < rows_per_seq ? st[long(r) * P.schunks + c] : make_float2(kNegInf, 0.0f);
       }
-      const float lt = P.T[(long(b) * (P.gamma + 1) + i) * P.vocab + x] - lse[i];
-      const float ld = P.Dl[(long(b) * P.gamma + i) * P.vocab + x] - lse[P.gamma + 1 + i];
-      const float lr = lt - ld;
-      const float a = lr >= 0.0f ? 1.0f : expf(lr);
-      const Philox4 r = philox4x32_10(0u, unsigned(b), P.step, unsigned(i) | (kPurposeAccept << 16),
-                                      P.k0, P.k1);
-      if (!(uniform01(r.x[0]) < a)) {
-        k = i;
-        break;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) combine_ms(m[j], sm[j], v[j].x, v[j].y);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      for (int o = 32; o > 0; o >>= 1)
+        combine_ms(m[j], sm[j], __shfl_xor(m[j], o, 64), __shfl_xor(sm[j], o, 64));
+      const int r = r0 + j * kWaves;
+      if (lane == 0 && r < rows_per_seq) s_lse[r] = m[j] + log2_hw(sm[j]);
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // lane i tests draft i: accept iff u_i < min(1, P_i(x_i) / Q_i(x_i)); an
+    // out-of-range token is rejected
+    bool reject = false;
+    if (t < P.gamma) {
+      if (x < 0 || x >= P.vocab) {
+        reject = true;
+      } else {
+        const float lp = tx * kLog2e - s_lse[t];
+        const float lq = dx * kLog2e - s_lse[P.gamma + 1 + t];
+        const float d = lp - lq;
+        const float acc = d >= 0.0f ? 1.0f : exp2_hw(d);
+        const Philox4 r = philox4x32_10(0u, unsigned(b), P.step, unsigned(t) | (kPurposeAccept << 16),
+                                        P.k0, P.k1);
+        reject = !(uniform01(r.x[0]) < acc);
       }
     }
-    s_k = k;
+    const unsigned long long rej = __ballot(reject);
+    if (t == 0) s_k = rej ? __builtin_ctzll(rej) : P.gamma;
   }
   __syncthreads();
   const int k = s_k;
-  if (k == P.gamma) {
-    if (threadIdx.x == 0) {
-      P.accepted_len[b] = k;
-      P.next_token[b] = P.bonus_tok[b];
-    }
-    return;
-  }
-  // residual max(0, P_k - Q_k): argmax of log(residual) + Gumbel; fall back to
-  // log P_k + Gumbel when the residual is zero everywhere
-  const float* trow = P.T + (long(b) * (P.gamma + 1) + k) * P.vocab;
-  const float* drow = P.Dl + (long(b) * P.gamma + k) * P.vocab;
-  const float lt = lse[k], ld = lse[P.gamma + 1 + k];
+  if (chunk == 0 && t == 0) P.accepted_len[b] = k;
+  const bool residual = k < P.gamma;
+  const float lt = s_lse[k], ld = residual ? s_lse[P.gamma + 1 + k] : 0.0f;
+  const int q0 = chunk * (kDrawChunk / 4);
+  float tv[kDrawQuads][4], dv[kDrawQuads][4];
   float rk = kNegInf, fk = kNegInf;
   int ri = 0x7FFFFFFF, fi = 0x7FFFFFFF;
-  const bool aligned = (P.vocab & 3) == 0;
-  const int nq = (P.vocab + 3) >> 2;
-  for (int qd = threadIdx.x; qd < nq; qd += kThreads) {
-    float tv[4], dv[4];
-    const int x0 = qd * 4;
-    if (aligned) {
-      const float4 a = reinterpret_cast<const float4*>(trow)[qd];
-      const float4 c = reinterpret_cast<const float4*>(drow)[qd];
-      tv[0] = a.x; tv[1] = a.y; tv[2] = a.z; tv[3] = a.w;
-      dv[0] = c.x; dv[1] = c.y; dv[2] = c.z; dv[3] = c.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        tv[e] = x0 + e < P.vocab ? trow[x0 + e] : kNegInf;
-        dv[e] = x0 + e < P.vocab ? drow[x0 + e] : kNegInf;
-      }
-    }
-    const Philox4 r = philox4x32_10(unsigned(qd), unsigned(b), P.step,
-                                    unsigned(k) | (kPurposeSample << 16), P.k0, P.k1);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (x0 + e >= P.vocab) continue;
-      const float g = gumbel(uniform01(r.x[e]));
-      const float res = expf(tv[e] - lt) - expf(dv[e] - ld);
-      if (res > 0.0f) better(rk, ri, logf(res) + g, x0 + e);
-      better(fk, fi, tv[e] + g, x0 + e);
-    }
+  const unsigned c3 = unsigned(k) | (kPurposeSample << 16);
+  load_chunk<kAligned, kDrawQuads>(row_ptr(P, b, k), P.vocab, q0, tv);
+  if (residual) {
+    load_chunk<kAligned, kDrawQuads>(row_ptr(P, b, P.gamma + 1 + k), P.vocab, q0, dv);
+    draw_quads<true>(tv, dv, q0, b, c3, lt, ld, P, rk, ri, fk, fi);
+  } else {
+    draw_quads<false>(tv, dv, q0, b, c3, lt, ld, P, rk, ri, fk, fi);
   }
-  block_argmax(rk, ri, sk, si);
+  for (int o = 32; o > 0; o >>= 1) {
+    better(rk, ri, __shfl_xor(rk, o, 64), __shfl_xor(ri, o, 64));
+    better(fk, fi, __shfl_xor(fk, o, 64), __shfl_xor(fi, o, 64));
+  }
+  if (lane == 0) {
+    sk[0][wave] = rk;
+    si[0][wave] = ri;
+    sk[1][wave] = fk;
+    si[1][wave] = fi;
+  }
   __syncthreads();
-  block_argmax(fk, fi, sk, si);
-  if (threadIdx.x == 0) {
-    P.accepted_len[b] = k;
-    P.next_token[b] = rk > kNegInf ? ri : fi;
+  if (t == 0) {
+    for (int w = 1; w < kWaves; ++w) {
+      better(rk, ri, sk[0][w], si[0][w]);
+      better(fk, fi, sk[1][w], si[1][w]);
+    }
+    P.cand[long(b) * P.dchunks + chunk] = make_int4(__float_as_int(rk), ri, __float_as_int(fk), fi);
   }
 }
 
-size_t ws_layout(const pkv_accept_args* a, size_t* off_key, size_t* off_tok) {
-  const size_t lse = size_t(a->batch) * (2 * a->gamma + 1) * sizeof(float);
-  *off_key = (lse + 255) & ~size_t(255);
-  *off_tok = *off_key + ((size_t(a->batch) * sizeof(float) + 255) & ~size_t(255));
-  return *off_tok + size_t(a->batch) * sizeof(int);
+// One wave per sequence: the best candidate over the chunks.
+__global__ __launch_bounds__(64) void accept_finish_kernel(AcceptParams P) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  float rk = kNegInf, fk = kNegInf;
+  int ri = 0x7FFFFFFF, fi = 0x7FFFFFFF;
+  for (int c = lane; c < P.dchunks; c += 64) {
+    const int4 v = P.cand[long(b) * P.dchunks + c];
+    better(rk, ri, __int_as_float(v.x), v.y);
+    better(fk, fi, __int_as_float(v.z), v.w);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    better(rk, ri, __shfl_xor(rk, o, 64), __shfl_xor(ri, o, 64));
+    better(fk, fi, __shfl_xor(fk, o, 64), __shfl_xor(fi, o, 64));
+  }
+  // residual zero everywhere (or k = gamma): the draw from P_k
+  if (lane == 0) P.next_token[b] = rk > kNegInf ? ri : fi;
+}
+
+struct WsLayout {
+  size_t stats, cand, total;
+};
+
+WsLayout ws_layout(const pkv_accept_args* a) {
+  const size_t sch = (size_t(a->vocab) + kStatsChunk - 1) / kStatsChunk;
+  const size_t dch = (size_t(a->vocab) + kDrawChunk - 1) / kDrawChunk;
+  WsLayout w;
+  w.stats = 0;
+  const size_t stats_bytes = size_t(a->batch) * (2 * a->gamma + 1) * sch * sizeof(float2);
+  w.cand = (stats_bytes + 255) & ~size_t(255);
+  w.total = w.cand + size_t(a->batch) * dch * sizeof(int4);
+  return w;
 }
 
 pkv_status check_shape(const pkv_accept_args* a) {
   if (!a) return fail(PKV_ERR_INVALID_ARG, "null args");
-  if (a->batch < 1) return fail(PKV_ERR_INVALID_ARG, "batch must be >= 1");
+  if (a->batch < 1 || a->batch > kMaxBatch) return fail(PKV_ERR_INVALID_ARG, "batch must be in [1, 2^20]");
   if (a->gamma < 1 || a->gamma > 64) return fail(PKV_ERR_INVALID_ARG, "gamma must be in [1, 64]");
-  if (a->vocab < 1) return fail(PKV_ERR_INVALID_ARG, "vocab must be >= 1");
+  if (a->vocab < 1 || a->vocab > kMaxVocab) return fail(PKV_ERR_INVALID_ARG, "vocab must be in [1, 2^26]");
+  const long long sch = (a->vocab + kStatsChunk - 1) / kStatsChunk;
+  const long long dch = (a->vocab + kDrawChunk - 1) / kDrawChunk;
+  if (sch * a->batch * (2 * a->gamma + 1) > 0x7FFFFFFFll || dch * a->batch > 0x7FFFFFFFll)
+    return fail(PKV_ERR_INVALID_ARG, "batch * (2 gamma + 1) * vocab too large for one launch");
   return PKV_OK;
 }
 
@@ -285,18 +389,18 @@ extern "C" pkv_status spec_accept_workspace_size(const pkv_accept_args* a, size_
   if (!bytes_out) return fail(PKV_ERR_INVALID_ARG, "null output");
   pkv_status st = check_shape(a);
   if (st != PKV_OK) return st;
-  size_t ok, ot;
-  *bytes_out = ws_layout(a, &ok, &ot);
+  *bytes_out = ws_layout(a).total;
   return PKV_OK;
 }
 
 extern "C" pkv_status spec_accept(const pkv_accept_args* a, void* stream) {
   pkv_status st = check(a);
   if (st != PKV_OK) return st;
-  size_t off_key, off_tok;
-  const size_t need = ws_layout(a, &off_key, &off_tok);
-  if (!a->workspace || a->workspace_bytes < need)
+  const WsLayout w = ws_layout(a);
+  if (!a->workspace || a->workspace_bytes < w.total)
     return fail(PKV_ERR_WORKSPACE, "workspace smaller than spec_accept_workspace_size");
+  if (reinterpret_cast<uintptr_t>(a->workspace) & 15)
+    return fail(PKV_ERR_WORKSPACE, "workspace must be 16-byte aligned");
   AcceptParams p{};
   p.T = a->target_logits;
   p.Dl = a->draft_logits;
@@ -304,20 +408,30 @@ extern "C" pkv_status spec_accept(const pkv_accept_args* a, void* stream) {
   p.accepted_len = a->accepted_len;
   p.next_token = a->next_token;
   char* ws = static_cast<char*>(a->workspace);
-  p.lse = reinterpret_cast<float*>(ws);
-  p.bonus_key = reinterpret_cast<float*>(ws + off_key);
-  p.bonus_tok = reinterpret_cast<int*>(ws + off_tok);
+  p.stats = reinterpret_cast<float2*>(ws + w.stats);
+  p.cand = reinterpret_cast<int4*>(ws + w.cand);
   p.batch = a->batch;
   p.gamma = a->gamma;
   p.vocab = a->vocab;
+  p.schunks = (a->vocab + kStatsChunk - 1) / kStatsChunk;
+  p.dchunks = (a->vocab + kDrawChunk - 1) / kDrawChunk;
   p.k0 = unsigned(a->seed & 0xFFFFFFFFu);
   p.k1 = unsigned(a->seed >> 32);
   p.step = a->step;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(accept_rowstats_kernel, dim3(a->batch * (2 * a->gamma + 1)), dim3(kThreads), 0, s, p);
+  const bool aligned = (a->vocab & 3) == 0;
+  const unsigned n_stats = unsigned(a->batch) * (2 * a->gamma + 1) * p.schunks;
+  const unsigned n_draw = unsigned(a->batch) * p.dchunks;
+  if (aligned) hipLaunchKernelGGL(accept_stats_kernel<true>, dim3(n_stats), dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL(accept_stats_kernel<false>, dim3(n_stats), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) {
-    hipLaunchKernelGGL(accept_decide_kernel, dim3(a->batch), dim3(kThreads), 0, s, p);
+    if (aligned) hipLaunchKernelGGL(accept_draw_kernel<true>, dim3(n_draw), dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL(accept_draw_kernel<false>, dim3(n_draw), dim3(kThreads), 0, s, p);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(accept_finish_kernel, dim3(a->batch), dim3(64), 0, s, p);
     e = hipGetLastError();
   }
   if (e != hipSuccess) return fail(PKV_ERR_DEVICE, std::string("accept launch: ") + hipGetErrorString(e));

@@ -1,6 +1,8 @@
 // Pool-update kernel: applies PoolTask records (copy-on-write page copies,
 // token scatter into the tiled page layout with optional FP8 quantisation,
-// block-table entries and sequence lengths) in stream order.
+// block-table entries and sequence lengths) in stream order.  A workgroup
+// takes one task and four KV heads; each wave moves one head's tokens in
+// groups of 8 channels, all loads of a lane issued before its stores.
 //
 // FP8 quantisation (reading of atozofsoftwareengineering.blog, section
 // "Custom FP8 Quantized Memory Block Layout", per-block scales S_K, S_V):
@@ -18,29 +20,14 @@ namespace pkv {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+// 8-channel groups of one head in one task: at most 16 tokens x 128/8 groups,
+// i.e. four per lane of the head's wave.
+constexpr int kItemsPerLane = 4;
 
 __device__ inline float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
-}
-
-__device__ inline float block_max(float v, float* red) {
-  v = wave_max(v);
-  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, red[w]);
-  return r;
-}
-
-__device__ inline float load_src(const void* src, int dtype, long idx) {
-  if (dtype == PKV_BF16) {
-    unsigned short b = static_cast<const unsigned short*>(src)[idx];
-    return __uint_as_float(unsigned(b) << 16);
-  }
-  return static_cast<const float*>(src)[idx];
 }
 
 __device__ inline unsigned char quant_e4m3(float x, float inv) {
@@ -51,88 +38,176 @@ __device__ inline unsigned char quant_e4m3(float x, float inv) {
   return static_cast<unsigned char>(packed & 0xFF);
 }
 
+// Item it of a task (token it / G, channel group it % G) for the calling lane.
+struct Item {
+  bool ok;
+  int slot, c0;
+  long src;  // element offset of channel c0 of head h in the source row
+};
+
+__device__ inline Item item(const PoolTask& t, int u, int h, int H, int D) {
+  const int G = D / 8;
+  const int it = u * 64 + int(threadIdx.x & 63);
+  Item r;
+  r.ok = it < t.n * G;
+  const int tok = it / G;
+  r.c0 = (it % G) * 8;
+  r.slot = t.slot_begin + tok;
+  r.src = (long(t.src_row) + tok) * H * D + long(h) * D + r.c0;
+  return r;
+}
+
+// bf16 pool, bf16 source: 16-byte loads; K groups of 8 channels are
+// contiguous in the tiled layout (D/4 is a multiple of 8), V is scattered.
+__device__ void write_bf16(const PoolDevice& dev, const PoolTask& t, int h, int H, int D, long pb) {
+  const uint4* ks = static_cast<const uint4*>(dev.k_src);
+  const uint4* vs = static_cast<const uint4*>(dev.v_src);
+  uint4 kx[kItemsPerLane], vx[kItemsPerLane];
+  Item im[kItemsPerLane];
+#pragma unroll
+  for (int u = 0; u < kItemsPerLane; ++u) {
+    im[u] = item(t, u, h, H, D);
+    if (im[u].ok) {
+      kx[u] = ks[im[u].src / 8];
+      vx[u] = vs[im[u].src / 8];
+    }
+  }
+  char* kslab = static_cast<char*>(dev.k_pages) + (long(t.page) * H + h) * pb;
+  unsigned short* vslab = reinterpret_cast<unsigned short*>(static_cast<char*>(dev.v_pages) + (long(t.page) * H + h) * pb);
+#pragma unroll
+  for (int u = 0; u < kItemsPerLane; ++u) {
+    if (!im[u].ok) continue;
+    *reinterpret_cast<uint4*>(kslab + 2 * k_index_bf16(im[u].slot, im[u].c0, D)) = kx[u];
+    const unsigned w[4] = {vx[u].x, vx[u].y, vx[u].z, vx[u].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      vslab[v_index_bf16(im[u].slot, im[u].c0 + i)] = static_cast<unsigned short>(w[i / 2] >> (16 * (i % 2)));
+  }
+}
+
+// fp32 pool, fp32 source: row-major slab, two 16-byte moves per group.
+__device__ void write_f32(const PoolDevice& dev, const PoolTask& t, int h, int H, int D, long pb) {
+  const float4* ks = static_cast<const float4*>(dev.k_src);
+  const float4* vs = static_cast<const float4*>(dev.v_src);
+  float4 kx[kItemsPerLane][2], vx[kItemsPerLane][2];
+  Item im[kItemsPerLane];
+#pragma unroll
+  for (int u = 0; u < kItemsPerLane; ++u) {
+    im[u] = item(t, u, h, H, D);
+    if (im[u].ok) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        kx[u][p] = ks[im[u].src / 4 + p];
+        vx[u][p] = vs[im[u].src / 4 + p];
+      }
+    }
+  }
+  float4* kslab = reinterpret_cast<float4*>(static_cast<char*>(dev.k_pages) + (long(t.page) * H + h) * pb);
+  float4* vslab = reinterpret_cast<float4*>(static_cast<char*>(dev.v_pages) + (long(t.page) * H + h) * pb);
+#pragma unroll
+  for (int u = 0; u < kItemsPerLane; ++u) {
+    if (!im[u].ok) continue;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      kslab[index_f32(im[u].slot, im[u].c0, D) / 4 + p] = kx[u][p];
+      vslab[index_f32(im[u].slot, im[u].c0, D) / 4 + p] = vx[u][p];
+    }
+  }
+}
+
+// FP8 pool, fp32 source: the head's values stay in registers while the wave
+// reduces amax for a fresh page; K groups of 8 channels are 8 contiguous
+// bytes of the tiled layout (D/4 is a multiple of 16), V is scattered.
+__device__ void write_fp8(const PoolDevice& dev, const PoolTask& t, int h, int H, int D, long pb) {
+  const float4* ks = static_cast<const float4*>(dev.k_src);
+  const float4* vs = static_cast<const float4*>(dev.v_src);
+  float kx[kItemsPerLane][8], vx[kItemsPerLane][8];
+  Item im[kItemsPerLane];
+  float ak = 0.0f, av = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kItemsPerLane; ++u) {
+    im[u] = item(t, u, h, H, D);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const float4 a = im[u].ok ? ks[im[u].src / 4 + p] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 b = im[u].ok ? vs[im[u].src / 4 + p] : make_float4(0.f, 0.f, 0.f, 0.f);
+      kx[u][4 * p + 0] = a.x; kx[u][4 * p + 1] = a.y; kx[u][4 * p + 2] = a.z; kx[u][4 * p + 3] = a.w;
+      vx[u][4 * p + 0] = b.x; vx[u][4 * p + 1] = b.y; vx[u][4 * p + 2] = b.z; vx[u][4 * p + 3] = b.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ak = fmaxf(ak, fabsf(kx[u][i]));
+      av = fmaxf(av, fabsf(vx[u][i]));
+    }
+  }
+  const long sidx = long(t.page) * H + h;
+  float sk, sv;
+  if (t.flags & kFresh) {
+    ak = wave_max(ak);
+    av = wave_max(av);
+    sk = ak == 0.0f ? 1.0f : ak / 448.0f;
+    sv = av == 0.0f ? 1.0f : av / 448.0f;
+    if ((threadIdx.x & 63) == 0) {
+      dev.k_scale[sidx] = sk;
+      dev.v_scale[sidx] = sv;
+    }
+  } else {
+    sk = dev.k_scale[sidx];
+    sv = dev.v_scale[sidx];
+  }
+  const float ik = 1.0f / sk, iv = 1.0f / sv;
+  unsigned char* kslab = static_cast<unsigned char*>(dev.k_pages) + sidx * pb;
+  unsigned char* vslab = static_cast<unsigned char*>(dev.v_pages) + sidx * pb;
+#pragma unroll
+  for (int u = 0; u < kItemsPerLane; ++u) {
+    if (!im[u].ok) continue;
+    unsigned lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= unsigned(quant_e4m3(kx[u][i], ik)) << (8 * i);
+      hi |= unsigned(quant_e4m3(kx[u][4 + i], ik)) << (8 * i);
+    }
+    *reinterpret_cast<uint2*>(kslab + k_index_fp8(im[u].slot, im[u].c0, D)) = make_uint2(lo, hi);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vslab[v_index_fp8(im[u].slot, im[u].c0 + i)] = quant_e4m3(vx[u][i], iv);
+  }
+}
+
+// Block (task, y) handles KV heads 4y .. 4y+3 of its task, one wave per head.
 __global__ __launch_bounds__(kThreads) void pool_update_kernel(PoolDevice dev, PoolUpdateBatch batch) {
   const PoolTask t = batch.tasks[blockIdx.x];
   const int H = batch.num_kv_heads, D = batch.head_dim;
   const long pb = batch.page_bytes;
-  const bool fp8 = batch.kv_dtype == PKV_FP8_E4M3;
-  __shared__ float red[kThreads / 64];
-  __shared__ float s_scale[2];
+  const int h0 = blockIdx.y * kWaves;
+  const int nh = min(kWaves, H - h0);
 
   if (t.cow_src >= 0) {
-    const long n16 = H * pb / 16;
-    const uint4* sk = reinterpret_cast<const uint4*>(static_cast<const char*>(dev.k_pages) + t.cow_src * H * pb);
-    const uint4* sv = reinterpret_cast<const uint4*>(static_cast<const char*>(dev.v_pages) + t.cow_src * H * pb);
-    uint4* dk = reinterpret_cast<uint4*>(static_cast<char*>(dev.k_pages) + long(t.page) * H * pb);
-    uint4* dv = reinterpret_cast<uint4*>(static_cast<char*>(dev.v_pages) + long(t.page) * H * pb);
+    const long n16 = nh * pb / 16;
+    const long so = (long(t.cow_src) * H + h0) * pb, dO = (long(t.page) * H + h0) * pb;
+    const uint4* sk = reinterpret_cast<const uint4*>(static_cast<const char*>(dev.k_pages) + so);
+    const uint4* sv = reinterpret_cast<const uint4*>(static_cast<const char*>(dev.v_pages) + so);
+    uint4* dk = reinterpret_cast<uint4*>(static_cast<char*>(dev.k_pages) + dO);
+    uint4* dv = reinterpret_cast<uint4*>(static_cast<char*>(dev.v_pages) + dO);
     for (long i = threadIdx.x; i < n16; i += kThreads) {
       dk[i] = sk[i];
       dv[i] = sv[i];
     }
-    if (fp8) {
-      for (int h = threadIdx.x; h < H; h += kThreads) {
-        dev.k_scale[long(t.page) * H + h] = dev.k_scale[long(t.cow_src) * H + h];
-        dev.v_scale[long(t.page) * H + h] = dev.v_scale[long(t.cow_src) * H + h];
-      }
+    if (batch.kv_dtype == PKV_FP8_E4M3 && int(threadIdx.x) < nh) {
+      const int h = h0 + threadIdx.x;
+      dev.k_scale[long(t.page) * H + h] = dev.k_scale[long(t.cow_src) * H + h];
+      dev.v_scale[long(t.page) * H + h] = dev.v_scale[long(t.cow_src) * H + h];
     }
-  }
-  __syncthreads();
-
-  if (t.n > 0) {
-    const int per_tok = H * D;
-    for (int h = 0; h < H; ++h) {
-      float inv_k = 1.0f, inv_v = 1.0f;
-      if (fp8) {
-        if (t.flags & kFresh) {
-          float ak = 0.0f, av = 0.0f;
-          for (int e = threadIdx.x; e < t.n * D; e += kThreads) {
-            long idx = long(t.src_row + e / D) * per_tok + h * D + (e % D);
-            ak = fmaxf(ak, fabsf(load_src(dev.k_src, batch.src_dtype, idx)));
-            av = fmaxf(av, fabsf(load_src(dev.v_src, batch.src_dtype, idx)));
-          }
-          ak = block_max(ak, red);
-          av = block_max(av, red);
-          if (threadIdx.x == 0) {
-            float sk = ak == 0.0f ? 1.0f : ak / 448.0f;
-            float sv = av == 0.0f ? 1.0f : av / 448.0f;
-            dev.k_scale[long(t.page) * H + h] = sk;
-            dev.v_scale[long(t.page) * H + h] = sv;
-            s_scale[0] = sk;
-            s_scale[1] = sv;
-          }
-        } else if (threadIdx.x == 0) {
-          s_scale[0] = dev.k_scale[long(t.page) * H + h];
-          s_scale[1] = dev.v_scale[long(t.page) * H + h];
-        }
-        __syncthreads();
-        inv_k = 1.0f / s_scale[0];
-        inv_v = 1.0f / s_scale[1];
-      }
-      char* kslab = static_cast<char*>(dev.k_pages) + (long(t.page) * H + h) * pb;
-      char* vslab = static_cast<char*>(dev.v_pages) + (long(t.page) * H + h) * pb;
-      for (int e = threadIdx.x; e < t.n * D; e += kThreads) {
-        const int tok = e / D, c = e % D, slot = t.slot_begin + tok;
-        const long idx = long(t.src_row + tok) * per_tok + h * D + c;
-        if (batch.kv_dtype == PKV_F32) {
-          reinterpret_cast<float*>(kslab)[index_f32(slot, c, D)] = load_src(dev.k_src, PKV_F32, idx);
-          reinterpret_cast<float*>(vslab)[index_f32(slot, c, D)] = load_src(dev.v_src, PKV_F32, idx);
-        } else if (batch.kv_dtype == PKV_BF16) {
-          reinterpret_cast<unsigned short*>(kslab)[k_index_bf16(slot, c, D)] =
-              static_cast<const unsigned short*>(dev.k_src)[idx];
-          reinterpret_cast<unsigned short*>(vslab)[v_index_bf16(slot, c)] =
-              static_cast<const unsigned short*>(dev.v_src)[idx];
-        } else {
-          reinterpret_cast<unsigned char*>(kslab)[k_index_fp8(slot, c, D)] =
-              quant_e4m3(load_src(dev.k_src, batch.src_dtype, idx), inv_k);
-          reinterpret_cast<unsigned char*>(vslab)[v_index_fp8(slot, c)] =
-              quant_e4m3(load_src(dev.v_src, batch.src_dtype, idx), inv_v);
-        }
-      }
-      __syncthreads();
-    }
+    __syncthreads();
   }
 
-  if (threadIdx.x == 0) {
+  const int h = h0 + int(threadIdx.x >> 6);
+  if (t.n > 0 && h < H) {
+    if (batch.kv_dtype == PKV_BF16) write_bf16(dev, t, h, H, D, pb);
+    else if (batch.kv_dtype == PKV_F32) write_f32(dev, t, h, H, D, pb);
+    else write_fp8(dev, t, h, H, D, pb);
+  }
+
+  if (blockIdx.y == 0 && threadIdx.x == 0) {
     if (t.flags & kWriteTable) dev.block_table[long(t.row) * batch.bt_stride + t.logical] = t.page;
     if (t.flags & kSetLen) dev.seq_lens[t.row] = t.new_len;
   }
@@ -142,7 +217,8 @@ __global__ __launch_bounds__(kThreads) void pool_update_kernel(PoolDevice dev, P
 
 pkv_status launch_pool_update(const PoolDevice& dev, const PoolUpdateBatch& batch, void* stream) {
   if (batch.n_tasks <= 0) return PKV_OK;
-  hipLaunchKernelGGL(pool_update_kernel, dim3(batch.n_tasks), dim3(kThreads), 0,
+  const unsigned gy = unsigned((batch.num_kv_heads + kWaves - 1) / kWaves);
+  hipLaunchKernelGGL(pool_update_kernel, dim3(batch.n_tasks, gy), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), dev, batch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_DEVICE, std::string("pool update launch: ") + hipGetErrorString(e));

@@ -264,6 +264,9 @@ pkv_status paged_kv_append(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
   }
   if (pool->device && total_tokens > 0 && (!k_src || !v_src))
     return fail(PKV_ERR_INVALID_ARG, "null source arrays");
+  if (pool->device && total_tokens > 0 &&
+      ((reinterpret_cast<uintptr_t>(k_src) | reinterpret_cast<uintptr_t>(v_src)) & 15))
+    return fail(PKV_ERR_INVALID_ARG, "source arrays must be 16-byte aligned");
   if (need > int64_t(pool->free_ranks.size()))
     return fail(PKV_ERR_OUT_OF_PAGES, "page pool exhausted");
 

@@ -138,3 +138,18 @@ def test_special_cases():
     bad[:, 1] = V + 3                                    # invalid draft token: rejected there
     k, _ = _gpu(T, T[:, :g].copy(), bad, 5, 0)
     assert np.all(k == 1)
+
+
+def test_prepared_accept_matches():
+    from paged_kv_speculative_amd import PreparedAccept
+    rng = np.random.default_rng(11)
+    B, gamma, V = 6, 4, 5000
+    T = (rng.standard_normal((B, gamma + 1, V)) * 2).astype(np.float32)
+    D = (rng.standard_normal((B, gamma, V)) * 2).astype(np.float32)
+    x = rng.integers(0, V, (B, gamma)).astype(np.int32)
+    Tt, Dt, xt = (torch.from_numpy(a).cuda() for a in (T, D, x))
+    call = PreparedAccept(Tt, Dt, xt, seed=99)
+    for step in (0, 5):
+        k1, t1 = (a.clone() for a in call(step))
+        k2, t2 = spec_accept(Tt, Dt, xt, 99, step)
+        assert torch.equal(k1, k2) and torch.equal(t1, t2)

@@ -233,3 +233,18 @@ def test_batch_slots():
                                  g.pool.seq_lens, n_q=w.n_q, num_kv_heads=w.num_kv_heads,
                                  kv_dtype="bf16", batch_slots=slots)
     assert torch.equal(O, O_all[[3, 1]]) and torch.equal(L, L_all[[3, 1]])
+
+
+def test_prepared_verify_matches():
+    """The prepared launch reads the same tensors in place: after an append
+    and a rollback it gives, bitwise, what a fresh call gives."""
+    w = wl.make(2, small=True, batch=4)
+    g = H.GpuSide(w)
+    call = g.pool.prepare_verify(g.q, w.n_q, sm_scale=w.sm_scale)
+    O1, L1 = (x.clone() for x in call())
+    O2, L2 = g.verify()
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+    g.pool.rollback(range(w.batch), [2] * w.batch)
+    O3, L3 = (x.clone() for x in call())
+    O4, L4 = g.verify()
+    assert torch.equal(O3, O4) and torch.equal(L3, L4) and not torch.equal(O1, O3)
