@@ -77,11 +77,10 @@ EXPORTS = {
     "pkv_pool_destroy": (None, [C.c_void_p]),
     "paged_kv_alloc": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int32,
                                  C.POINTER(C.c_int32), C.c_void_p]),
-    "paged_kv_append": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int64),
-                                  C.POINTER(C.c_int32), C.c_void_p, C.c_void_p, C.c_int,
-                                  C.c_void_p]),
-    "paged_kv_rollback": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int64),
-                                    C.POINTER(C.c_int32), C.c_void_p]),
+    # int64_t* seqs and int32_t* n_tokens are passed as addresses
+    "paged_kv_append": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                  C.c_void_p, C.c_int, C.c_void_p]),
+    "paged_kv_rollback": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
     "paged_kv_release": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p]),
     "paged_kv_block_table": (C.c_int, [C.c_void_p, C.c_int64, C.POINTER(C.c_int32), C.c_int32,
                                        C.POINTER(C.c_int32), C.POINTER(C.c_int32),

@@ -11,12 +11,18 @@ PAGE_SIZE = 16
 _TORCH_SRC = {torch.float32: F32, torch.bfloat16: BF16}
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream):
+    """hipStream_t of `stream` (None: torch's current stream) as an address."""
     if stream is None:
-        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+        if _raw_stream is not None:
+            return _raw_stream(torch.cuda.current_device())
+        return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, torch.cuda.Stream):
-        return C.c_void_p(stream.cuda_stream)
-    return C.c_void_p(int(stream))
+        return stream.cuda_stream
+    return int(stream)
 
 
 def _ptr(t):
@@ -24,12 +30,12 @@ def _ptr(t):
 
 
 def _ints(values, dtype):
-    """A C array view of a sequence of integers (list, range or ndarray)."""
-    a = np.ascontiguousarray(np.asarray(values, dtype=dtype))
-    if a.ndim != 1:
-        a = a.reshape(-1)
-    ctype = C.c_int64 if dtype == np.int64 else C.c_int32
-    return a, a.ctypes.data_as(C.POINTER(ctype))
+    """(array, address) of a sequence of integers (list, range or ndarray) as
+    a contiguous C array of `dtype`; the array keeps the memory alive."""
+    if not (type(values) is np.ndarray and values.dtype == dtype and values.ndim == 1
+            and values.flags.c_contiguous):
+        values = np.ascontiguousarray(np.asarray(values, dtype=dtype).reshape(-1))
+    return values, values.ctypes.data
 
 
 def page_bytes(kv_dtype, head_dim, page_size=PAGE_SIZE):

@@ -59,6 +59,11 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
+// s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8) that waits until at most n vector memory operations are
+// outstanding and leaves the other counters alone.
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int kVmcnt0 = vmcnt_imm(0);
 
 struct VerifyParams {
   const void* q;
@@ -152,6 +157,7 @@ struct Shape {
   static constexpr int DT = D / 16;                  // 16-channel tiles of the output
   static constexpr int KL = FP8 ? KS / 2 : KS;       // 16-byte K loads per page
   static constexpr int VL = FP8 ? D / 64 : D / 32;   // 16-byte V loads per page
+  static constexpr int LPP = KL + VL;                // vector loads per page
   // pages in flight per wave while one page is computed
   static constexpr int PF = FP8 ? (NT <= 2 ? 8 : (NT == 3 ? 5 : 3)) : (NT <= 2 ? 5 : (NT == 3 ? 3 : 2));
 };
@@ -549,6 +555,10 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
             }
           } else {
             load_q(qf, anc, M.b, M.g);           // its Q was overwritten in the ring window
+            // wait here, on this rare path, so that the common path's MFMAs
+            // never inherit a wait for these loads (which would also drain
+            // every prefetched page)
+            __builtin_amdgcn_s_waitcnt(kVmcnt0);
           }
           u_b = M.b;
           u_g = M.g;
