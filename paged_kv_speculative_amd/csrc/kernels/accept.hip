@@ -121,8 +121,9 @@ __device__ inline void combine_ms(float& m, float& s, float m2, float s2) {
 }
 
 // Loads NQ quads per thread of one row, quad q at logits 4q..4q+3, thread t
-// taking quads q0 + u * kThreads + t.  Past the row's end: -inf.
-template <bool kAligned, int NQ>
+// taking quads q0 + u * kThreads + t.  Past the row's end: -inf.  kStream:
+// non-temporal loads for data read once.
+template <bool kAligned, int NQ, bool kStream = false>
 __device__ inline void load_chunk(const float* row, int vocab, int q0, float (&v)[NQ][4]) {
   if (kAligned) {
     const int nq = vocab >> 2;
@@ -130,8 +131,11 @@ __device__ inline void load_chunk(const float* row, int vocab, int q0, float (&v
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
       const int q = q0 + u * kThreads + int(threadIdx.x);
-      f[u] = q < nq ? reinterpret_cast<const float4*>(row)[q]
-                    : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      const f32x4* src = reinterpret_cast<const f32x4*>(row) + q;
+      f32x4 x = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+      if (q < nq) x = kStream ? __builtin_nontemporal_load(src) : *src;
+      f[u] = make_float4(x[0], x[1], x[2], x[3]);
     }
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
@@ -162,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void accept_stats_kernel(AcceptParams P) 
   const int rows_per_seq = 2 * P.gamma + 1;
   const float* row = row_ptr(P, r / rows_per_seq, r % rows_per_seq);
   float v[kStatsQuads][4];
-  load_chunk<kAligned, kStatsQuads>(row, P.vocab, chunk * (kStatsChunk / 4), v);
+  load_chunk<kAligned, kStatsQuads, true>(row, P.vocab, chunk * (kStatsChunk / 4), v);
   float m = kNegInf;
 #pragma unroll
   for (int u = 0; u < kStatsQuads; ++u)
