@@ -43,6 +43,32 @@ def parse():
     return ap.parse_args()
 
 
+TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                               "verify_traffic_llama3-8b-layer.md")
+
+
+def measured_traffic(config):
+    """HBM-side bytes per verification call from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when the
+    summary is for another workload or the kernel source has changed since."""
+    import hashlib
+    if config != 2 or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_PROFILE):
+        k, sep, v = line.strip().partition(": ")
+        if sep:
+            fields[k] = v.strip()
+    try:
+        src = os.path.join(os.path.dirname(os.path.abspath(__file__)), fields["kernel_source"])
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if digest != fields["kernel_source_sha256"]:
+            return None
+        return float(fields["traffic_bytes_per_call"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
 def kv_bytes(lens, w):
     """Algorithmic KV bytes of one verification call: every K and V element of
     every token of every sequence once (the shared prefix counted once), plus
@@ -275,7 +301,9 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": measured_traffic(args.config),
+            "traffic_unit": "bytes per spec_verify_attention call (FETCH_SIZE + WRITE_SIZE)",
+            "algorithmic_bytes": float(np.mean(r["attn_bytes"])),
         },
     }
     if r["acc_ms"] is not None:
