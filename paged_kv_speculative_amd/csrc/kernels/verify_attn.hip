@@ -81,6 +81,8 @@ struct VerifyParams {
   int* cum;              // [batch + 1] page prefix sums (written by workgroup 0)
   long slab_bytes;       // bytes of one (page, KV head) slab
   int batch, n_q, Hq, Hkv, G, rows, bt_stride, n_wg;
+  int rg;                // row groups: waves that share a range, each taking rows_w rows
+  int rows_w;            // rows per wave (rows when rg = 1)
   int min_range;         // fewest page-heads per workgroup range
   float scale_log2;      // sm_scale * log2(e)
 };
@@ -182,7 +184,7 @@ struct Shape {
   static constexpr int DT = D / 16;                  // 16-channel tiles of the output
   static constexpr int KL = FP8 ? KS / 2 : KS;       // 16-byte K loads per page
   static constexpr int VL = FP8 ? D / 64 : D / 32;   // 16-byte V loads per page
-  static constexpr int LPP = KL + VL;                // vector loads per page
+  static constexpr int LPP = KL + VL + (FP8 ? 2 : 0); // vector loads per page (FP8: + scales)
   // Q of a unit staged in LDS: QS slots per wave of NT*16 rows x D bf16, plus
   // the unit's n_q ancestor masks
   static constexpr int QS = 2;
@@ -190,6 +192,7 @@ struct Shape {
   static constexpr int ASLOT = 64 * 8;
   // pages in flight per wave while one page is computed
   static constexpr int PF = FP8 ? (NT <= 2 ? 8 : (NT == 3 ? 5 : 3)) : (NT <= 2 ? 4 : (NT == 3 ? 3 : 2));
+  static constexpr int RS = PF + 1;                 // ring slots
 };
 
 template <int D, bool FP8>
@@ -199,10 +202,12 @@ struct PageRegs {
   u32x4 v[VL];
 };
 
-// Where a ring slot's page sits: sequence, KV head, page, and the
-// sequence's length (all wave-uniform).
+// Where a ring slot's page sits (all wave-uniform, kept to three scalars per
+// slot): unit = sequence << 16 | KV head, page, and the sequence's length n
+// (0 for a slot past the range).  The sequence's page count is (n + 15) / 16.
 struct PageMeta {
-  int b, g, page, np, n, valid, ks_bits, vs_bits;
+  int unit, page, n;
+  float ks, vs;          // FP8 scales of the page (per lane, all lanes alike)
 };
 
 // Values every lane of the wave holds alike (read from LDS or computed from
@@ -241,6 +246,13 @@ __device__ void page_prefix(const VerifyParams& P, int* s_cum, int* s_tmp) {
 // Work range of worker w out of n over W positions: [lo(w), lo(w+1)).
 __device__ inline long range_lo(long w, long W, long n) { return w * W / n; }
 
+// Waves in use and ranges over W positions: every range is taken by rg waves
+// (one per row group), and no range is empty.
+__device__ inline int used_ranges(const VerifyParams& P, long W) {
+  const long waves = min(long(P.n_wg) * kWaves, max(long(P.rg), W * P.rg / P.min_range));
+  return int(max(1L, min(W, waves / P.rg)));
+}
+
 // Worker whose range holds position p (all ranges are non-empty: n <= W).
 __device__ inline int owner_of(long p, long W, int n) {
   int w = int(p * n / W);
@@ -262,9 +274,12 @@ struct Cursor {
   int b, g, page, np, row, n;
 };
 
-template <int D, int NT, bool FP8, bool TREE>
+// SHARED: two waves (row groups) read the same pages at about the same time;
+// their loads keep the default cache policy so the second finds the first's
+// lines in L2.  Otherwise pages stream with the non-temporal policy.
+template <int D, int NT, bool FP8, bool TREE, bool SHARED>
 __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, int hi, int worker,
-                             int q_lds_off) {
+                             int q_lds_off, int row0) {
   using SH = Shape<D, NT, FP8>;
   using Regs = PageRegs<D, FP8>;
   constexpr int KS = SH::KS, DT = SH::DT, PF = SH::PF;
@@ -272,8 +287,6 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
   const int m16 = lane & 15, jg = lane >> 4;
   const unsigned lane_off = unsigned(m16 * 64 + jg * 16);
   const long page_stride = long(P.Hkv) * P.slab_bytes;
-  const i32x4 ks_rsrc = scalar_rsrc(P.k_scale, 0xFFFFFFFFu);
-  const i32x4 vs_rsrc = scalar_rsrc(P.v_scale, 0xFFFFFFFFu);
   const i32x4 len_rsrc = scalar_rsrc(P.seq_lens, 0xFFFFFFFFu);
   const i32x4 slot_rsrc = scalar_rsrc(P.batch_slots, P.batch_slots ? unsigned(P.batch) * 4u : 0u);
 
@@ -324,27 +337,38 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
     const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vb), 0, nrec, kBufferFlags);
 #pragma unroll
     for (int u = 0; u < SH::KL; ++u)
-      R.k[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off + u * 1024, 0, kStreamPolicy));
+      R.k[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off + u * 1024, 0, SHARED ? 0 : kStreamPolicy));
 #pragma unroll
     for (int cc = 0; cc < SH::VL; ++cc)
-      R.v[cc] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off + cc * 1024, 0, kStreamPolicy));
-    M.b = c.b;
-    M.g = c.g;
+      R.v[cc] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off + cc * 1024, 0, SHARED ? 0 : kStreamPolicy));
+    M.unit = (c.b << 16) | c.g;
     M.page = c.page;
-    M.np = c.np;
-    M.n = c.n;
-    M.valid = valid;
+    M.n = valid ? c.n : 0;
     if (FP8) {
-      M.ks_bits = s_buffer_load_dword(ks_rsrc, (id * P.Hkv + c.g) * 4, 0);
-      M.vs_bits = s_buffer_load_dword(vs_rsrc, (id * P.Hkv + c.g) * 4, 0);
+      // the scales come through the vector path, issued after the page's
+      // loads: they complete with the page, whereas a scalar load here
+      // (a random line of the scale arrays) would be waited for at the
+      // next scalar wait, one page later
+      const int so = (id * P.Hkv + c.g) * 4;
+      const auto rks = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(P.k_scale), 0, valid ? 0x7FFFFFFF : 0,
+                                                         kBufferFlags);
+      const auto rvs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(P.v_scale), 0, valid ? 0x7FFFFFFF : 0,
+                                                         kBufferFlags);
+      M.ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rks, 0, so, 0));
+      M.vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rvs, 0, so, 0));
     }
   };
-  // Q fragments (B operand of S^T = K Q^T) of unit (b, g): row 16nt+m16,
-  // channels (D/4)jg + 8s .. +7; rows past n_q*G read row 0 (never output).
+  // This wave's rows are row0 .. row0 + rows_here - 1 of the unit's n_q*G
+  // rows; lane row 16nt+m16 is local.  Rows past them read row row0 (never
+  // output).
+  const int rows_here = min(P.rows_w, P.rows - row0);
+  auto local_ok = [&](int nt) { return nt * 16 + m16 < rows_here; };
+  // Q fragments (B operand of S^T = K Q^T) of unit (b, g): local row 16nt+m16,
+  // channels (D/4)jg + 8s .. +7.
   auto load_q = [&](u32x4 (&q)[NT][KS], unsigned long long (&an)[NT], int b, int g) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int r = nt * 16 + m16 < P.rows ? nt * 16 + m16 : 0;
+      const int r = row0 + (local_ok(nt) ? nt * 16 + m16 : 0);
       const int i = r / P.G, h = g * P.G + r % P.G;
       const unsigned short* qp = static_cast<const unsigned short*>(P.q) +
                                  (long(b * P.n_q + i) * P.Hq + h) * D + (D / 4) * jg;
@@ -357,7 +381,7 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
   // ---- per-unit state --------------------------------------------------------
   int qi[NT];                     // verification slot of the row (padding rows: 64)
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) qi[nt] = nt * 16 + m16 < P.rows ? (nt * 16 + m16) / P.G : 64;
+  for (int nt = 0; nt < NT; ++nt) qi[nt] = local_ok(nt) ? (row0 + nt * 16 + m16) / P.G : 64;
   u32x4 qf[NT][KS];
   unsigned long long anc[NT];
 
@@ -384,9 +408,8 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
     const int rr = lane / LANES_PER_ROW, ch = lane % LANES_PER_ROW;
 #pragma unroll
     for (int k = 0; k < NT * 16 / RPI; ++k) {
-      if (k * RPI < P.rows) {
-        int r = k * RPI + rr;
-        r = r < P.rows ? r : 0;
+      if (k * RPI < rows_here) {
+        const int r = row0 + (k * RPI + rr < rows_here ? k * RPI + rr : 0);
         const int i = r / P.G, h = g * P.G + r % P.G;
         const unsigned short* src = static_cast<const unsigned short*>(P.q) +
                                     (long(b * P.n_q + i) * P.Hq + h) * D + ch * 8;
@@ -403,11 +426,12 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
     const unsigned char* qs = q_lds + slot * QSLOT;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int r = nt * 16 + m16 < P.rows ? nt * 16 + m16 : 0;
+      const int r = local_ok(nt) ? nt * 16 + m16 : 0;     // LDS row (local)
 #pragma unroll
       for (int s = 0; s < KS; ++s)
         qf[nt][s] = *reinterpret_cast<const u32x4*>(qs + (r * D + (D / 4) * jg + 8 * s) * 2);
-      if (TREE) anc[nt] = *reinterpret_cast<const unsigned long long*>(a_lds + slot * ASLOT + (r / P.G) * 8);
+      if (TREE)
+        anc[nt] = *reinterpret_cast<const unsigned long long*>(a_lds + slot * ASLOT + ((row0 + r) / P.G) * 8);
     }
   };
   float m_run[NT], l_run[NT];
@@ -417,18 +441,18 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
   auto finalize = [&]() {
     const bool full = u_first == 0 && u_last == u_np - 1;
     const int slot = units_done == 0 ? 0 : 1;
-    float* part = P.part + (long(worker) * 2 + slot) * slot_floats(P.rows, D);
+    float* part = P.part + (long(worker) * 2 + slot) * slot_floats(P.rows_w, D);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float l = l_run[nt];
       l += __shfl_xor(l, 16, 64);
       l += __shfl_xor(l, 32, 64);
-      const int r = nt * 16 + m16;
-      if (r < P.rows) {
+      const int rl = nt * 16 + m16, r = row0 + rl;
+      if (local_ok(nt)) {
         const float inv = full ? 1.0f / l : 1.0f;
         const int i = r / P.G, h = u_g * P.G + r % P.G;
         const long oi = long(u_b * P.n_q + i) * P.Hq + h;
-        float* dst = full ? P.out + oi * D : part + long(r) * D;
+        float* dst = full ? P.out + oi * D : part + long(rl) * D;
         if (FP8) {
 #pragma unroll
           for (int c = 0; c < D / 64; ++c)
@@ -455,8 +479,8 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
           if (full) {
             if (P.lse) P.lse[oi] = (m_run[nt] + __log2f(l)) * kLn2;
           } else {
-            part[long(P.rows) * D + r] = m_run[nt];
-            part[long(P.rows) * D + P.rows + r] = l;
+            part[long(P.rows_w) * D + rl] = m_run[nt];
+            part[long(P.rows_w) * D + P.rows_w + rl] = l;
           }
         }
       }
@@ -493,8 +517,8 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
     }
     float ksc = P.scale_log2, vsc = 1.0f;
     if (FP8) {
-      ksc *= __int_as_float(M.ks_bits);
-      vsc = __int_as_float(M.vs_bits);
+      ksc *= M.ks;
+      vsc = M.vs;
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -604,8 +628,9 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
   // ahead through the scalar unit.  The loop body is straight-line (positions
   // past hi are null loads, and their compute is skipped by a uniform branch),
   // so the compiler's wait counts keep all PF pages in flight.
-  Regs ring[PF + 1];
-  PageMeta meta[PF + 1];
+  constexpr int RS = SH::RS;
+  Regs ring[RS];
+  PageMeta meta[RS];
   Cursor c = locate(lo);
   const int len = hi - lo;
   int id_pend = s_buffer_load_dword(bt_rsrc(c), c.page * 4, 0);
@@ -628,14 +653,15 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
   };
 #pragma unroll
   for (int r = 0; r < PF; ++r) prefetch(ring[r], meta[r], r);
-  for (int i0 = 0; i0 < len; i0 += PF + 1) {
+  for (int i0 = 0; i0 < len; i0 += RS) {
 #pragma unroll
-    for (int r = 0; r <= PF; ++r) {
+    for (int r = 0; r < RS; ++r) {
       const int i = i0 + r;
-      prefetch(ring[(r + PF) % (PF + 1)], meta[(r + PF) % (PF + 1)], i + PF);
+      prefetch(ring[(r + PF) % RS], meta[(r + PF) % RS], i + PF);
       const PageMeta& M = meta[r];
-      if (M.valid) {
-        if (M.b != u_b || M.g != u_g) {          // a new unit starts at this position
+      if (M.n > 0) {
+        const int mb = M.unit >> 16, mg = M.unit & 0xFFFF;
+        if (mb != u_b || mg != u_g) {            // a new unit starts at this position
           if (u_b >= 0) finalize();
           if ((staged >> (cm_units & 31)) & 1u) {
             // the copy was issued before this page's loads, and the loads
@@ -644,17 +670,17 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
             asm volatile("" ::: "memory");
             read_q(cm_units % QS);
           } else {
-            load_q(qf, anc, M.b, M.g);
+            load_q(qf, anc, mb, mg);
             // wait here, on this rare path, so that the common path's MFMAs
             // never inherit a wait for these loads (which would also drain
             // every prefetched page)
             __builtin_amdgcn_s_waitcnt(kVmcnt0);
           }
           ++cm_units;
-          u_b = M.b;
-          u_g = M.g;
+          u_b = mb;
+          u_g = mg;
           u_first = M.page;
-          u_np = M.np;
+          u_np = (M.n + 15) >> 4;
           u_n = M.n;
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
@@ -686,18 +712,20 @@ __global__ __launch_bounds__(kThreads) void verify_merge_kernel(VerifyParams P) 
   if (W == 0) return;
   const int np = cum[b + 1] - cum[b];
   if (np == 0) return;
-  const int n_eff = int(min(long(P.n_wg) * kWaves, max(1L, W / P.min_range)));
+  const int n_rng = used_ranges(P, W);
   const long u0 = long(P.Hkv) * cum[b] + long(g) * np, u1 = u0 + np;
-  const int wf = owner_of(u0, W, n_eff), wl = owner_of(u1 - 1, W, n_eff);
+  const int wf = owner_of(u0, W, n_rng), wl = owner_of(u1 - 1, W, n_rng);
   if (wf == wl) return;                         // finished in place
   const int R = P.rows;
   const int x = blockIdx.y * kThreads + threadIdx.x;
   if (x >= R * (D / 4)) return;
   const int r = x / (D / 4), c4 = x % (D / 4);
-  const long sf = slot_floats(R, D);
-  // the first worker's piece is its second slot when its range began in an
+  // row r is row rl of row group rgi, held by wave (range * rg + rgi)
+  const int rgi = r / P.rows_w, rl = r % P.rows_w, RW = P.rows_w;
+  const long sf = slot_floats(RW, D);
+  // the first range's piece is its second slot when the range began in an
   // earlier unit; for the others the unit is their first
-  const long first_base = (2L * wf + (range_lo(wf, W, n_eff) != u0 ? 1 : 0)) * sf;
+  const long first_base = (2L * (long(wf) * P.rg + rgi) + (range_lo(wf, W, n_rng) != u0 ? 1 : 0)) * sf;
   const float* __restrict__ part = P.part;
   constexpr int KB = 8;
   float M = kNegInf, Ls = 0.0f;
@@ -708,10 +736,10 @@ __global__ __launch_bounds__(kThreads) void verify_merge_kernel(VerifyParams P) 
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int w = min(w0 + u, wl);
-      const long base = w == wf ? first_base : 2L * w * sf;
-      mk[u] = part[base + long(R) * D + r];
-      lk[u] = part[base + long(R) * D + R + r];
-      v[u] = *reinterpret_cast<const float4*>(part + base + long(r) * D + 4 * c4);
+      const long base = w == wf ? first_base : 2L * (long(w) * P.rg + rgi) * sf;
+      mk[u] = part[base + long(RW) * D + rl];
+      lk[u] = part[base + long(RW) * D + RW + rl];
+      v[u] = *reinterpret_cast<const float4*>(part + base + long(rl) * D + 4 * c4);
     }
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
@@ -749,7 +777,7 @@ size_t split_smem(int batch) {
 
 // Each wave is one worker streaming an equal contiguous range of the
 // (sequence, KV head, page) positions.
-template <int D, int NT, bool FP8, bool TREE>
+template <int D, int NT, bool FP8, bool TREE, bool SHARED>
 __global__ __launch_bounds__(kThreads) void verify_stream_kernel(VerifyParams P) {
   extern __shared__ int s_cum[];
   const int cum_words = (P.batch + 1 + 3) & ~3;
@@ -759,10 +787,11 @@ __global__ __launch_bounds__(kThreads) void verify_stream_kernel(VerifyParams P)
   const int W = P.Hkv * uni(s_cum[P.batch]);
   if (W == 0) return;
   const int worker = blockIdx.x * kWaves + uni(threadIdx.x >> 6);
-  const int n_eff = int(min(long(P.n_wg) * kWaves, max(1L, long(W) / P.min_range)));
-  if (worker >= n_eff) return;
-  const int lo = int(range_lo(worker, W, n_eff)), hi = int(range_lo(worker + 1, W, n_eff));
-  stream_range<D, NT, FP8, TREE>(P, s_cum, lo, hi, worker, cum_lds_bytes(P.batch));
+  const int n_rng = used_ranges(P, W);
+  const int range = worker / P.rg, rgi = worker % P.rg;
+  if (range >= n_rng) return;
+  const int lo = int(range_lo(range, W, n_rng)), hi = int(range_lo(range + 1, W, n_rng));
+  stream_range<D, NT, FP8, TREE, SHARED>(P, s_cum, lo, hi, worker, cum_lds_bytes(P.batch), rgi * P.rows_w);
 }
 
 // fp32 K/V (plain [token][channel] pages): one workgroup per (query head,
@@ -840,7 +869,7 @@ __global__ __launch_bounds__(128) void verify_f32_kernel(VerifyParams P) {
 }
 
 struct Plan {
-  int D, NT, rows, n_wg;
+  int D, NT, rows, n_wg, rg, rows_w;
   bool fp8, tree, f32;
   size_t cum_bytes, part_bytes;
 };
@@ -849,8 +878,9 @@ pkv_status check_args(const pkv_verify_args* a, Plan* pl) {
   if (!a) return fail(PKV_ERR_INVALID_ARG, "null args");
   if (a->batch < 1 || a->batch > 4096) return fail(PKV_ERR_INVALID_ARG, "batch must be in [1, 4096]");
   if (a->n_q < 1 || a->n_q > 64) return fail(PKV_ERR_INVALID_ARG, "n_q must be in [1, 64]");
-  if (a->num_kv_heads < 1 || a->num_q_heads < a->num_kv_heads || a->num_q_heads % a->num_kv_heads)
-    return fail(PKV_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+  if (a->num_kv_heads < 1 || a->num_kv_heads > 65535 || a->num_q_heads < a->num_kv_heads ||
+      a->num_q_heads % a->num_kv_heads)
+    return fail(PKV_ERR_INVALID_ARG, "num_kv_heads must be in [1, 65535] and divide num_q_heads");
   if (a->page_size != kPageSize) return fail(PKV_ERR_UNSUPPORTED, "page_size must be 16");
   if (a->head_dim != 64 && a->head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (a->block_table_stride < 1) return fail(PKV_ERR_INVALID_ARG, "block_table_stride must be >= 1");
@@ -875,7 +905,11 @@ pkv_status check_args(const pkv_verify_args* a, Plan* pl) {
   } else {
     return fail(PKV_ERR_INVALID_ARG, "unknown dtype");
   }
-  pl->NT = (pl->rows + 15) / 16;
+  // More than 48 rows: two waves share each range, 32 rows each (the same
+  // pages reach both from one fetch, and each keeps a 32-row register set).
+  pl->rg = pl->rows > 48 ? 2 : 1;
+  pl->rows_w = pl->rg == 1 ? pl->rows : 32;
+  pl->NT = (pl->rows_w + 15) / 16;
   return PKV_OK;
 }
 
@@ -915,9 +949,9 @@ size_t split_smem_rt(int D, int NT, int batch) {
   }
 }
 
-template <int D, int NT, bool FP8, bool TREE>
+template <int D, int NT, bool FP8, bool TREE, bool SHARED = false>
 const void* split_fn() {
-  return reinterpret_cast<const void*>(&verify_stream_kernel<D, NT, FP8, TREE>);
+  return reinterpret_cast<const void*>(&verify_stream_kernel<D, NT, FP8, TREE, SHARED>);
 }
 
 template <int D, int NT>
@@ -927,12 +961,15 @@ const void* pick_fn(bool fp8, bool tree) {
 }
 
 template <int D>
-const void* pick_fn(int NT, bool fp8, bool tree) {
+const void* pick_fn(int NT, bool shared, bool fp8, bool tree) {
+  if (shared) {
+    if (fp8) return tree ? split_fn<D, 2, true, true, true>() : split_fn<D, 2, true, false, true>();
+    return tree ? split_fn<D, 2, false, true, true>() : split_fn<D, 2, false, false, true>();
+  }
   switch (NT) {
     case 1: return pick_fn<D, 1>(fp8, tree);
     case 2: return pick_fn<D, 2>(fp8, tree);
-    case 3: return pick_fn<D, 3>(fp8, tree);
-    default: return pick_fn<D, 4>(fp8, tree);
+    default: return pick_fn<D, 3>(fp8, tree);
   }
 }
 
@@ -946,25 +983,25 @@ pkv_status make_plan(const pkv_verify_args* a, Plan* pl) {
     int n = a->num_splits;
     if (n == 0) {
       const size_t smem = split_smem_rt(pl->D, pl->NT, a->batch);
-      const void* fn = pl->D == 64 ? pick_fn<64>(pl->NT, pl->fp8, pl->tree)
-                                   : pick_fn<128>(pl->NT, pl->fp8, pl->tree);
+      const void* fn = pl->D == 64 ? pick_fn<64>(pl->NT, pl->rg > 1, pl->fp8, pl->tree)
+                                   : pick_fn<128>(pl->NT, pl->rg > 1, pl->fp8, pl->tree);
       n = resident_workgroups(fn, smem);
     }
     pl->n_wg = n;
     pl->cum_bytes = ((size_t(a->batch) + 1) * sizeof(int) + 255) & ~size_t(255);
-    pl->part_bytes = size_t(n) * kWaves * 2 * size_t(pl->rows) * (pl->D + 2) * sizeof(float);
+    pl->part_bytes = size_t(n) * kWaves * 2 * size_t(pl->rows_w) * (pl->D + 2) * sizeof(float);
   }
   return PKV_OK;
 }
 
-template <int D, int NT, bool FP8, bool TREE>
+template <int D, int NT, bool FP8, bool TREE, bool SHARED = false>
 hipError_t launch_split(const VerifyParams& p, hipStream_t st) {
   const size_t smem = split_smem<D, NT>(p.batch);
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&verify_stream_kernel<D, NT, FP8, TREE>),
+      reinterpret_cast<const void*>(&verify_stream_kernel<D, NT, FP8, TREE, SHARED>),
       hipFuncAttributeMaxDynamicSharedMemorySize, int(split_smem<D, NT>(4096)));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((verify_stream_kernel<D, NT, FP8, TREE>), dim3(p.n_wg), dim3(kThreads), smem, st, p);
+  hipLaunchKernelGGL((verify_stream_kernel<D, NT, FP8, TREE, SHARED>), dim3(p.n_wg), dim3(kThreads), smem, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((verify_merge_kernel<D>), dim3(p.batch * p.Hkv, (p.rows * (D / 4) + kThreads - 1) / kThreads),
@@ -980,11 +1017,14 @@ hipError_t dispatch_kv(const VerifyParams& p, bool fp8, bool tree, hipStream_t s
 
 template <int D>
 hipError_t dispatch_nt(const VerifyParams& p, int NT, bool fp8, bool tree, hipStream_t st) {
+  if (p.rg > 1) {
+    if (fp8) return tree ? launch_split<D, 2, true, true, true>(p, st) : launch_split<D, 2, true, false, true>(p, st);
+    return tree ? launch_split<D, 2, false, true, true>(p, st) : launch_split<D, 2, false, false, true>(p, st);
+  }
   switch (NT) {
     case 1: return dispatch_kv<D, 1>(p, fp8, tree, st);
     case 2: return dispatch_kv<D, 2>(p, fp8, tree, st);
-    case 3: return dispatch_kv<D, 3>(p, fp8, tree, st);
-    default: return dispatch_kv<D, 4>(p, fp8, tree, st);
+    default: return dispatch_kv<D, 3>(p, fp8, tree, st);
   }
 }
 
@@ -1033,6 +1073,8 @@ extern "C" pkv_status spec_verify_attention(const pkv_verify_args* a, void* stre
   p.Hkv = a->num_kv_heads;
   p.G = a->num_q_heads / a->num_kv_heads;
   p.rows = pl.rows;
+  p.rg = pl.rg;
+  p.rows_w = pl.rows_w;
   p.bt_stride = a->block_table_stride;
   p.n_wg = pl.n_wg;
   p.scale_log2 = a->sm_scale * kLog2e;
