@@ -19,7 +19,6 @@
 #include <mutex>
 #include <set>
 #include <unordered_map>
-#include <unordered_set>
 #include <vector>
 
 #include "common.h"
@@ -42,6 +41,7 @@ using namespace pkv;
 struct Seq {
   int32_t row = -1;
   int32_t len = 0;
+  uint64_t stamp = 0;                 // last call that listed this sequence
   std::vector<int32_t> pages;
 };
 
@@ -57,6 +57,7 @@ struct pkv_pool {
   std::set<int32_t> free_rows;
   std::unordered_map<int64_t, Seq> seqs;
   int64_t cow_copies = 0;
+  uint64_t calls = 0;                 // stamps of multi-sequence calls (duplicate check)
 
   int32_t take_page() {
     auto it = free_ranks.begin();
@@ -236,17 +237,22 @@ pkv_status paged_kv_append(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
     if (!ok) return fail(PKV_ERR_INVALID_ARG, "source dtype does not match the pool dtype");
   }
   // Validate and count pages by simulating the whole call on a copy of the
-  // reference counts of the touched tail pages.
-  std::unordered_set<int64_t> seen;
-  std::unordered_map<int32_t, int32_t> sim_ref;
+  // reference counts of the touched shared tail pages (few: a short list).
+  thread_local std::vector<Seq*> touched;
+  thread_local std::vector<std::pair<int32_t, int32_t>> sim_ref;
+  touched.clear();
+  sim_ref.clear();
+  const uint64_t stamp = ++pool->calls;
   int64_t need = 0, total_tokens = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
     auto it = pool->seqs.find(seqs[i]);
     if (it == pool->seqs.end()) return fail(PKV_ERR_UNKNOWN_SEQ, "append to unknown sequence");
-    if (!seen.insert(seqs[i]).second) return fail(PKV_ERR_INVALID_ARG, "sequence listed twice");
+    Seq& s = it->second;
+    if (s.stamp == stamp) return fail(PKV_ERR_INVALID_ARG, "sequence listed twice");
+    s.stamp = stamp;
+    touched.push_back(&s);
     int32_t n = n_tokens[i];
     if (n < 0) return fail(PKV_ERR_INVALID_ARG, "negative token count");
-    const Seq& s = it->second;
     int64_t new_pages = ceil_div(int64_t(s.len) + n, kPageSize);
     if (new_pages > d.max_pages_per_seq) return fail(PKV_ERR_CAPACITY, "sequence exceeds max_pages_per_seq");
     if (int64_t(s.len) + n > INT32_MAX) return fail(PKV_ERR_CAPACITY, "sequence too long");
@@ -254,10 +260,14 @@ pkv_status paged_kv_append(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
     if (n == 0) continue;
     if (s.len % kPageSize) {
       int32_t tail = s.pages[s.len / kPageSize];
-      auto r = sim_ref.emplace(tail, pool->refcount[tail]).first;
-      if (r->second > 1) {
-        need += 1;
-        r->second -= 1;
+      if (pool->refcount[tail] > 1) {
+        size_t r = 0;
+        while (r < sim_ref.size() && sim_ref[r].first != tail) ++r;
+        if (r == sim_ref.size()) sim_ref.emplace_back(tail, pool->refcount[tail]);
+        if (sim_ref[r].second > 1) {
+          need += 1;
+          sim_ref[r].second -= 1;
+        }
       }
     }
     need += new_pages - int64_t(s.pages.size());
@@ -273,10 +283,12 @@ pkv_status paged_kv_append(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
   // Copy-on-write copies go to the device before any token write of this
   // call: a write may land in a page that another sequence just stopped
   // sharing, and the copy must see that page's old contents.
-  std::vector<PoolTask> copies, writes;
+  thread_local std::vector<PoolTask> copies, writes;
+  copies.clear();
+  writes.clear();
   int64_t src_row = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
-    Seq& s = pool->seqs[seqs[i]];
+    Seq& s = *touched[i];
     int32_t n = n_tokens[i];
     if (n == 0) continue;
     int32_t L = s.len;
@@ -296,11 +308,8 @@ pkv_status paged_kv_append(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
         copies.push_back(c);
       }
     }
-    std::vector<char> fresh(ceil_div(int64_t(L) + n, kPageSize), 0);
-    while (int64_t(s.pages.size()) < ceil_div(int64_t(L) + n, kPageSize)) {
-      fresh[s.pages.size()] = 1;
-      s.pages.push_back(pool->take_page());
-    }
+    const int32_t first_fresh = int32_t(s.pages.size());     // pages taken by this call follow
+    while (int64_t(s.pages.size()) < ceil_div(int64_t(L) + n, kPageSize)) s.pages.push_back(pool->take_page());
     int32_t first_blk = L / kPageSize;
     int32_t last_blk = int32_t(ceil_div(int64_t(L) + n, kPageSize)) - 1;
     for (int32_t blk = first_blk; blk <= last_blk; ++blk) {
@@ -314,8 +323,9 @@ pkv_status paged_kv_append(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
       t.src_row = int32_t(src_row + (t0 - L));
       t.slot_begin = t0 - blk * kPageSize;
       t.n = t1 - t0;
-      t.flags = (fresh[blk] ? kFresh : 0) |
-                ((fresh[blk] || (blk == first_blk && cow_src >= 0)) ? kWriteTable : 0) |
+      const bool fresh = blk >= first_fresh;
+      t.flags = (fresh ? kFresh : 0) |
+                ((fresh || (blk == first_blk && cow_src >= 0)) ? kWriteTable : 0) |
                 (blk == last_blk ? kSetLen : 0);
       t.new_len = L + n;
       writes.push_back(t);
@@ -337,17 +347,21 @@ pkv_status paged_kv_rollback(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs
   if (n_seqs < 0 || (n_seqs > 0 && (!seqs || !n_tokens)))
     return fail(PKV_ERR_INVALID_ARG, "bad sequence list");
   std::lock_guard<std::mutex> lock(pool->mu);
-  std::unordered_set<int64_t> seen;
+  thread_local std::vector<Seq*> touched;
+  touched.clear();
+  const uint64_t stamp = ++pool->calls;
   for (int32_t i = 0; i < n_seqs; ++i) {
     auto it = pool->seqs.find(seqs[i]);
     if (it == pool->seqs.end()) return fail(PKV_ERR_UNKNOWN_SEQ, "rollback of unknown sequence");
-    if (!seen.insert(seqs[i]).second) return fail(PKV_ERR_INVALID_ARG, "sequence listed twice");
+    if (it->second.stamp == stamp) return fail(PKV_ERR_INVALID_ARG, "sequence listed twice");
+    it->second.stamp = stamp;
     if (n_tokens[i] < 0 || n_tokens[i] > it->second.len)
       return fail(PKV_ERR_INVALID_ARG, "rollback outside [0, len]");
+    touched.push_back(&it->second);
   }
   TaskSink sink(pool, nullptr, nullptr, pool->desc.kv_dtype, stream);
   for (int32_t i = 0; i < n_seqs; ++i) {
-    Seq& s = pool->seqs[seqs[i]];
+    Seq& s = *touched[i];
     if (n_tokens[i] == 0) continue;
     s.len -= n_tokens[i];
     size_t keep = size_t(ceil_div(s.len, kPageSize));
