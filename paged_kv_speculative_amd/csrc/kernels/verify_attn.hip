@@ -221,6 +221,21 @@ __device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 // Exclusive prefix of pages per sequence into s_cum[0..batch].
 __device__ void page_prefix(const VerifyParams& P, int* s_cum, int* s_tmp) {
   const int tid = threadIdx.x;
+  if (P.batch <= 64) {                         // one wave: a shuffle scan
+    if (tid < 64) {
+      int v = 0;
+      if (tid < P.batch) v = (P.seq_lens[P.batch_slots ? P.batch_slots[tid] : tid] + 15) >> 4;
+      int x = v;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (tid >= off) x += y;
+      }
+      if (tid < P.batch) s_cum[tid] = x - v;
+      if (tid == 63) s_cum[P.batch] = x;
+    }
+    __syncthreads();
+    return;
+  }
   const int per = (P.batch + kThreads - 1) / kThreads;
   const int b0 = min(P.batch, tid * per), b1 = min(P.batch, b0 + per);
   int local = 0;
