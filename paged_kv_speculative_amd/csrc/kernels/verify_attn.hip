@@ -273,12 +273,19 @@ __device__ inline int used_ranges(const VerifyParams& P, long W) {
 
 // Worker whose range holds position p (all ranges are non-empty: n <= W).
 __device__ inline int owner_of(long p, long W, int n) {
-  int w = int(p * n / W);
-  while (w + 1 < n && range_lo(w + 1, W, n) <= p) ++w;
-  while (w > 0 && range_lo(w, W, n) > p) --w;
+  // range_lo(w) <= p  <=>  w * W < (p + 1) * n: integer products only (no
+  // 64-bit division in the loop)
+  int w = int((double(p) * n) / double(W));
+  w = min(max(w, 0), n - 1);
+  while (w + 1 < n && long(w + 1) * W < (p + 1) * n) ++w;
+  while (w > 0 && long(w) * W >= (p + 1) * n) --w;
   return w;
 }
 
+// range_lo(w, W, n) == p without a division.
+__device__ inline bool range_starts_at(long w, long W, long n, long p) {
+  return p * n <= w * W && w * W < (p + 1) * n;
+}
 // The running maximum of a row is only moved when the block maximum exceeds
 // it by more than this (log2 units), so P <= 2^8 and the O rescale is rare.
 constexpr float kRescaleSlack = 8.0f;
@@ -743,7 +750,7 @@ __global__ __launch_bounds__(kThreads) void verify_merge_kernel(VerifyParams P) 
   const long sf = slot_floats(RW, D);
   // the first range's piece is its second slot when the range began in an
   // earlier unit; for the others the unit is their first
-  const long first_base = (2L * (long(wf) * P.rg + rgi) + (range_lo(wf, W, n_rng) != u0 ? 1 : 0)) * sf;
+  const long first_base = (2L * (long(wf) * P.rg + rgi) + (range_starts_at(wf, W, n_rng, u0) ? 0 : 1)) * sf;
   const float* __restrict__ part = P.part;
   constexpr int KB = 8;
   float M = kNegInf, Ls = 0.0f;
