@@ -50,7 +50,10 @@ TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "prof
 def measured_traffic(config):
     """HBM-side bytes per verification call from the committed counter
     summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when the
-    summary is for another workload or the kernel source has changed since."""
+    summary is for another workload or the kernel has changed since: the
+    summary names the files that make the kernel (its source and the build
+    script that holds its compile flags) and the sha256 of their contents,
+    concatenated in that order."""
     import hashlib
     if config != 2 or not os.path.exists(TRAFFIC_PROFILE):
         return None
@@ -60,8 +63,11 @@ def measured_traffic(config):
         if sep:
             fields[k] = v.strip()
     try:
-        src = os.path.join(os.path.dirname(os.path.abspath(__file__)), fields["kernel_source"])
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        root = os.path.dirname(os.path.abspath(__file__))
+        h = hashlib.sha256()
+        for name in fields["kernel_source"].split():
+            h.update(open(os.path.join(root, name), "rb").read())
+        digest = h.hexdigest()
         if digest != fields["kernel_source_sha256"]:
             return None
         return float(fields["traffic_bytes_per_call"])

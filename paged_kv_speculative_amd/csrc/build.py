@@ -23,6 +23,11 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 VALU ops are kept out of generated code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
+# Per-source additions.  The verification kernels keep their MFMA accumulators
+# in architectural VGPRs: left to its heuristics the compiler runs the MFMAs on
+# AGPRs and copies all O^T accumulators to VGPRs and back around every page
+# (about 130 extra VALU moves per page for 20 rows x head_dim 128).
+EXTRA = {"kernels/verify_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc():
@@ -35,9 +40,10 @@ def hipcc():
 def _compile(src):
     path = os.path.join(HERE, src)
     obj = os.path.join(BUILD, src.replace("/", "_") + ".o")
-    cmd = [hipcc()] + FLAGS + ["-c", path, "-o", obj]
+    flags = FLAGS + EXTRA.get(src, [])
+    cmd = [hipcc()] + flags + ["-c", path, "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [hipcc(), "-x", "hip"] + FLAGS + ["-c", path, "-o", obj]
+        cmd = [hipcc(), "-x", "hip"] + flags + ["-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)

@@ -100,20 +100,25 @@ __device__ inline unsigned pack_hi16(float a, float b) {
   return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
 }
 
-// bf16 round-to-nearest-even bits of a finite float, in the upper half.
-__device__ inline unsigned rne_bf16_bits(float x) {
-  unsigned u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two finite floats -> two bf16 rounded to nearest even (one hardware
+// conversion), a in the low half.
+__device__ inline unsigned pack_rne_bf16(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// Four fp8 (OCP E4M3) bytes -> four bf16 (exact) in two dwords.
+// Four fp8 (OCP E4M3) bytes -> four bf16 in two dwords, bytes 0,1 in the
+// first.  Every E4M3 value is a bf16 value, so with a unit scale the
+// conversion is exact.
 struct Dw2 {
   unsigned lo, hi;
 };
 __device__ inline Dw2 fp8x4_to_bf16x4(unsigned w) {
-  auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-  return Dw2{pack_hi16(f01[0], f01[1]), pack_hi16(f23[0], f23[1])};
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return Dw2{__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b)};
 }
 
 __device__ inline u32x4 load16(const void* p) { return *static_cast<const u32x4*>(p); }
@@ -608,21 +613,21 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
 #pragma unroll
         for (int e = 0; e < 4; ++e) p[e] *= vsc;
       }
-      float hi[4], lo[4];
+      if (kSplitP) {
+        // P = hi + lo: hi the truncated upper half, lo the rounded rest
+        float r[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (kSplitP) {
-          hi[e] = __uint_as_float(__float_as_uint(p[e]) & 0xFFFF0000u);
-          lo[e] = __uint_as_float(rne_bf16_bits(p[e] - hi[e]));
-        } else {
-          hi[e] = __uint_as_float(rne_bf16_bits(p[e]));
-          lo[e] = 0.0f;
-        }
+        for (int e = 0; e < 4; ++e)
+          r[e] = p[e] - __uint_as_float(__float_as_uint(p[e]) & 0xFFFF0000u);
+        ph[nt][0] = pack_hi16(p[0], p[1]);
+        ph[nt][1] = pack_hi16(p[2], p[3]);
+        pl[nt][0] = pack_rne_bf16(r[0], r[1]);
+        pl[nt][1] = pack_rne_bf16(r[2], r[3]);
+      } else {
+        ph[nt][0] = pack_rne_bf16(p[0], p[1]);
+        ph[nt][1] = pack_rne_bf16(p[2], p[3]);
+        pl[nt][0] = pl[nt][1] = 0u;
       }
-      ph[nt][0] = pack_hi16(hi[0], hi[1]);
-      ph[nt][1] = pack_hi16(hi[2], hi[3]);
-      pl[nt][0] = pack_hi16(lo[0], lo[1]);
-      pl[nt][1] = pack_hi16(lo[2], lo[3]);
     }
 
     // O^T += V^T P^T  (16 tokens of the page per MFMA)
