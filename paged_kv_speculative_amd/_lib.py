@@ -102,7 +102,7 @@ EXPORTS = {
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m paged_kv_speculative_amd.csrc.build` (there is no fallback)")
+                          "`python paged_kv_speculative_amd/csrc/build.py` (there is no fallback)")
     lib = C.CDLL(LIB_PATH)
     for name, (res, args) in EXPORTS.items():
         fn = getattr(lib, name)

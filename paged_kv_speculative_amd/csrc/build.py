@@ -1,6 +1,6 @@
 """Build libpkvspec.so for gfx950 with hipcc, in-tree.
 
-    python -m paged_kv_speculative_amd.csrc.build [--jobs N]
+    python paged_kv_speculative_amd/csrc/build.py [--jobs N]
 
 Every source is compiled on each call (the "does it build" check); objects go
 to paged_kv_speculative_amd/csrc/_build/ and the library to
