@@ -30,6 +30,8 @@ The model stores page contents in a plain [page][head][slot][dim] array (its
 own layout), so gathering a sequence back to contiguous K/V is a loop over the
 block table.
 """
+import heapq
+
 import numpy as np
 
 from . import fp8
@@ -54,6 +56,8 @@ class PoolModel:
         assert sorted(free_order) == list(range(num_pages)), "free order must be a permutation"
         self.rank = {p: r for r, p in enumerate(free_order)}
         self.free = set(range(num_pages))
+        # the same free set as a heap on (rank, page): lowest rank first
+        self._heap = sorted((r, p) for p, r in self.rank.items())
         self.refcount = [0] * num_pages
         self.tables = {}      # seq -> list of page ids
         self.lens = {}        # seq -> length in tokens
@@ -69,7 +73,8 @@ class PoolModel:
 
     # -- free set --------------------------------------------------------------
     def _take(self):
-        p = min(self.free, key=self.rank.__getitem__)
+        _, p = heapq.heappop(self._heap)
+        assert p in self.free
         self.free.remove(p)
         self.refcount[p] = 1
         return p
@@ -79,6 +84,7 @@ class PoolModel:
         assert self.refcount[p] >= 0
         if self.refcount[p] == 0:
             self.free.add(p)
+            heapq.heappush(self._heap, (self.rank[p], p))
 
     # -- sequence operations ---------------------------------------------------
     def alloc(self, seq, share_from=None, n_shared=0):
