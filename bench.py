@@ -47,14 +47,31 @@ TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "prof
                                "verify_traffic_llama3-8b-layer.md")
 
 
+def kernel_build_digest(sources):
+    """sha256 over the given source files (repository-relative) followed by
+    the hipcc flags the build script compiles the first of them with."""
+    import hashlib
+    import importlib.util
+    root = os.path.dirname(os.path.abspath(__file__))
+    spec = importlib.util.spec_from_file_location(
+        "_pkv_build_flags", os.path.join(root, "paged_kv_speculative_amd", "csrc", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    h = hashlib.sha256()
+    for name in sources:
+        h.update(open(os.path.join(root, name), "rb").read())
+    rel = os.path.relpath(os.path.join(root, sources[0]),
+                          os.path.join(root, "paged_kv_speculative_amd", "csrc"))
+    h.update(" ".join(b.FLAGS + b.EXTRA.get(rel, [])).encode())
+    return h.hexdigest()
+
+
 def measured_traffic(config):
     """HBM-side bytes per verification call from the committed counter
     summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when the
     summary is for another workload or the kernel has changed since: the
-    summary names the files that make the kernel (its source and the build
-    script that holds its compile flags) and the sha256 of their contents,
-    concatenated in that order."""
-    import hashlib
+    summary names the source files that make the kernel and the sha256 of
+    their contents followed by the kernel file's compile flags."""
     if config != 2 or not os.path.exists(TRAFFIC_PROFILE):
         return None
     fields = {}
@@ -63,12 +80,7 @@ def measured_traffic(config):
         if sep:
             fields[k] = v.strip()
     try:
-        root = os.path.dirname(os.path.abspath(__file__))
-        h = hashlib.sha256()
-        for name in fields["kernel_source"].split():
-            h.update(open(os.path.join(root, name), "rb").read())
-        digest = h.hexdigest()
-        if digest != fields["kernel_source_sha256"]:
+        if kernel_build_digest(fields["kernel_source"].split()) != fields["kernel_source_sha256"]:
             return None
         return float(fields["traffic_bytes_per_call"])
     except (KeyError, OSError, ValueError):
