@@ -115,3 +115,89 @@ def expected_accepted(alphas):
 def speedup(expected_k, gamma, r):
     """eta = (E[K] + 1) / (gamma * r + 1) (innvotechnologies.co, eq. eta)."""
     return (expected_k + 1.0) / (gamma * r + 1.0)
+
+
+# ----------------------------------------------------------------------------
+# Draft trees
+# ----------------------------------------------------------------------------
+# The pages verify a whole draft tree in one pass and then commit the accepted
+# branch (atozofsoftwareengineering.blog, pipeline diagram: "Tree-Attention
+# Verification" followed by "Dynamic KV Rollback/Commit") but state no
+# acceptance rule for several candidates at one position.  Reading taken: the
+# per-token rule of eq. alpha_i applied child by child with the residual
+# update between candidates (multi-candidate speculative sampling, as in
+# SpecInfer, Miao et al., ASPLOS 2024):
+#   at node u with target P and draft Q, the children c_1 < c_2 < ... of u
+#   (drafted i.i.d. from Q) are tried in index order; child c_j is accepted iff
+#   u_{c_j} < min(1, P_{j-1}(x_{c_j}) / Q(x_{c_j})), where P_0 = P and
+#   P_j = max(0, P_{j-1} - Q) normalised (P_j = P_{j-1} if that is zero
+#   everywhere).  An accepted child becomes the new node; if every child is
+#   rejected the next token is drawn from P_m (m = number of children); at a
+#   leaf the next token is drawn from the leaf's P (the bonus).
+# On a chain (one child per node) this is exactly accept_one with draft i =
+# node i + 1, which is why the counters are indexed the same way: the test of
+# node c uses accept_uniform(.., c - 1) and the draw at node u uses
+# sample_uniforms(.., u, V).
+
+
+def children_of(parents):
+    n = len(parents)
+    kids = [[] for _ in range(n)]
+    for c in range(1, n):
+        kids[parents[c]].append(c)
+    return kids
+
+
+def accept_tree_one(T, D, parents, tokens, seed, step, b):
+    """One sequence.  T, D [n, V]: target and draft logits at each node (the
+    distributions of that node's children); parents [n] (parents[0] = -1,
+    parents[c] < c); tokens [n] (tokens[0], the root's, is not used).
+    Returns dict with the accepted path (node ids, depth order, root
+    excluded), k = its length, the next token, its source and the decision
+    margins."""
+    n, V = T.shape
+    kids = children_of(parents)
+    margins = []
+    path = []
+    u = 0
+    while True:
+        if not kids[u]:
+            keys = np.asarray(T[u], dtype=np.float64) + gumbel(philox.sample_uniforms(seed, step, b, u, V))
+            source = "bonus"
+            break
+        p = np.exp(log_softmax(T[u]))
+        q = np.exp(log_softmax(D[u]))
+        taken = None
+        for c in kids[u]:
+            x = int(tokens[c])
+            a = min(1.0, p[x] / q[x])
+            uc = philox.accept_uniform(seed, step, b, c - 1)
+            margins.append(abs(uc - a))
+            if uc < a:
+                taken = c
+                break
+            r = np.maximum(p - q, 0.0)
+            if np.any(r > 0):
+                p = r / r.sum()
+        if taken is not None:
+            path.append(taken)
+            u = taken
+            continue
+        with np.errstate(divide="ignore"):
+            keys = np.log(p) + gumbel(philox.sample_uniforms(seed, step, b, u, V))
+        source = "residual"
+        break
+    token, gap = _argmax_with_gap(keys)
+    return {"k": len(path), "path": path, "node": u, "token": token, "source": source,
+            "accept_margins": margins, "sample_gap": gap}
+
+
+def spec_accept_tree(target_logits, draft_logits, parents, tokens, seed, step):
+    """Batch version.  target_logits, draft_logits [B, n, V]; parents, tokens
+    [B, n].  Returns (k [B], token [B], paths, per-sequence info)."""
+    B = target_logits.shape[0]
+    out = [accept_tree_one(target_logits[b], draft_logits[b], list(parents[b]), tokens[b],
+                           seed, step, b) for b in range(B)]
+    k = np.array([r["k"] for r in out], dtype=np.int32)
+    tok = np.array([r["token"] for r in out], dtype=np.int32)
+    return k, tok, [r["path"] for r in out], out

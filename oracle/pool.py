@@ -180,6 +180,50 @@ class PoolModel:
         del table[keep:]
         self.lens[seq] = L - n
 
+    def commit_path(self, seq, n_tree, path):
+        """Keep the accepted branch of a verified draft tree and drop the rest
+        (atozofsoftwareengineering.blog, pipeline diagram: tree verification
+        followed by "Dynamic KV Rollback/Commit").  The last n_tree tokens of
+        the sequence are the tree's nodes in index order (node 0, the root,
+        first); path lists the accepted nodes in depth order (root excluded,
+        ids strictly increasing, so node path[d] >= d + 1).  Node path[d]'s
+        K/V moves to position base + 1 + d (base = position of the root), in
+        increasing d, and the sequence is then truncated to base + 1 + k.
+        Reading: an FP8 token keeps its code when both positions share the
+        page's scale bit for bit, and is otherwise decoded with the source
+        scale (fp32 product) and quantised again with the destination scale
+        (the append rule's encoder)."""
+        if seq not in self.tables:
+            raise UnknownSeq(seq)
+        L, table = self.lens[seq], self.tables[seq]
+        k = len(path)
+        if not 1 <= n_tree <= L or k > n_tree - 1:
+            raise ValueError("bad tree size or path length")
+        if any(not 0 < c < n_tree for c in path) or any(a >= b for a, b in zip(path, path[1:])):
+            raise ValueError("path nodes must be increasing ids in (0, n_tree)")
+        base = L - n_tree
+        for d, c in enumerate(path):
+            src, dst = base + c, base + 1 + d
+            if src == dst:
+                continue
+            ps, os_ = table[src // self.S], src % self.S
+            pd, od = table[dst // self.S], dst % self.S
+            if self.refcount[pd] > 1:
+                raise ValueError("destination page is shared")
+            if self.fp8:
+                for h in range(self.H):
+                    for codes, sc in ((self.kc, self.ks), (self.vc, self.vs)):
+                        if np.float32(sc[ps, h]).view(np.uint32) == np.float32(sc[pd, h]).view(np.uint32):
+                            codes[pd, h, od] = codes[ps, h, os_]
+                        else:
+                            x = (fp8.decode(codes[ps, h, os_]).astype(np.float32) * np.float32(sc[ps, h])
+                                 ).astype(np.float32)
+                            codes[pd, h, od] = fp8.quantise(x, sc[pd, h])
+            else:
+                self.k[pd, :, od] = self.k[ps, :, os_]
+                self.v[pd, :, od] = self.v[ps, :, os_]
+        self.rollback(seq, n_tree - 1 - k)
+
     def release(self, seq):
         if seq not in self.tables:
             raise UnknownSeq(seq)

@@ -134,6 +134,28 @@ class Workload:
                 x[b, i] = min(int(np.searchsorted(c, u[b, i] * c[-1], side="right")), V - 1)
         return T, D, x
 
+    def tree_accept_inputs(self, step=0, batch=None):
+        """Draft-tree acceptance inputs: target and draft logits [B, n, V] ~
+        N(0, std) float32 at every node, and node tokens [B, n] where node c's
+        token is drawn from the draft distribution at its parent (siblings
+        independently) with the generator's own stream; token 0 (the root,
+        already emitted) is -1."""
+        B = self.batch if batch is None else batch
+        V, n = self.accept_vocab, self.n_q
+        rng = _rng(self.seed, 43, step)
+        T = rng.standard_normal((B, n, V), dtype=np.float32) * np.float32(self.accept_std)
+        D = rng.standard_normal((B, n, V), dtype=np.float32) * np.float32(self.accept_std)
+        u = rng.random((B, n))
+        x = np.full((B, n), -1, dtype=np.int32)
+        for b in range(B):
+            par = self.tree_parents[b % len(self.tree_parents)]
+            for c in range(1, n):
+                z = D[b, par[c]].astype(np.float64)
+                w = np.exp(z - z.max())
+                cs = np.cumsum(w)
+                x[b, c] = min(int(np.searchsorted(cs, u[b, c] * cs[-1], side="right")), V - 1)
+        return T, D, x
+
 
 def _pool_pages(seq_lens, prefix_len, factor=1.25):
     pages = sum(-(-int(n) // PAGE) for n in seq_lens)
@@ -202,6 +224,7 @@ def make(cfg, small=False, batch=None, seed=None):
         w = Workload("tree-fp8", seed, B, 15, 16, 32, 8, 128, "fp8", "bf16",
                      np.full(B, L))
         w.tree_parents = [_tree(_rng(seed, 51, b)) for b in range(B)]
+        w.accept_vocab = 1000 if small else VOCAB
     elif cfg == 5:
         B = batch or (6 if small else 256)
         prefix = 48 if small else 800
