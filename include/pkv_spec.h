@@ -148,6 +148,27 @@ pkv_status paged_kv_append(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
 pkv_status paged_kv_rollback(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
                              const int32_t* n_tokens, void* stream);
 
+/* Commit the accepted branch of a verified draft tree and drop the rest
+ * (atozofsoftwareengineering.blog, pipeline diagram: "Tree-Attention
+ * Verification" followed by "Dynamic KV Rollback/Commit").  For sequence
+ * seqs[i] the last n_tree[i] tokens are the tree's nodes in index order (node 0,
+ * the root, at position base = len - n_tree[i]); its accepted nodes are the
+ * next path_len[i] entries of path_nodes (all sequences' paths concatenated in
+ * call order), in depth order, root excluded, strictly increasing ids in
+ * (0, n_tree[i]) -- what spec_accept_tree returns.  Node path[d]'s K/V moves to
+ * position base + 1 + d (increasing d), then the sequence is truncated to
+ * base + 1 + path_len[i] tokens as by paged_kv_rollback.  FP8 pools keep a
+ * token's codes when source and destination (page, head) scales are equal bit
+ * for bit, and otherwise decode with the source scale and encode with the
+ * destination's (fp32, round to nearest even, saturating).  Requirements:
+ * 1 <= n_tree[i] <= min(64, len), path_len[i] <= n_tree[i] - 1, and every page
+ * holding a destination position referenced by this sequence only (else
+ * PKV_ERR_INVALID_ARG).  All-or-nothing over the call; the moves and the new
+ * lengths are written on `stream`. */
+pkv_status paged_kv_commit_path(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
+                                const int32_t* n_tree, const int32_t* path_len,
+                                const int32_t* path_nodes, void* stream);
+
 /* Unregister a sequence: every page loses a reference
  * (PagedKVCacheManager.ReleaseSession); its row's length is set to 0. */
 pkv_status paged_kv_release(pkv_pool* pool, int64_t seq, void* stream);
@@ -277,6 +298,54 @@ typedef struct {
 
 pkv_status spec_accept_workspace_size(const pkv_accept_args* args, size_t* bytes_out);
 pkv_status spec_accept(const pkv_accept_args* args, void* stream);
+
+/*
+ * Draft-tree acceptance.  The pages verify a draft tree in one pass and commit
+ * its accepted branch (atozofsoftwareengineering.blog, pipeline diagram) but
+ * give no rule for several candidates at one position; the rule implemented
+ * applies eq. alpha_i of innvotechnologies.co child by child with the residual
+ * update between candidates (multi-candidate speculative sampling, SpecInfer,
+ * Miao et al., ASPLOS 2024), which keeps the emitted tokens distributed as the
+ * target when sibling candidates are drawn independently from the draft:
+ *   at node u (starting at the root, node 0) with P = softmax(target_logits[b,u])
+ *   and Q = softmax(draft_logits[b,u]), the children c_1 < c_2 < ... of u are
+ *   tried in index order; c_j is accepted iff u_{c_j} < min(1, P_{j-1}(x_c)/Q(x_c)),
+ *   P_0 = P, P_j = max(0, P_{j-1} - Q) normalised (P_j = P_{j-1} if that is
+ *   zero everywhere); an accepted child becomes the new node.  If every child
+ *   of u is rejected, next_token is drawn from P_m (m = u's child count); at a
+ *   leaf it is drawn from the leaf's P (the bonus).
+ * Outputs: accepted_len[b] = k (depth of the accepted node), accepted_nodes[b]
+ * = the accepted node ids in depth order followed by -1s, next_token[b].  A
+ * sequence whose parents are not a tree in index order (parents[0] = -1,
+ * parents[c] in [0, c)) or whose nodes have more than max_children children
+ * gets k = -1 and next_token = -1.  A node token outside [0, vocab) is
+ * rejected.  Uniforms are those of spec_accept with draft i = node i + 1: the
+ * test of node c uses counter (0, b, step, (c - 1) | 1<<16) word 0, the draw at
+ * node u counters (x/4, b, step, u | 2<<16).  On a chain
+ * (parents[c] = c - 1) the result equals spec_accept's.
+ */
+typedef struct {
+  int32_t batch;
+  int32_t n_nodes;            /* nodes per tree including the root, 2..64        */
+  int32_t max_children;       /* bound on any node's child count, 1..n_nodes-1   */
+  int32_t vocab;              /* 1..2^26                                         */
+  const float* target_logits; /* device [batch][n_nodes][vocab]: at each node     */
+  const float* draft_logits;  /* device [batch][n_nodes][vocab]: at each node     */
+  const int32_t* parents;     /* device [batch][n_nodes]                          */
+  const int32_t* tokens;      /* device [batch][n_nodes]; entry 0 is not read     */
+  uint64_t seed;
+  uint32_t step;
+  int32_t* accepted_len;      /* device [batch]                                  */
+  int32_t* accepted_nodes;    /* device [batch][n_nodes]                          */
+  int32_t* next_token;        /* device [batch]                                  */
+  void* workspace;            /* device, >= spec_accept_tree_workspace_size bytes,
+                                 16-byte aligned; calls sharing it must not
+                                 overlap in time                                 */
+  size_t workspace_bytes;
+} pkv_tree_accept_args;
+
+pkv_status spec_accept_tree_workspace_size(const pkv_tree_accept_args* args, size_t* bytes_out);
+pkv_status spec_accept_tree(const pkv_tree_accept_args* args, void* stream);
 
 /* ------------------------------------------------------------------------ */
 const char* pkv_status_string(pkv_status status);

@@ -170,7 +170,7 @@ def accept_tree_one(T, D, parents, tokens, seed, step, b):
         taken = None
         for c in kids[u]:
             x = int(tokens[c])
-            a = min(1.0, p[x] / q[x])
+            a = min(1.0, p[x] / q[x]) if 0 <= x < V else 0.0   # a token outside the vocabulary is rejected
             uc = philox.accept_uniform(seed, step, b, c - 1)
             margins.append(abs(uc - a))
             if uc < a:

@@ -70,6 +70,16 @@ class AcceptArgs(C.Structure):
     ]
 
 
+class TreeAcceptArgs(C.Structure):
+    _fields_ = [
+        ("batch", C.c_int32), ("n_nodes", C.c_int32), ("max_children", C.c_int32),
+        ("vocab", C.c_int32), ("target_logits", C.c_void_p), ("draft_logits", C.c_void_p),
+        ("parents", C.c_void_p), ("tokens", C.c_void_p), ("seed", C.c_uint64), ("step", C.c_uint32),
+        ("accepted_len", C.c_void_p), ("accepted_nodes", C.c_void_p), ("next_token", C.c_void_p),
+        ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
+    ]
+
+
 EXPORTS = {
     # name: (restype, argtypes)
     "pkv_page_bytes": (C.c_int64, [C.c_int, C.c_int32, C.c_int32]),
@@ -82,6 +92,8 @@ EXPORTS = {
                                   C.c_void_p, C.c_int, C.c_void_p]),
     "paged_kv_rollback": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
     "paged_kv_release": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p]),
+    "paged_kv_commit_path": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                       C.c_void_p, C.c_void_p]),
     "paged_kv_block_table": (C.c_int, [C.c_void_p, C.c_int64, C.POINTER(C.c_int32), C.c_int32,
                                        C.POINTER(C.c_int32), C.POINTER(C.c_int32),
                                        C.POINTER(C.c_int32)]),
@@ -93,6 +105,8 @@ EXPORTS = {
     "spec_verify_attention": (C.c_int, [C.POINTER(VerifyArgs), C.c_void_p]),
     "spec_accept_workspace_size": (C.c_int, [C.POINTER(AcceptArgs), C.POINTER(C.c_size_t)]),
     "spec_accept": (C.c_int, [C.POINTER(AcceptArgs), C.c_void_p]),
+    "spec_accept_tree_workspace_size": (C.c_int, [C.POINTER(TreeAcceptArgs), C.POINTER(C.c_size_t)]),
+    "spec_accept_tree": (C.c_int, [C.POINTER(TreeAcceptArgs), C.c_void_p]),
     "pkv_status_string": (C.c_char_p, [C.c_int]),
     "pkv_last_error": (C.c_char_p, []),
     "pkv_version": (C.c_char_p, []),

@@ -4,8 +4,8 @@ import ctypes as C
 import numpy as np
 import torch
 
-from ._lib import (AcceptArgs, DTYPES, F32, BF16, FP8_E4M3, PoolDesc, PoolStats, VerifyArgs,
-                   check, i32_array, i64_array, lib)
+from ._lib import (AcceptArgs, DTYPES, F32, BF16, FP8_E4M3, PoolDesc, PoolStats, TreeAcceptArgs,
+                   VerifyArgs, check, i32_array, i64_array, lib)
 
 PAGE_SIZE = 16
 _TORCH_SRC = {torch.float32: F32, torch.bfloat16: BF16}
@@ -122,7 +122,8 @@ class Pool:
         sa, sp = _ints(seqs, np.int64)
         na, np_ = _ints(n_tokens, np.int32)
         assert sa.size == na.size
-        src_dtype, kp, vp = F32, None, None
+        # with nothing to write the source dtype only has to be a valid one
+        src_dtype, kp, vp = (F32 if self.kv_dtype == "fp8" else DTYPES[self.kv_dtype]), None, None
         if self.device is not None and int(na.sum()) > 0:
             assert k_src.is_contiguous() and v_src.is_contiguous() and k_src.dtype == v_src.dtype
             assert k_src.numel() >= int(na.sum()) * self.num_kv_heads * self.head_dim
@@ -141,6 +142,19 @@ class Pool:
         assert sa.size == na.size
         st = _stream(stream) if self.device is not None else None
         check(lib.paged_kv_rollback(self._h, sa.size, sp, np_, st))
+
+    def commit_path(self, seqs, n_tree, paths, stream=None):
+        """Keep each sequence's accepted tree branch (paths[i]: node ids in
+        depth order, root excluded) and drop the other tree nodes."""
+        sa, sp = _ints(seqs, np.int64)
+        ta, tp = _ints(n_tree, np.int32)
+        paths = [list(map(int, p)) for p in paths]
+        la, lp = _ints([len(p) for p in paths], np.int32)
+        flat = [c for p in paths for c in p]
+        fa, fp = _ints(flat if flat else [0], np.int32)
+        assert sa.size == ta.size == la.size
+        st = _stream(stream) if self.device is not None else None
+        check(lib.paged_kv_commit_path(self._h, sa.size, sp, tp, lp, fp, st))
 
     def release(self, seq, stream=None):
         st = _stream(stream) if self.device is not None else None
@@ -333,3 +347,44 @@ class PreparedAccept:
             self.args.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
         check(lib.spec_accept(C.byref(self.args), _stream(stream)))
         return self.buffers.accepted_len, self.buffers.next_token
+
+
+def tree_accept_workspace_size(args):
+    n = C.c_size_t()
+    check(lib.spec_accept_tree_workspace_size(C.byref(args), C.byref(n)))
+    return n.value
+
+
+def spec_accept_tree(target_logits, draft_logits, parents, tokens, seed, step, max_children=None,
+                     stream=None):
+    """Draft-tree acceptance.  target_logits, draft_logits [B, n, V] fp32,
+    parents and tokens [B, n] int32 (device).  max_children bounds any node's
+    child count (computed from the parents when not given: one host copy).
+    Returns (accepted_len [B], accepted_nodes [B, n], next_token [B])."""
+    B, n, V = target_logits.shape
+    assert draft_logits.shape == (B, n, V) and parents.shape == (B, n) and tokens.shape == (B, n)
+    assert target_logits.dtype == torch.float32 and draft_logits.dtype == torch.float32
+    assert parents.dtype == torch.int32 and tokens.dtype == torch.int32
+    for t in (target_logits, draft_logits, parents, tokens):
+        assert t.is_contiguous()
+    if max_children is None:
+        max_children = 1
+        for p in parents.cpu().numpy():
+            q = p[1:][(p[1:] >= 0) & (p[1:] < n)]
+            if q.size:
+                max_children = max(max_children, int(np.bincount(q).max()))
+        max_children = min(max_children, n - 1)
+    a = TreeAcceptArgs()
+    a.batch, a.n_nodes, a.max_children, a.vocab = B, n, int(max_children), V
+    a.target_logits, a.draft_logits = target_logits.data_ptr(), draft_logits.data_ptr()
+    a.parents, a.tokens = parents.data_ptr(), tokens.data_ptr()
+    a.seed, a.step = int(seed) & 0xFFFFFFFFFFFFFFFF, int(step) & 0xFFFFFFFF
+    dev = target_logits.device
+    k = torch.empty(B, dtype=torch.int32, device=dev)
+    nodes = torch.empty((B, n), dtype=torch.int32, device=dev)
+    tok = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, tree_accept_workspace_size(a)), dtype=torch.uint8, device=dev)
+    a.accepted_len, a.accepted_nodes, a.next_token = k.data_ptr(), nodes.data_ptr(), tok.data_ptr()
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    check(lib.spec_accept_tree(C.byref(a), _stream(stream)))
+    return k, nodes, tok

@@ -64,7 +64,32 @@ struct PoolDevice {
   const void* v_src;
 };
 
+// Token moves of a path commit: the K/V of token slot src_slot of page
+// src_page (all KV heads) go to slot dst_slot of page dst_page.  Moves of one
+// sequence form a group applied in order by one workgroup per four heads;
+// FP8 codes are re-encoded when the two pages' scales differ.
+struct PoolMove {
+  int32_t src_page;
+  int32_t dst_page;
+  int32_t slots;         // src_slot | dst_slot << 8
+};
+
+constexpr int kMoveGroups = 32;
+constexpr int kMovesPerLaunch = 256;
+
+struct PoolMoveBatch {
+  int32_t n_groups;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t kv_dtype;
+  int64_t page_bytes;
+  int32_t first[kMoveGroups + 1];    // group g = moves[first[g] .. first[g+1])
+  PoolMove moves[kMovesPerLaunch];
+};
+static_assert(sizeof(PoolMoveBatch) <= 4000, "kernel argument block too large");
+
 // Implemented in kernels/kv_append.hip.
 pkv_status launch_pool_update(const PoolDevice& dev, const PoolUpdateBatch& batch, void* stream);
+pkv_status launch_pool_moves(const PoolDevice& dev, const PoolMoveBatch& batch, void* stream);
 
 }  // namespace pkv

@@ -213,7 +213,85 @@ __global__ __launch_bounds__(kThreads) void pool_update_kernel(PoolDevice dev, P
   }
 }
 
+// Element e of channel c, token slot t of a (page, head) slab, in the pool's
+// layout, as raw bits (bf16/fp8) or a float (fp32).
+template <typename E>
+__device__ inline E& k_elem(char* slab, int t, int c, int D, int dtype) {
+  if (dtype == PKV_BF16) return *reinterpret_cast<E*>(slab + 2 * k_index_bf16(t, c, D));
+  if (dtype == PKV_F32) return *reinterpret_cast<E*>(slab + 4 * index_f32(t, c, D));
+  return *reinterpret_cast<E*>(slab + k_index_fp8(t, c, D));
+}
+template <typename E>
+__device__ inline E& v_elem(char* slab, int t, int c, int D, int dtype) {
+  if (dtype == PKV_BF16) return *reinterpret_cast<E*>(slab + 2 * v_index_bf16(t, c));
+  if (dtype == PKV_F32) return *reinterpret_cast<E*>(slab + 4 * index_f32(t, c, D));
+  return *reinterpret_cast<E*>(slab + v_index_fp8(t, c));
+}
+
+// One FP8 code moved between pages: kept when the scales are equal bit for
+// bit, else decoded with the source scale (fp32 product) and encoded again
+// with the destination's.
+__device__ inline unsigned char move_fp8(unsigned char code, float s_src, float s_dst) {
+  if (__float_as_uint(s_src) == __float_as_uint(s_dst)) return code;
+  const float x = __builtin_amdgcn_cvt_f32_fp8(int(code), 0) * s_src;
+  return quant_e4m3(x, 1.0f / s_dst);
+}
+
+// Block (group, y): heads 4y .. 4y+3 of one sequence's moves, one wave per
+// head, lane l moving channels l and l + 64.  The moves of a group run in
+// order; a later move never reads a slot an earlier one wrote (path nodes
+// lie at or after their destinations), and each lane touches only its own
+// channels, so program order is the only ordering needed.
+__global__ __launch_bounds__(kThreads) void pool_move_kernel(PoolDevice dev, PoolMoveBatch batch) {
+  const int H = batch.num_kv_heads, D = batch.head_dim, dt = batch.kv_dtype;
+  const long pb = batch.page_bytes;
+  const int h = blockIdx.y * kWaves + int(threadIdx.x >> 6);
+  if (h >= H) return;
+  const int lane = threadIdx.x & 63;
+  char* K = static_cast<char*>(dev.k_pages);
+  char* V = static_cast<char*>(dev.v_pages);
+  for (int i = batch.first[blockIdx.x]; i < batch.first[blockIdx.x + 1]; ++i) {
+    const PoolMove m = batch.moves[i];
+    const int ts = m.slots & 0xFF, td = (m.slots >> 8) & 0xFF;
+    const long so = (long(m.src_page) * H + h) * pb, dO = (long(m.dst_page) * H + h) * pb;
+    if (dt == PKV_FP8_E4M3) {
+      const float ks = dev.k_scale[long(m.src_page) * H + h], kd = dev.k_scale[long(m.dst_page) * H + h];
+      const float vs = dev.v_scale[long(m.src_page) * H + h], vd = dev.v_scale[long(m.dst_page) * H + h];
+      for (int c = lane; c < D; c += 64) {
+        const unsigned char kc = k_elem<unsigned char>(K + so, ts, c, D, dt);
+        const unsigned char vc = v_elem<unsigned char>(V + so, ts, c, D, dt);
+        k_elem<unsigned char>(K + dO, td, c, D, dt) = move_fp8(kc, ks, kd);
+        v_elem<unsigned char>(V + dO, td, c, D, dt) = move_fp8(vc, vs, vd);
+      }
+    } else if (dt == PKV_BF16) {
+      for (int c = lane; c < D; c += 64) {
+        const unsigned short kc = k_elem<unsigned short>(K + so, ts, c, D, dt);
+        const unsigned short vc = v_elem<unsigned short>(V + so, ts, c, D, dt);
+        k_elem<unsigned short>(K + dO, td, c, D, dt) = kc;
+        v_elem<unsigned short>(V + dO, td, c, D, dt) = vc;
+      }
+    } else {
+      for (int c = lane; c < D; c += 64) {
+        const float kc = k_elem<float>(K + so, ts, c, D, dt);
+        const float vc = v_elem<float>(V + so, ts, c, D, dt);
+        k_elem<float>(K + dO, td, c, D, dt) = kc;
+        v_elem<float>(V + dO, td, c, D, dt) = vc;
+      }
+    }
+  }
+}
+
 }  // namespace
+
+pkv_status launch_pool_moves(const PoolDevice& dev, const PoolMoveBatch& batch, void* stream) {
+  if (batch.n_groups <= 0) return PKV_OK;
+  const unsigned gy = unsigned((batch.num_kv_heads + kWaves - 1) / kWaves);
+  hipLaunchKernelGGL(pool_move_kernel, dim3(batch.n_groups, gy), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), dev, batch);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_ERR_DEVICE, std::string("pool move launch: ") + hipGetErrorString(e));
+  return PKV_OK;
+}
 
 pkv_status launch_pool_update(const PoolDevice& dev, const PoolUpdateBatch& batch, void* stream) {
   if (batch.n_tasks <= 0) return PKV_OK;

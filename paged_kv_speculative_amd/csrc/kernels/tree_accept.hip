@@ -1,0 +1,460 @@
+// Draft-tree acceptance: accepted branch and next token (gfx950).
+//
+// Rule (the per-token test of innvotechnologies.co, section "Verification
+// Acceptance Probabilities and Speedup Math", eq. alpha_i, applied to the
+// candidates of a draft tree child by child with the residual update between
+// them, as in multi-candidate speculative sampling; the pages verify and
+// commit trees, atozofsoftwareengineering.blog pipeline diagram, without
+// stating a rule):
+//   at node u with P = softmax(target at u), Q = softmax(draft at u), the
+//   children c_1 < c_2 < ... are tried in index order; c_j is accepted iff
+//   u_{c_j} < min(1, P_{j-1}(x) / Q(x)), P_0 = P, P_j = max(0, P_{j-1} - Q)
+//   normalised (P_{j-1} again if that is zero everywhere).  Accepting moves to
+//   the child; rejecting every child ends with a draw from P_m; a leaf ends
+//   with a draw from its P (the bonus).
+//
+// The residual after j rejections depends on the node only, not on the draws,
+// so every candidate's test can be evaluated up front, in parallel:
+//  1. stats: workgroup (sequence, node, T|D row, chunk) reduces (max, sum 2^x)
+//     of its 8192 logits (internal nodes only);
+//  2. levels 1 .. max_children-1, one launch each: workgroup (sequence, node,
+//     chunk) sums 2^lr_j over its chunk, lr_j = log2 max(0, P_{j-1} - Q), with
+//     P_{j-1} rebuilt per logit from the row normalisers and the earlier
+//     levels' masses Z_1..Z_{j-1};
+//  3. draw: workgroup (sequence, chunk of 2048) tests every candidate (lane c
+//     tests node c against its sibling rank's residual), walks the tree by
+//     ballots to the stopping node, and computes its chunk's Gumbel-max
+//     candidates for the token drawn there;
+//  4. finish: one wave per sequence takes the best candidate.
+// Everything is kept in base-2 logs; P_{j-1} - Q is formed as
+// lp + log2(1 - 2^(lq - lp)), accurate where the two nearly cancel.
+
+#include <hip/hip_runtime.h>
+
+#include "../common.h"
+#include "sampling.h"
+
+namespace pkv {
+
+namespace {
+
+using namespace sampling;
+
+constexpr int kWaves = kThreads / 64;
+constexpr int kQuads = 8;                                 // 16-byte loads per thread (stats, levels)
+constexpr int kChunk = kThreads * kQuads * 4;             // logits per stats / level workgroup
+constexpr int kDrawQuads = 2;
+constexpr int kDrawChunk = kThreads * kDrawQuads * 4;     // logits per draw workgroup
+constexpr int kMaxVocab = 1 << 26;
+constexpr int kMaxBatch = 1 << 20;
+constexpr int kMaxNodes = 64;
+
+struct TreeParams {
+  const float* T;
+  const float* Dl;
+  const int* parents;
+  const int* tokens;
+  int* accepted_len;
+  int* accepted_nodes;
+  int* next_token;
+  float2* stats;       // [batch][n][2][chunks] (max, sum 2^x) in base 2
+  float* zpart;        // [batch][n][levels][chunks] residual masses per chunk
+  int4* cand;          // [batch][dchunks] (residual key bits, index, fallback key bits, index)
+  int batch, n, levels, max_children, vocab, chunks, dchunks;
+  unsigned k0, k1, step;
+};
+
+__device__ inline const float* trow(const TreeParams& P, int b, int u) {
+  return P.T + (long(b) * P.n + u) * P.vocab;
+}
+__device__ inline const float* drow(const TreeParams& P, int b, int u) {
+  return P.Dl + (long(b) * P.n + u) * P.vocab;
+}
+
+// Children of node u in sequence b (uniform across the workgroup).
+__device__ inline int child_count(const TreeParams& P, int b, int u) {
+  int m = 0;
+  for (int c = u + 1; c < P.n; ++c) m += P.parents[long(b) * P.n + c] == u;
+  return m;
+}
+
+// Block-wide (max, sum) combine of one value pair per thread; thread 0 gets it.
+__device__ inline void block_ms(float& m, float& s) {
+  for (int o = 32; o > 0; o >>= 1) combine_ms(m, s, __shfl_xor(m, o, 64), __shfl_xor(s, o, 64));
+  __shared__ float sm[kWaves], ss[kWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) {
+    sm[wave] = m;
+    ss[wave] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int w = 1; w < kWaves; ++w) combine_ms(m, s, sm[w], ss[w]);
+}
+
+__device__ inline float block_sum(float s) {
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  __shared__ float sp[kWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) sp[wave] = s;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int w = 1; w < kWaves; ++w) s += sp[w];
+  return s;
+}
+
+template <bool kAligned>
+__global__ __launch_bounds__(kThreads) void tree_stats_kernel(TreeParams P) {
+  const int chunk = blockIdx.x % P.chunks;
+  const int r = blockIdx.x / P.chunks;           // (b * n + u) * 2 + which
+  const int which = r & 1, u = (r >> 1) % P.n, b = (r >> 1) / P.n;
+  if (child_count(P, b, u) == 0) return;         // a leaf's normalisers are never used
+  const float* row = which ? drow(P, b, u) : trow(P, b, u);
+  float v[kQuads][4];
+  load_chunk<kAligned, kQuads, true>(row, P.vocab, chunk * (kChunk / 4), v);
+  float m = kNegInf;
+#pragma unroll
+  for (int q = 0; q < kQuads; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = fmaxf(m, v[q][e]);
+  m *= kLog2e;
+  float s = 0.0f;
+  if (m > kNegInf) {
+#pragma unroll
+    for (int q = 0; q < kQuads; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s += exp2_hw(__builtin_fmaf(v[q][e], kLog2e, -m));
+  }
+  block_ms(m, s);
+  if (threadIdx.x == 0) P.stats[long(r) * P.chunks + chunk] = make_float2(m, s);
+}
+
+// Base-2 log normaliser of row (b, u, which) from its chunk partials.
+__device__ inline float row_lse(const TreeParams& P, int b, int u, int which) {
+  const float2* st = P.stats + (long(b * P.n + u) * 2 + which) * P.chunks;
+  float m = kNegInf, s = 0.0f;
+  for (int c = 0; c < P.chunks; ++c) combine_ms(m, s, st[c].x, st[c].y);
+  return m + log2_hw(s);
+}
+
+// log2 of the residual mass Z_j of node u (j >= 1; -inf when it is zero).
+__device__ inline float level_lz(const TreeParams& P, int b, int u, int j) {
+  const float* z = P.zpart + (long(b * P.n + u) * P.levels + (j - 1)) * P.chunks;
+  float s = 0.0f;
+  for (int c = 0; c < P.chunks; ++c) s += z[c];
+  return s > 0.0f ? log2_hw(s) : kNegInf;
+}
+
+// One residual step in base-2 logs: lr = log2 max(0, 2^lp - 2^lq).
+__device__ inline float residual_log(float lp, float lq) {
+  return lp > lq ? lp + log2_one_minus_exp2(lq - lp) : kNegInf;
+}
+
+// lp_{j} from lp_0 through the node's first j levels (lz[i-1] = log2 Z_i).
+__device__ inline float advance_levels(float lp, float lq, const float* lz, int j) {
+  for (int i = 0; i < j; ++i) {
+    const float lr = residual_log(lp, lq);
+    lp = lz[i] > kNegInf ? lr - lz[i] : lp;
+  }
+  return lp;
+}
+
+// Level j (1-based): residual mass of P_{j-1} - Q per chunk, for nodes with
+// more than j children (their (j+1)-th candidate is tested against P_j).
+template <bool kAligned>
+__global__ __launch_bounds__(kThreads) void tree_level_kernel(TreeParams P, int j) {
+  const int chunk = blockIdx.x % P.chunks;
+  const int r = blockIdx.x / P.chunks;           // b * n + u
+  const int u = r % P.n, b = r / P.n;
+  if (child_count(P, b, u) <= j) return;
+  __shared__ float s_lz[kMaxNodes];
+  __shared__ float s_l[2];
+  const int t = threadIdx.x;
+  if (t < j - 1) s_lz[t] = level_lz(P, b, u, t + 1);
+  if (t == 64) s_l[0] = row_lse(P, b, u, 0);
+  if (t == 128) s_l[1] = row_lse(P, b, u, 1);
+  __syncthreads();
+  const float lt = s_l[0], ld = s_l[1];
+  float tv[kQuads][4], dv[kQuads][4];
+  const int q0 = chunk * (kChunk / 4);
+  load_chunk<kAligned, kQuads>(trow(P, b, u), P.vocab, q0, tv);
+  load_chunk<kAligned, kQuads>(drow(P, b, u), P.vocab, q0, dv);
+  float s = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kQuads; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lq = __builtin_fmaf(dv[q][e], kLog2e, -ld);
+      const float lp = advance_levels(__builtin_fmaf(tv[q][e], kLog2e, -lt), lq, s_lz, j - 1);
+      const float lr = residual_log(lp, lq);
+      s += lr > kNegInf ? exp2_hw(lr) : 0.0f;     // past the row: -inf
+    }
+  s = block_sum(s);
+  if (t == 0) P.zpart[(long(r) * P.levels + (j - 1)) * P.chunks + chunk] = s;
+}
+
+template <bool kAligned>
+__global__ __launch_bounds__(kThreads) void tree_draw_kernel(TreeParams P) {
+  const int chunk = blockIdx.x % P.dchunks;
+  const int b = blockIdx.x / P.dchunks;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  __shared__ int s_par[kMaxNodes];
+  __shared__ int s_nkids[kMaxNodes];
+  __shared__ float s_lt[kMaxNodes], s_ld[kMaxNodes];
+  __shared__ float s_lz[kMaxNodes][kMaxNodes];   // [node][level - 1]
+  __shared__ int s_node, s_m, s_bad;
+  __shared__ float sk[2][kWaves];
+  __shared__ int si[2][kWaves];
+  // tree shape: parents and child counts
+  if (wave == 0) {
+    const int par = lane < P.n ? (lane == 0 ? -1 : P.parents[long(b) * P.n + lane]) : -2;
+    const bool bad_par = lane < P.n && (lane == 0 ? P.parents[long(b) * P.n] != -1 : (par < 0 || par >= lane));
+    s_par[lane] = par;
+    int kids = 0;
+    for (int c = 0; c < P.n; ++c) kids += __shfl(par, c, 64) == lane;
+    s_nkids[lane] = lane < P.n ? kids : 0;
+    const unsigned long long bad = __ballot(bad_par || kids > P.max_children);
+    if (lane == 0) s_bad = bad != 0;
+  }
+  __syncthreads();
+  if (s_bad) {
+    if (chunk == 0) {
+      for (int i = t; i < P.n; i += kThreads) P.accepted_nodes[long(b) * P.n + i] = -1;
+      if (t == 0) P.accepted_len[b] = -1;
+    }
+    return;
+  }
+  // normalisers of internal nodes and their residual masses
+  for (int i = t; i < 2 * P.n; i += kThreads) {
+    const int u = i >> 1;
+    if (s_nkids[u] > 0) (i & 1 ? s_ld : s_lt)[u] = row_lse(P, b, u, i & 1);
+  }
+  for (int i = t; i < P.n * P.levels; i += kThreads) {
+    const int u = i / P.levels, j = i % P.levels + 1;
+    if (j < s_nkids[u]) s_lz[u][j - 1] = level_lz(P, b, u, j);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // lane c >= 1 tests candidate c against the residual of its sibling rank
+    bool acc = false;
+    if (lane >= 1 && lane < P.n) {
+      const int u = s_par[lane];
+      int rank = 0;
+      for (int c = 1; c < lane; ++c) rank += s_par[c] == u;
+      const int x = P.tokens[long(b) * P.n + lane];
+      if (x >= 0 && x < P.vocab) {
+        const float lq = __builtin_fmaf(drow(P, b, u)[x], kLog2e, -s_ld[u]);
+        const float lp = advance_levels(__builtin_fmaf(trow(P, b, u)[x], kLog2e, -s_lt[u]), lq, s_lz[u], rank);
+        const float d = lp - lq;
+        const float a = d >= 0.0f ? 1.0f : exp2_hw(d);
+        const Philox4 r = philox4x32_10(0u, unsigned(b), P.step, unsigned(lane - 1) | (kPurposeAccept << 16),
+                                        P.k0, P.k1);
+        acc = uniform01(r.x[0]) < a;
+      }
+    }
+    const unsigned long long accepted = __ballot(acc);
+    // walk from the root: the first accepted child (in index order) is taken
+    int node = 0, depth = 0;
+    unsigned long long kids;
+    while (true) {
+      kids = __ballot(lane < P.n && s_par[lane] == node);
+      const unsigned long long take = kids & accepted;
+      if (!take) break;
+      node = __builtin_ctzll(take);
+      if (chunk == 0 && lane == 0) P.accepted_nodes[long(b) * P.n + depth] = node;
+      ++depth;
+    }
+    if (lane == 0) {
+      s_node = node;
+      s_m = __builtin_popcountll(kids);
+      if (chunk == 0) P.accepted_len[b] = depth;
+    }
+    if (chunk == 0)
+      for (int i = depth + lane; i < P.n; i += 64) P.accepted_nodes[long(b) * P.n + i] = -1;
+  }
+  __syncthreads();
+  const int u = s_node, m = s_m;
+  const int q0 = chunk * (kDrawChunk / 4);
+  float tv[kDrawQuads][4], dv[kDrawQuads][4];
+  float rk = kNegInf, fk = kNegInf;
+  int ri = 0x7FFFFFFF, fi = 0x7FFFFFFF;
+  const unsigned c3 = unsigned(u) | (kPurposeSample << 16);
+  load_chunk<kAligned, kDrawQuads>(trow(P, b, u), P.vocab, q0, tv);
+  if (m > 0) {
+    // every child rejected: residual P_{m-1} - Q, falling back to P_{m-1}
+    load_chunk<kAligned, kDrawQuads>(drow(P, b, u), P.vocab, q0, dv);
+    const float lt = s_lt[u], ld = s_ld[u];
+#pragma unroll
+    for (int qq = 0; qq < kDrawQuads; ++qq) {
+      const int q = q0 + qq * kThreads + t;
+      const Philox4 r = philox4x32_10(unsigned(q), unsigned(b), P.step, c3, P.k0, P.k1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int x = q * 4 + e;
+        const float g = gumbel2(uniform01(r.x[e]));
+        const float lq = __builtin_fmaf(dv[qq][e], kLog2e, -ld);
+        const float lp = advance_levels(__builtin_fmaf(tv[qq][e], kLog2e, -lt), lq, s_lz[u], m - 1);
+        better(fk, fi, lp + g, x);
+        better(rk, ri, residual_log(lp, lq) + g, x);
+      }
+    }
+  } else {
+    // a leaf: the bonus draw from its target (keys shifted by a constant)
+#pragma unroll
+    for (int qq = 0; qq < kDrawQuads; ++qq) {
+      const int q = q0 + qq * kThreads + t;
+      const Philox4 r = philox4x32_10(unsigned(q), unsigned(b), P.step, c3, P.k0, P.k1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) better(fk, fi, tv[qq][e] * kLog2e + gumbel2(uniform01(r.x[e])), q * 4 + e);
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    better(rk, ri, __shfl_xor(rk, o, 64), __shfl_xor(ri, o, 64));
+    better(fk, fi, __shfl_xor(fk, o, 64), __shfl_xor(fi, o, 64));
+  }
+  if (lane == 0) {
+    sk[0][wave] = rk;
+    si[0][wave] = ri;
+    sk[1][wave] = fk;
+    si[1][wave] = fi;
+  }
+  __syncthreads();
+  if (t == 0) {
+    for (int w = 1; w < kWaves; ++w) {
+      better(rk, ri, sk[0][w], si[0][w]);
+      better(fk, fi, sk[1][w], si[1][w]);
+    }
+    P.cand[long(b) * P.dchunks + chunk] = make_int4(__float_as_int(rk), ri, __float_as_int(fk), fi);
+  }
+}
+
+// One wave per sequence: the best candidate over the chunks (-1 for a
+// sequence whose tree was rejected).
+__global__ __launch_bounds__(64) void tree_finish_kernel(TreeParams P) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  if (P.accepted_len[b] < 0) {
+    if (lane == 0) P.next_token[b] = -1;
+    return;
+  }
+  float rk = kNegInf, fk = kNegInf;
+  int ri = 0x7FFFFFFF, fi = 0x7FFFFFFF;
+  for (int c = lane; c < P.dchunks; c += 64) {
+    const int4 v = P.cand[long(b) * P.dchunks + c];
+    better(rk, ri, __int_as_float(v.x), v.y);
+    better(fk, fi, __int_as_float(v.z), v.w);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    better(rk, ri, __shfl_xor(rk, o, 64), __shfl_xor(ri, o, 64));
+    better(fk, fi, __shfl_xor(fk, o, 64), __shfl_xor(fi, o, 64));
+  }
+  if (lane == 0) P.next_token[b] = rk > kNegInf ? ri : fi;
+}
+
+struct WsLayout {
+  size_t stats, zpart, cand, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+WsLayout ws_layout(const pkv_tree_accept_args* a) {
+  const size_t ch = (size_t(a->vocab) + kChunk - 1) / kChunk;
+  const size_t dch = (size_t(a->vocab) + kDrawChunk - 1) / kDrawChunk;
+  const size_t levels = size_t(a->max_children > 1 ? a->max_children - 1 : 1);
+  const size_t rows = size_t(a->batch) * a->n_nodes;
+  WsLayout w;
+  w.stats = 0;
+  w.zpart = align256(rows * 2 * ch * sizeof(float2));
+  w.cand = w.zpart + align256(rows * levels * ch * sizeof(float));
+  w.total = w.cand + size_t(a->batch) * dch * sizeof(int4);
+  return w;
+}
+
+pkv_status check_shape(const pkv_tree_accept_args* a) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "null args");
+  if (a->batch < 1 || a->batch > kMaxBatch) return fail(PKV_ERR_INVALID_ARG, "batch must be in [1, 2^20]");
+  if (a->n_nodes < 2 || a->n_nodes > kMaxNodes) return fail(PKV_ERR_INVALID_ARG, "n_nodes must be in [2, 64]");
+  if (a->max_children < 1 || a->max_children > a->n_nodes - 1)
+    return fail(PKV_ERR_INVALID_ARG, "max_children must be in [1, n_nodes - 1]");
+  if (a->vocab < 1 || a->vocab > kMaxVocab) return fail(PKV_ERR_INVALID_ARG, "vocab must be in [1, 2^26]");
+  const long long ch = (a->vocab + kChunk - 1) / kChunk;
+  const long long dch = (a->vocab + kDrawChunk - 1) / kDrawChunk;
+  if (ch * a->batch * a->n_nodes * 2 > 0x7FFFFFFFll || dch * a->batch > 0x7FFFFFFFll)
+    return fail(PKV_ERR_INVALID_ARG, "batch * n_nodes * vocab too large for one launch");
+  return PKV_OK;
+}
+
+}  // namespace
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" pkv_status spec_accept_tree_workspace_size(const pkv_tree_accept_args* a, size_t* bytes_out) {
+  if (!bytes_out) return fail(PKV_ERR_INVALID_ARG, "null output");
+  pkv_status st = check_shape(a);
+  if (st != PKV_OK) return st;
+  *bytes_out = ws_layout(a).total;
+  return PKV_OK;
+}
+
+extern "C" pkv_status spec_accept_tree(const pkv_tree_accept_args* a, void* stream) {
+  pkv_status st = check_shape(a);
+  if (st != PKV_OK) return st;
+  if (!a->target_logits || !a->draft_logits || !a->parents || !a->tokens || !a->accepted_len ||
+      !a->accepted_nodes || !a->next_token)
+    return fail(PKV_ERR_INVALID_ARG, "null device pointer");
+  if ((reinterpret_cast<uintptr_t>(a->target_logits) | reinterpret_cast<uintptr_t>(a->draft_logits)) & 15)
+    return fail(PKV_ERR_INVALID_ARG, "logit arrays must be 16-byte aligned");
+  const WsLayout w = ws_layout(a);
+  if (!a->workspace || a->workspace_bytes < w.total)
+    return fail(PKV_ERR_WORKSPACE, "workspace smaller than spec_accept_tree_workspace_size");
+  if (reinterpret_cast<uintptr_t>(a->workspace) & 15)
+    return fail(PKV_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  TreeParams p{};
+  p.T = a->target_logits;
+  p.Dl = a->draft_logits;
+  p.parents = a->parents;
+  p.tokens = a->tokens;
+  p.accepted_len = a->accepted_len;
+  p.accepted_nodes = a->accepted_nodes;
+  p.next_token = a->next_token;
+  char* ws = static_cast<char*>(a->workspace);
+  p.stats = reinterpret_cast<float2*>(ws + w.stats);
+  p.zpart = reinterpret_cast<float*>(ws + w.zpart);
+  p.cand = reinterpret_cast<int4*>(ws + w.cand);
+  p.batch = a->batch;
+  p.n = a->n_nodes;
+  p.max_children = a->max_children;
+  p.levels = a->max_children > 1 ? a->max_children - 1 : 1;
+  p.vocab = a->vocab;
+  p.chunks = (a->vocab + kChunk - 1) / kChunk;
+  p.dchunks = (a->vocab + kDrawChunk - 1) / kDrawChunk;
+  p.k0 = unsigned(a->seed & 0xFFFFFFFFu);
+  p.k1 = unsigned(a->seed >> 32);
+  p.step = a->step;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool aligned = (a->vocab & 3) == 0;
+  const unsigned rows = unsigned(a->batch) * a->n_nodes;
+  if (aligned) hipLaunchKernelGGL(tree_stats_kernel<true>, dim3(rows * 2 * p.chunks), dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL(tree_stats_kernel<false>, dim3(rows * 2 * p.chunks), dim3(kThreads), 0, s, p);
+  hipError_t e = hipGetLastError();
+  for (int j = 1; e == hipSuccess && j < a->max_children; ++j) {
+    if (aligned) hipLaunchKernelGGL(tree_level_kernel<true>, dim3(rows * p.chunks), dim3(kThreads), 0, s, p, j);
+    else hipLaunchKernelGGL(tree_level_kernel<false>, dim3(rows * p.chunks), dim3(kThreads), 0, s, p, j);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) {
+    const unsigned n_draw = unsigned(a->batch) * p.dchunks;
+    if (aligned) hipLaunchKernelGGL(tree_draw_kernel<true>, dim3(n_draw), dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL(tree_draw_kernel<false>, dim3(n_draw), dim3(kThreads), 0, s, p);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(tree_finish_kernel, dim3(a->batch), dim3(64), 0, s, p);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return fail(PKV_ERR_DEVICE, std::string("tree accept launch: ") + hipGetErrorString(e));
+  return PKV_OK;
+}

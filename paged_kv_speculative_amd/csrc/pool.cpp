@@ -373,6 +373,99 @@ pkv_status paged_kv_rollback(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs
   return sink.status;
 }
 
+pkv_status paged_kv_commit_path(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
+                                const int32_t* n_tree, const int32_t* path_len,
+                                const int32_t* path_nodes, void* stream) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "null pool");
+  if (n_seqs < 0 || (n_seqs > 0 && (!seqs || !n_tree || !path_len)))
+    return fail(PKV_ERR_INVALID_ARG, "bad sequence list");
+  std::lock_guard<std::mutex> lock(pool->mu);
+  thread_local std::vector<Seq*> touched;
+  touched.clear();
+  const uint64_t stamp = ++pool->calls;
+  int64_t off = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    auto it = pool->seqs.find(seqs[i]);
+    if (it == pool->seqs.end()) return fail(PKV_ERR_UNKNOWN_SEQ, "commit of unknown sequence");
+    Seq& s = it->second;
+    if (s.stamp == stamp) return fail(PKV_ERR_INVALID_ARG, "sequence listed twice");
+    s.stamp = stamp;
+    const int32_t nt = n_tree[i], k = path_len[i];
+    if (nt < 1 || nt > 64 || nt > s.len) return fail(PKV_ERR_INVALID_ARG, "n_tree outside [1, min(64, len)]");
+    if (k < 0 || k > nt - 1) return fail(PKV_ERR_INVALID_ARG, "path_len outside [0, n_tree - 1]");
+    if (k > 0 && !path_nodes) return fail(PKV_ERR_INVALID_ARG, "null path_nodes");
+    const int32_t base = s.len - nt;
+    for (int32_t d = 0; d < k; ++d) {
+      const int32_t c = path_nodes[off + d];
+      if (c <= (d ? path_nodes[off + d - 1] : 0) || c >= nt)
+        return fail(PKV_ERR_INVALID_ARG, "path nodes must be increasing ids in (0, n_tree)");
+      if (c != d + 1 && pool->refcount[s.pages[(base + 1 + d) / kPageSize]] > 1)
+        return fail(PKV_ERR_INVALID_ARG, "destination page is shared with another sequence");
+    }
+    off += k;
+    touched.push_back(&s);
+  }
+  // the moves, one group per sequence (in call order), then the truncation
+  PoolMoveBatch mb{};
+  mb.num_kv_heads = pool->desc.num_kv_heads;
+  mb.head_dim = pool->desc.head_dim;
+  mb.kv_dtype = pool->desc.kv_dtype;
+  mb.page_bytes = pool->page_bytes;
+  pkv_status status = PKV_OK;
+  int32_t n_moves = 0;
+  auto flush = [&]() {
+    if (mb.n_groups > 0 && pool->device) {
+      pkv_status st = launch_pool_moves(PoolDevice{pool->desc.k_pages, pool->desc.v_pages, pool->desc.k_scale,
+                                                   pool->desc.v_scale, pool->desc.block_table,
+                                                   pool->desc.seq_lens, nullptr, nullptr},
+                                        mb, stream);
+      if (st != PKV_OK && status == PKV_OK) status = st;
+    }
+    mb.n_groups = 0;
+    n_moves = 0;
+    mb.first[0] = 0;
+  };
+  off = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const Seq& s = *touched[i];
+    const int32_t nt = n_tree[i], k = path_len[i], base = s.len - nt;
+    bool open = false;
+    for (int32_t d = 0; d < k; ++d) {
+      const int32_t src = base + path_nodes[off + d], dst = base + 1 + d;
+      if (src == dst) continue;
+      if (n_moves == kMovesPerLaunch || (!open && mb.n_groups == kMoveGroups)) {
+        if (open) mb.n_groups++;
+        flush();
+        open = false;
+      }
+      if (!open) {
+        mb.first[mb.n_groups] = n_moves;
+        open = true;
+      }
+      mb.moves[n_moves++] = PoolMove{s.pages[src / kPageSize], s.pages[dst / kPageSize],
+                                     (src % kPageSize) | ((dst % kPageSize) << 8)};
+      mb.first[mb.n_groups + 1] = n_moves;
+    }
+    if (open) mb.n_groups++;
+    off += k;
+  }
+  flush();
+  if (status != PKV_OK) return status;
+  TaskSink sink(pool, nullptr, nullptr, pool->desc.kv_dtype, stream);
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    Seq& s = *touched[i];
+    const int32_t drop = n_tree[i] - 1 - path_len[i];
+    if (drop == 0) continue;
+    s.len -= drop;
+    size_t keep = size_t(ceil_div(s.len, kPageSize));
+    for (size_t j = keep; j < s.pages.size(); ++j) pool->unref(s.pages[j]);
+    s.pages.resize(keep);
+    sink.add(len_task(s.row, s.len));
+  }
+  sink.flush();
+  return sink.status;
+}
+
 pkv_status paged_kv_release(pkv_pool* pool, int64_t seq, void* stream) {
   if (!pool) return fail(PKV_ERR_INVALID_ARG, "null pool");
   std::lock_guard<std::mutex> lock(pool->mu);

@@ -197,3 +197,57 @@ def test_layout_maps_are_bijections():
             for f in (lambda: k_index(t, c, dt, D), lambda: v_index(t, c, dt)):
                 idx = f().reshape(-1)
                 assert sorted(idx.tolist()) == list(range(16 * D))
+
+
+def test_commit_path_bookkeeping_matches_oracle():
+    """paged_kv_commit_path on a metadata-only pool keeps the same pages,
+    lengths and free set as the oracle's commit (moves need a GPU)."""
+    rng = np.random.default_rng(12)
+    order = rng.permutation(120).astype(np.int32)
+    lp = Pool(120, 1, 64, "bf16", max_seqs=8, max_pages_per_seq=32, free_order=order)
+    model = PoolModel(120, 16, 1, 1, free_order=order)
+    parents = [-1, 0, 0, 0, 1, 1, 2, 3, 4, 4, 6, 8]
+    kids = [[c for c in range(len(parents)) if parents[c] == u] for u in range(len(parents))]
+    z = lambda n: np.zeros((n, 1, 1))
+    for s in range(6):
+        lp.alloc(s)
+        model.alloc(s)
+        ctx = int(rng.integers(0, 50))
+        lp.append([s], [ctx + len(parents)])
+        model.append(s, z(ctx + len(parents)), z(ctx + len(parents)))
+    for rnd in range(3):
+        paths = []
+        for s in range(6):
+            path, u = [], 0
+            while kids[u] and rng.random() < 0.7:
+                u = int(rng.choice(kids[u]))
+                path.append(u)
+            paths.append(path)
+        lp.commit_path(range(6), [len(parents)] * 6, paths)
+        for s in range(6):
+            model.commit_path(s, len(parents), paths[s])
+        _tables_equal(lp, model)
+        assert lp.stats()["free_pages"] == len(model.free)
+        for s in range(6):
+            lp.append([s], [len(parents)])
+            model.append(s, z(len(parents)), z(len(parents)))
+    model.check_invariants()
+
+
+def test_commit_path_errors_change_nothing():
+    lp = Pool(40, 1, 64, "bf16", max_seqs=4, max_pages_per_seq=8)
+    lp.alloc(0)
+    lp.append([0], [30])
+    before = lp.table(0)
+    for n_tree, path in [(6, [2, 1]), (6, [6]), (6, [0]), (31, []), (0, []), (6, [1, 2, 3, 4, 5, 6])]:
+        with pytest.raises(PkvError):
+            lp.commit_path([0], [n_tree], [path])
+        assert lp.table(0) == before
+    with pytest.raises(PkvError):                  # listed twice
+        lp.commit_path([0, 0], [6, 6], [[1], [1]])
+    lp.alloc(1, 0, 30)                             # every page now shared
+    with pytest.raises(PkvError):
+        lp.commit_path([0], [6], [[3]])
+    assert lp.table(0) == before
+    lp.commit_path([0], [6], [[1, 2]])             # in place: no move, truncation only
+    assert lp.table(0)[1] == 27
