@@ -5,6 +5,8 @@ A step is one pass of the whole path over the batch, as a serving loop runs it:
   2. spec_verify_attention verification queries over each sequence's pages
   3. spec_accept           acceptance rule, accepted length, next token
   4. paged_kv_rollback     commit 1+k tokens, drop the rejected gamma-k
+For a draft-tree workload steps 3 and 4 are spec_accept_tree (accepted branch)
+and paged_kv_commit_path (the branch's K/V moved into place, the rest dropped).
 (the accepted lengths are read back to the host each step, as a serving loop
 must to emit tokens).  Inputs are resident in HBM before the timed region.
 Several independent pool instances are used round-robin so that no step finds
@@ -143,6 +145,20 @@ class Instance:
             self.anc = torch.tensor(np.array(m, dtype=np.uint64).view(np.int64), device="cuda")
         V, gam = w.accept_vocab, w.gamma
         self.accept = V > 0 and w.tree_parents is None
+        self.tree_accept = V > 0 and w.tree_parents is not None
+        if self.tree_accept:
+            # logits at every tree node; node tokens drawn from the draft at
+            # the parent (siblings independently)
+            n = w.n_q
+            par = torch.tensor(np.array(w.tree_parents, dtype=np.int32), device="cuda")
+            self.parents = par
+            self.T = torch.randn((B, n, V), generator=g, device="cuda") * w.accept_std
+            self.D = torch.randn((B, n, V), generator=g, device="cuda") * w.accept_std
+            tok = torch.full((B, n), -1, dtype=torch.int32, device="cuda")
+            for c in range(1, n):
+                rows = self.D[torch.arange(B, device="cuda"), par[:, c].long()]
+                tok[:, c] = torch.multinomial(torch.softmax(rows, -1), 1, generator=g)[:, 0].to(torch.int32)
+            self.tokens = tok
         if self.accept:
             self.T = torch.randn((B, gam + 1, V), generator=g, device="cuda") * w.accept_std
             self.D = torch.randn((B, gam, V), generator=g, device="cuda") * w.accept_std
@@ -163,6 +179,8 @@ def run_gpu(args, w, torch, api):
         I.verify = I.pool.prepare_verify(I.q, nq, anc_mask=I.anc, sm_scale=w.sm_scale)
         if I.accept:
             I.accept_call = api.PreparedAccept(I.T, I.D, I.x, seed=12345)
+        if I.tree_accept:
+            I.accept_call = api.PreparedTreeAccept(I.T, I.D, I.parents, I.tokens, seed=12345)
     seq_ids = np.arange(B, dtype=np.int64)
     n_new = np.full(B, nq, dtype=np.int32)
     torch.cuda.synchronize()
@@ -172,6 +190,7 @@ def run_gpu(args, w, torch, api):
               for _ in range(total_steps)]
     step_lens, accepted = [], []
     k_host = torch.empty(B, dtype=torch.int32, pin_memory=True)
+    nodes_host = torch.empty((B, nq), dtype=torch.int32, pin_memory=True)
 
     def step(s):
         I = insts[s % R]
@@ -191,8 +210,25 @@ def run_gpu(args, w, torch, api):
             k_host.copy_(k, non_blocking=True)        # host needs k (and the tokens) every step
             torch.cuda.current_stream().synchronize()
             k = k_host.numpy()
+        elif I.tree_accept:
+            timed_acc = s % 4 == 0
+            if timed_acc:
+                acc_ev[s][0].record()
+            k, nodes, _ = I.accept_call(step=s)
+            if timed_acc:
+                acc_ev[s][1].record()
+            k_host.copy_(k, non_blocking=True)
+            nodes_host.copy_(nodes, non_blocking=True)
+            torch.cuda.current_stream().synchronize()
+            k = k_host.numpy()
+            nd = nodes_host.numpy()
+            accepted.append(k.copy())
+            # keep each accepted branch, drop the rest of the tree
+            I.pool.commit_path(seq_ids, n_new, [nd[b, :k[b]] for b in range(B)])
+            I.lens -= (nq - 1) - k
+            return
         else:
-            k = np.full(B, gam, dtype=np.int32)       # tree: commit policy outside this path
+            k = np.full(B, gam, dtype=np.int32)
             torch.cuda.synchronize()
         accepted.append(k.copy())
         drop = (nq - 1) - k
@@ -211,7 +247,7 @@ def run_gpu(args, w, torch, api):
     attn_ms = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in timed])
     attn_bytes = np.array([kv_bytes(step_lens[s], w) for s in timed], dtype=np.float64)
     acc_ms = (np.array([acc_ev[s][0].elapsed_time(acc_ev[s][1]) for s in timed if s % 4 == 0])
-              if insts[0].accept else None)
+              if insts[0].accept or insts[0].tree_accept else None)
     res = {
         "wall_s": wall, "steps": args.steps, "instances": R,
         "attn_ms": attn_ms, "attn_bytes": attn_bytes, "acc_ms": acc_ms,
@@ -243,8 +279,11 @@ def cpu_baseline(w, budget_s):
         for b in range(w.batch):
             if t_used >= budget_s:
                 break
-            if w.accept_vocab and w.tree_parents is None and T is None:
-                T, D, x = w.accept_inputs(step=0, batch=min(w.batch, 8))
+            if w.accept_vocab and T is None:
+                if w.tree_parents is None:
+                    T, D, x = w.accept_inputs(step=0, batch=min(w.batch, 8))
+                else:
+                    T, D, x = w.tree_accept_inputs(step=0, batch=min(w.batch, 4))
             t0 = time.perf_counter()
             n = int(w.seq_lens[b])
             pm = opool.PoolModel(-(-n // 16) + 2, 16, w.num_kv_heads, w.head_dim,
@@ -259,7 +298,10 @@ def cpu_baseline(w, budget_s):
             oatt.verify_attention(q[b:b + 1], [K], [V], w.n_q, anc, float(w.sm_scale))
             if T is not None:
                 j = b % T.shape[0]
-                oacc.accept_one(T[j], D[j], x[j], 12345, 0, j)
+                if w.tree_parents is None:
+                    oacc.accept_one(T[j], D[j], x[j], 12345, 0, j)
+                else:
+                    oacc.accept_tree_one(T[j], D[j], w.tree_parents[j], x[j], 12345, 0, j)
             t_used += time.perf_counter() - t0
             done += 1
     return {"value": done * w.n_q / t_used, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
@@ -328,7 +370,15 @@ def main():
             "algorithmic_bytes": float(np.mean(r["attn_bytes"])),
         },
     }
-    if r["acc_ms"] is not None:
+    if r["acc_ms"] is not None and w.tree_parents is not None:
+        # one pass over the target and draft rows of every internal node
+        internal = sum(len(set(p[1:])) for p in w.tree_parents[:B])
+        lb = 2 * internal * w.accept_vocab * 4
+        out["spec_accept_tree"] = {"us_median": float(np.median(r["acc_ms"]) * 1e3),
+                                   "logit_bytes": lb,
+                                   "logit_gbps": lb / (np.median(r["acc_ms"]) / 1e3) / 1e9,
+                                   "mean_accepted": r["mean_k"]}
+    elif r["acc_ms"] is not None:
         lb = B * (2 * w.gamma + 1) * w.accept_vocab * 4
         out["spec_accept"] = {"us_median": float(np.median(r["acc_ms"]) * 1e3),
                               "logit_gbps": lb / (np.median(r["acc_ms"]) / 1e3) / 1e9,

@@ -355,36 +355,59 @@ def tree_accept_workspace_size(args):
     return n.value
 
 
+def _max_children(parents, n):
+    m = 1
+    for p in parents.cpu().numpy():
+        q = p[1:][(p[1:] >= 0) & (p[1:] < n)]
+        if q.size:
+            m = max(m, int(np.bincount(q).max()))
+    return min(m, n - 1)
+
+
+class PreparedTreeAccept:
+    """spec_accept_tree with its arguments marshalled once.  target_logits,
+    draft_logits [B, n, V] fp32, parents and tokens [B, n] int32 (device),
+    read in place at each call.  max_children bounds any node's child count
+    (computed from the parents when not given: one host copy).  Each call
+    takes the step counter and returns (accepted_len [B], accepted_nodes
+    [B, n], next_token [B]) buffers it owns."""
+
+    def __init__(self, target_logits, draft_logits, parents, tokens, seed, max_children=None):
+        B, n, V = target_logits.shape
+        assert draft_logits.shape == (B, n, V) and parents.shape == (B, n) and tokens.shape == (B, n)
+        assert target_logits.dtype == torch.float32 and draft_logits.dtype == torch.float32
+        assert parents.dtype == torch.int32 and tokens.dtype == torch.int32
+        for t in (target_logits, draft_logits, parents, tokens):
+            assert t.is_contiguous()
+        if max_children is None:
+            max_children = _max_children(parents, n)
+        a = TreeAcceptArgs()
+        a.batch, a.n_nodes, a.max_children, a.vocab = B, n, int(max_children), V
+        a.target_logits, a.draft_logits = target_logits.data_ptr(), draft_logits.data_ptr()
+        a.parents, a.tokens = parents.data_ptr(), tokens.data_ptr()
+        a.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+        dev = target_logits.device
+        self.accepted_len = torch.empty(B, dtype=torch.int32, device=dev)
+        self.accepted_nodes = torch.empty((B, n), dtype=torch.int32, device=dev)
+        self.next_token = torch.empty(B, dtype=torch.int32, device=dev)
+        self.workspace = torch.empty(max(1, tree_accept_workspace_size(a)), dtype=torch.uint8, device=dev)
+        a.accepted_len, a.accepted_nodes = self.accepted_len.data_ptr(), self.accepted_nodes.data_ptr()
+        a.next_token = self.next_token.data_ptr()
+        a.workspace, a.workspace_bytes = self.workspace.data_ptr(), self.workspace.numel()
+        self.args = a
+        self._keep = (target_logits, draft_logits, parents, tokens)
+
+    def __call__(self, step, seed=None, stream=None):
+        self.args.step = int(step) & 0xFFFFFFFF
+        if seed is not None:
+            self.args.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+        check(lib.spec_accept_tree(C.byref(self.args), _stream(stream)))
+        return self.accepted_len, self.accepted_nodes, self.next_token
+
+
 def spec_accept_tree(target_logits, draft_logits, parents, tokens, seed, step, max_children=None,
                      stream=None):
-    """Draft-tree acceptance.  target_logits, draft_logits [B, n, V] fp32,
-    parents and tokens [B, n] int32 (device).  max_children bounds any node's
-    child count (computed from the parents when not given: one host copy).
-    Returns (accepted_len [B], accepted_nodes [B, n], next_token [B])."""
-    B, n, V = target_logits.shape
-    assert draft_logits.shape == (B, n, V) and parents.shape == (B, n) and tokens.shape == (B, n)
-    assert target_logits.dtype == torch.float32 and draft_logits.dtype == torch.float32
-    assert parents.dtype == torch.int32 and tokens.dtype == torch.int32
-    for t in (target_logits, draft_logits, parents, tokens):
-        assert t.is_contiguous()
-    if max_children is None:
-        max_children = 1
-        for p in parents.cpu().numpy():
-            q = p[1:][(p[1:] >= 0) & (p[1:] < n)]
-            if q.size:
-                max_children = max(max_children, int(np.bincount(q).max()))
-        max_children = min(max_children, n - 1)
-    a = TreeAcceptArgs()
-    a.batch, a.n_nodes, a.max_children, a.vocab = B, n, int(max_children), V
-    a.target_logits, a.draft_logits = target_logits.data_ptr(), draft_logits.data_ptr()
-    a.parents, a.tokens = parents.data_ptr(), tokens.data_ptr()
-    a.seed, a.step = int(seed) & 0xFFFFFFFFFFFFFFFF, int(step) & 0xFFFFFFFF
-    dev = target_logits.device
-    k = torch.empty(B, dtype=torch.int32, device=dev)
-    nodes = torch.empty((B, n), dtype=torch.int32, device=dev)
-    tok = torch.empty(B, dtype=torch.int32, device=dev)
-    ws = torch.empty(max(1, tree_accept_workspace_size(a)), dtype=torch.uint8, device=dev)
-    a.accepted_len, a.accepted_nodes, a.next_token = k.data_ptr(), nodes.data_ptr(), tok.data_ptr()
-    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
-    check(lib.spec_accept_tree(C.byref(a), _stream(stream)))
-    return k, nodes, tok
+    """Draft-tree acceptance (one call).  Returns (accepted_len [B],
+    accepted_nodes [B, n], next_token [B])."""
+    return PreparedTreeAccept(target_logits, draft_logits, parents, tokens, seed,
+                              max_children)(step, stream=stream)

@@ -78,16 +78,16 @@ __device__ inline void combine_ms(float& m, float& s, float m2, float s2) {
 }
 
 // Loads NQ quads per thread of one row, quad q at logits 4q..4q+3, thread t
-// taking quads q0 + u * kThreads + t.  Past the row's end: -inf.  kStream:
+// taking quads q0 + u * TH + t (TH threads per workgroup).  Past the row's end: -inf.  kStream:
 // non-temporal loads for data read once.
-template <bool kAligned, int NQ, bool kStream = false>
+template <bool kAligned, int NQ, bool kStream = false, int TH = kThreads>
 __device__ inline void load_chunk(const float* row, int vocab, int q0, float (&v)[NQ][4]) {
   if (kAligned) {
     const int nq = vocab >> 2;
     float4 f[NQ];
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
-      const int q = q0 + u * kThreads + int(threadIdx.x);
+      const int q = q0 + u * TH + int(threadIdx.x);
       typedef float f32x4 __attribute__((ext_vector_type(4)));
       const f32x4* src = reinterpret_cast<const f32x4*>(row) + q;
       f32x4 x = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
@@ -104,7 +104,7 @@ __device__ inline void load_chunk(const float* row, int vocab, int q0, float (&v
   } else {
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
-      const int x0 = (q0 + u * kThreads + int(threadIdx.x)) * 4;
+      const int x0 = (q0 + u * TH + int(threadIdx.x)) * 4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[u][e] = x0 + e < vocab ? row[x0 + e] : kNegInf;
     }

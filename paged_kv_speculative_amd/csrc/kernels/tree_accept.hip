@@ -21,11 +21,12 @@
 //     chunk) sums 2^lr_j over its chunk, lr_j = log2 max(0, P_{j-1} - Q), with
 //     P_{j-1} rebuilt per logit from the row normalisers and the earlier
 //     levels' masses Z_1..Z_{j-1};
-//  3. draw: workgroup (sequence, chunk of 2048) tests every candidate (lane c
-//     tests node c against its sibling rank's residual), walks the tree by
-//     ballots to the stopping node, and computes its chunk's Gumbel-max
-//     candidates for the token drawn there;
-//  4. finish: one wave per sequence takes the best candidate.
+//  3. decide: one workgroup per sequence tests every candidate (lane c tests
+//     node c against its sibling rank's residual) and walks the tree by
+//     ballots to the stopping node;
+//  4. draw: workgroup (sequence, chunk of 2048) computes its chunk's
+//     Gumbel-max candidates for the token drawn there;
+//  5. finish: one wave per sequence takes the best candidate.
 // Everything is kept in base-2 logs; P_{j-1} - Q is formed as
 // lp + log2(1 - 2^(lq - lp)), accurate where the two nearly cancel.
 
@@ -42,7 +43,13 @@ using namespace sampling;
 
 constexpr int kWaves = kThreads / 64;
 constexpr int kQuads = 8;                                 // 16-byte loads per thread (stats, levels)
-constexpr int kChunk = kThreads * kQuads * 4;             // logits per stats / level workgroup
+constexpr int kChunk = kThreads * kQuads * 4;             // logits per stats workgroup
+// Level kernels: small chunks (2048 logits) so that the few rows a level
+// needs are spread over many workgroups.
+constexpr int kLevelThreads = kThreads;
+constexpr int kLevelWaves = kLevelThreads / 64;
+constexpr int kLevelQuads = 2;
+constexpr int kLevelChunk = kLevelThreads * kLevelQuads * 4;
 constexpr int kDrawQuads = 2;
 constexpr int kDrawChunk = kThreads * kDrawQuads * 4;     // logits per draw workgroup
 constexpr int kMaxVocab = 1 << 26;
@@ -58,9 +65,11 @@ struct TreeParams {
   int* accepted_nodes;
   int* next_token;
   float2* stats;       // [batch][n][2][chunks] (max, sum 2^x) in base 2
-  float* zpart;        // [batch][n][levels][chunks] residual masses per chunk
+  float* zpart;        // [batch][n][levels][zchunks] residual masses per level chunk
   int4* cand;          // [batch][dchunks] (residual key bits, index, fallback key bits, index)
-  int batch, n, levels, max_children, vocab, chunks, dchunks;
+  int* decision;       // [batch][4]: stopping node (-1: rejected tree), its child count
+  float* decision_f;   // [batch][64 + 2]: the stopping node's lse of T, D and log2 Z_1..Z_{m-1}
+  int batch, n, levels, max_children, vocab, chunks, zchunks, dchunks;
   unsigned k0, k1, step;
 };
 
@@ -71,11 +80,12 @@ __device__ inline const float* drow(const TreeParams& P, int b, int u) {
   return P.Dl + (long(b) * P.n + u) * P.vocab;
 }
 
-// Children of node u in sequence b (uniform across the workgroup).
+// Children of node u in sequence b: one parent per lane, counted by a ballot
+// (every lane of the calling wave takes part; the result is wave-uniform).
 __device__ inline int child_count(const TreeParams& P, int b, int u) {
-  int m = 0;
-  for (int c = u + 1; c < P.n; ++c) m += P.parents[long(b) * P.n + c] == u;
-  return m;
+  const int lane = threadIdx.x & 63;
+  const int par = lane > 0 && lane < P.n ? P.parents[long(b) * P.n + lane] : -1;
+  return __popcll(__ballot(par == u));
 }
 
 // Block-wide (max, sum) combine of one value pair per thread; thread 0 gets it.
@@ -93,15 +103,16 @@ __device__ inline void block_ms(float& m, float& s) {
     for (int w = 1; w < kWaves; ++w) combine_ms(m, s, sm[w], ss[w]);
 }
 
+template <int NW>
 __device__ inline float block_sum(float s) {
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-  __shared__ float sp[kWaves];
+  __shared__ float sp[NW];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
   if (lane == 0) sp[wave] = s;
   __syncthreads();
   if (threadIdx.x == 0)
-    for (int w = 1; w < kWaves; ++w) s += sp[w];
+    for (int w = 1; w < NW; ++w) s += sp[w];
   return s;
 }
 
@@ -131,19 +142,25 @@ __global__ __launch_bounds__(kThreads) void tree_stats_kernel(TreeParams P) {
   if (threadIdx.x == 0) P.stats[long(r) * P.chunks + chunk] = make_float2(m, s);
 }
 
-// Base-2 log normaliser of row (b, u, which) from its chunk partials.
+// Base-2 log normaliser of row (b, u, which) from its chunk partials: lanes
+// take chunks c, c + 64, ... and the wave combines them (every lane calls).
 __device__ inline float row_lse(const TreeParams& P, int b, int u, int which) {
+  const int lane = threadIdx.x & 63;
   const float2* st = P.stats + (long(b * P.n + u) * 2 + which) * P.chunks;
   float m = kNegInf, s = 0.0f;
-  for (int c = 0; c < P.chunks; ++c) combine_ms(m, s, st[c].x, st[c].y);
+  for (int c = lane; c < P.chunks; c += 64) combine_ms(m, s, st[c].x, st[c].y);
+  for (int o = 32; o > 0; o >>= 1) combine_ms(m, s, __shfl_xor(m, o, 64), __shfl_xor(s, o, 64));
   return m + log2_hw(s);
 }
 
-// log2 of the residual mass Z_j of node u (j >= 1; -inf when it is zero).
+// log2 of the residual mass Z_j of node u (j >= 1; -inf when it is zero),
+// summed over the chunk partials by the calling wave.
 __device__ inline float level_lz(const TreeParams& P, int b, int u, int j) {
-  const float* z = P.zpart + (long(b * P.n + u) * P.levels + (j - 1)) * P.chunks;
+  const int lane = threadIdx.x & 63;
+  const float* z = P.zpart + (long(b * P.n + u) * P.levels + (j - 1)) * P.zchunks;
   float s = 0.0f;
-  for (int c = 0; c < P.chunks; ++c) s += z[c];
+  for (int c = lane; c < P.zchunks; c += 64) s += z[c];
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
   return s > 0.0f ? log2_hw(s) : kNegInf;
 }
 
@@ -163,50 +180,72 @@ __device__ inline float advance_levels(float lp, float lq, const float* lz, int 
 
 // Level j (1-based): residual mass of P_{j-1} - Q per chunk, for nodes with
 // more than j children (their (j+1)-th candidate is tested against P_j).
+// Level j (1-based): residual mass of P_{j-1} - Q per chunk, for nodes with
+// more than j children (their (j+1)-th candidate is tested against P_j).  A
+// tree of n nodes has at most (n-1)/(j+1) such nodes; workgroup (sequence,
+// slot, chunk) takes the slot-th of them in index order, if it exists.
 template <bool kAligned>
-__global__ __launch_bounds__(kThreads) void tree_level_kernel(TreeParams P, int j) {
-  const int chunk = blockIdx.x % P.chunks;
-  const int r = blockIdx.x / P.chunks;           // b * n + u
-  const int u = r % P.n, b = r / P.n;
-  if (child_count(P, b, u) <= j) return;
+__global__ __launch_bounds__(kLevelThreads) void tree_level_kernel(TreeParams P, int j, int slots) {
+  const int chunk = blockIdx.x % P.zchunks;
+  const int slot = (blockIdx.x / P.zchunks) % slots;
+  const int b = blockIdx.x / P.zchunks / slots;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // lane u counts node u's children; the node of this slot is the slot-th
+  // lane (in index order) with more than j
+  const int par = lane > 0 && lane < P.n ? P.parents[long(b) * P.n + lane] : -1;
+  int kids = 0;
+  for (int c = 1; c < P.n; ++c) kids += __shfl(par, c, 64) == lane;
+  const unsigned long long q = __ballot(lane < P.n && kids > j);
+  if (__popcll(q) <= slot) return;
+  unsigned long long rest = q;
+  for (int i = 0; i < slot; ++i) rest &= rest - 1;
+  const int u = __builtin_ctzll(rest);
+  const int r = b * P.n + u;
   __shared__ float s_lz[kMaxNodes];
   __shared__ float s_l[2];
-  const int t = threadIdx.x;
-  if (t < j - 1) s_lz[t] = level_lz(P, b, u, t + 1);
-  if (t == 64) s_l[0] = row_lse(P, b, u, 0);
-  if (t == 128) s_l[1] = row_lse(P, b, u, 1);
+  // waves 0 and 1: the row normalisers; the others: the earlier levels' masses
+  if (wave < 2) {
+    const float l = row_lse(P, b, u, wave);
+    if (lane == 0) s_l[wave] = l;
+  } else {
+    for (int i = wave - 2; i < j - 1; i += kLevelWaves - 2) {
+      const float l = level_lz(P, b, u, i + 1);
+      if (lane == 0) s_lz[i] = l;
+    }
+  }
   __syncthreads();
   const float lt = s_l[0], ld = s_l[1];
-  float tv[kQuads][4], dv[kQuads][4];
-  const int q0 = chunk * (kChunk / 4);
-  load_chunk<kAligned, kQuads>(trow(P, b, u), P.vocab, q0, tv);
-  load_chunk<kAligned, kQuads>(drow(P, b, u), P.vocab, q0, dv);
+  float tv[kLevelQuads][4], dv[kLevelQuads][4];
+  const int q0 = chunk * (kLevelChunk / 4);
+  load_chunk<kAligned, kLevelQuads, false, kLevelThreads>(trow(P, b, u), P.vocab, q0, tv);
+  load_chunk<kAligned, kLevelQuads, false, kLevelThreads>(drow(P, b, u), P.vocab, q0, dv);
   float s = 0.0f;
 #pragma unroll
-  for (int q = 0; q < kQuads; ++q)
+  for (int qq = 0; qq < kLevelQuads; ++qq)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float lq = __builtin_fmaf(dv[q][e], kLog2e, -ld);
-      const float lp = advance_levels(__builtin_fmaf(tv[q][e], kLog2e, -lt), lq, s_lz, j - 1);
+      const float lq = __builtin_fmaf(dv[qq][e], kLog2e, -ld);
+      const float lp = advance_levels(__builtin_fmaf(tv[qq][e], kLog2e, -lt), lq, s_lz, j - 1);
       const float lr = residual_log(lp, lq);
       s += lr > kNegInf ? exp2_hw(lr) : 0.0f;     // past the row: -inf
     }
-  s = block_sum(s);
-  if (t == 0) P.zpart[(long(r) * P.levels + (j - 1)) * P.chunks + chunk] = s;
+  s = block_sum<kLevelWaves>(s);
+  if (t == 0) P.zpart[(long(r) * P.levels + (j - 1)) * P.zchunks + chunk] = s;
 }
 
-template <bool kAligned>
-__global__ __launch_bounds__(kThreads) void tree_draw_kernel(TreeParams P) {
-  const int chunk = blockIdx.x % P.dchunks;
-  const int b = blockIdx.x / P.dchunks;
+// One workgroup per sequence: checks the tree, gathers the normalisers and
+// residual masses of its internal nodes, tests every candidate (lane c tests
+// node c against the residual of its sibling rank), and walks from the root
+// by ballots to the stopping node.  Writes the accepted branch and, for the
+// draw, the stopping node, its child count and its normalisers.
+__global__ __launch_bounds__(kThreads) void tree_decide_kernel(TreeParams P) {
+  const int b = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   __shared__ int s_par[kMaxNodes];
   __shared__ int s_nkids[kMaxNodes];
   __shared__ float s_lt[kMaxNodes], s_ld[kMaxNodes];
   __shared__ float s_lz[kMaxNodes][kMaxNodes];   // [node][level - 1]
-  __shared__ int s_node, s_m, s_bad;
-  __shared__ float sk[2][kWaves];
-  __shared__ int si[2][kWaves];
+  __shared__ int s_bad;
   // tree shape: parents and child counts
   if (wave == 0) {
     const int par = lane < P.n ? (lane == 0 ? -1 : P.parents[long(b) * P.n + lane]) : -2;
@@ -219,73 +258,103 @@ __global__ __launch_bounds__(kThreads) void tree_draw_kernel(TreeParams P) {
     if (lane == 0) s_bad = bad != 0;
   }
   __syncthreads();
+  int* dec = P.decision + long(b) * 4;
   if (s_bad) {
-    if (chunk == 0) {
-      for (int i = t; i < P.n; i += kThreads) P.accepted_nodes[long(b) * P.n + i] = -1;
-      if (t == 0) P.accepted_len[b] = -1;
+    for (int i = t; i < P.n; i += kThreads) P.accepted_nodes[long(b) * P.n + i] = -1;
+    if (t == 0) {
+      P.accepted_len[b] = -1;
+      dec[0] = -1;
     }
     return;
   }
-  // normalisers of internal nodes and their residual masses
-  for (int i = t; i < 2 * P.n; i += kThreads) {
-    const int u = i >> 1;
-    if (s_nkids[u] > 0) (i & 1 ? s_ld : s_lt)[u] = row_lse(P, b, u, i & 1);
-  }
-  for (int i = t; i < P.n * P.levels; i += kThreads) {
-    const int u = i / P.levels, j = i % P.levels + 1;
-    if (j < s_nkids[u]) s_lz[u][j - 1] = level_lz(P, b, u, j);
-  }
-  __syncthreads();
-  if (wave == 0) {
-    // lane c >= 1 tests candidate c against the residual of its sibling rank
-    bool acc = false;
-    if (lane >= 1 && lane < P.n) {
-      const int u = s_par[lane];
-      int rank = 0;
-      for (int c = 1; c < lane; ++c) rank += s_par[c] == u;
-      const int x = P.tokens[long(b) * P.n + lane];
-      if (x >= 0 && x < P.vocab) {
-        const float lq = __builtin_fmaf(drow(P, b, u)[x], kLog2e, -s_ld[u]);
-        const float lp = advance_levels(__builtin_fmaf(trow(P, b, u)[x], kLog2e, -s_lt[u]), lq, s_lz[u], rank);
-        const float d = lp - lq;
-        const float a = d >= 0.0f ? 1.0f : exp2_hw(d);
-        const Philox4 r = philox4x32_10(0u, unsigned(b), P.step, unsigned(lane - 1) | (kPurposeAccept << 16),
-                                        P.k0, P.k1);
-        acc = uniform01(r.x[0]) < a;
+  // normalisers of internal nodes and their residual masses: item
+  // (u, 0) and (u, 1) are the target and draft rows, (u, 1 + j) level j;
+  // wave w takes items w, w + 4, ... (each a wave reduction)
+  const int items = P.n * (P.levels + 2);
+  for (int i = wave; i < items; i += kWaves) {
+    const int u = i / (P.levels + 2), q = i % (P.levels + 2);
+    if (q < 2) {
+      if (s_nkids[u] > 0) {
+        const float l = row_lse(P, b, u, q);
+        if (lane == 0) (q ? s_ld : s_lt)[u] = l;
       }
+    } else if (q - 1 < s_nkids[u]) {
+      const float l = level_lz(P, b, u, q - 1);
+      if (lane == 0) s_lz[u][q - 2] = l;
     }
-    const unsigned long long accepted = __ballot(acc);
-    // walk from the root: the first accepted child (in index order) is taken
-    int node = 0, depth = 0;
-    unsigned long long kids;
-    while (true) {
-      kids = __ballot(lane < P.n && s_par[lane] == node);
-      const unsigned long long take = kids & accepted;
-      if (!take) break;
-      node = __builtin_ctzll(take);
-      if (chunk == 0 && lane == 0) P.accepted_nodes[long(b) * P.n + depth] = node;
-      ++depth;
-    }
-    if (lane == 0) {
-      s_node = node;
-      s_m = __builtin_popcountll(kids);
-      if (chunk == 0) P.accepted_len[b] = depth;
-    }
-    if (chunk == 0)
-      for (int i = depth + lane; i < P.n; i += 64) P.accepted_nodes[long(b) * P.n + i] = -1;
   }
   __syncthreads();
-  const int u = s_node, m = s_m;
+  if (wave != 0) return;
+  bool acc = false;
+  if (lane >= 1 && lane < P.n) {
+    const int u = s_par[lane];
+    int rank = 0;
+    for (int c = 1; c < lane; ++c) rank += s_par[c] == u;
+    const int x = P.tokens[long(b) * P.n + lane];
+    if (x >= 0 && x < P.vocab) {
+      const float lq = __builtin_fmaf(drow(P, b, u)[x], kLog2e, -s_ld[u]);
+      const float lp = advance_levels(__builtin_fmaf(trow(P, b, u)[x], kLog2e, -s_lt[u]), lq, s_lz[u], rank);
+      const float d = lp - lq;
+      const float a = d >= 0.0f ? 1.0f : exp2_hw(d);
+      const Philox4 r = philox4x32_10(0u, unsigned(b), P.step, unsigned(lane - 1) | (kPurposeAccept << 16),
+                                      P.k0, P.k1);
+      acc = uniform01(r.x[0]) < a;
+    }
+  }
+  const unsigned long long accepted = __ballot(acc);
+  // walk from the root: the first accepted child (in index order) is taken
+  int node = 0, depth = 0;
+  unsigned long long kids;
+  while (true) {
+    kids = __ballot(lane < P.n && s_par[lane] == node);
+    const unsigned long long take = kids & accepted;
+    if (!take) break;
+    node = __builtin_ctzll(take);
+    if (lane == 0) P.accepted_nodes[long(b) * P.n + depth] = node;
+    ++depth;
+  }
+  for (int i = depth + lane; i < P.n; i += 64) P.accepted_nodes[long(b) * P.n + i] = -1;
+  const int m = __builtin_popcountll(kids);
+  float* decf = P.decision_f + long(b) * (kMaxNodes + 2);
+  if (m > 0) {
+    if (lane == 0) {
+      decf[0] = s_lt[node];
+      decf[1] = s_ld[node];
+    }
+    if (lane < m - 1) decf[2 + lane] = s_lz[node][lane];
+  }
+  if (lane == 0) {
+    P.accepted_len[b] = depth;
+    dec[0] = node;
+    dec[1] = m;
+  }
+}
+
+// Workgroup (sequence, chunk of 2048 logits): the chunk's Gumbel-max
+// candidates for the token drawn at the stopping node: from the residual
+// P_{m-1} - Q after m rejections (falling back to P_{m-1}), or from the
+// target at a leaf (the bonus).
+template <bool kAligned>
+__global__ __launch_bounds__(kThreads) void tree_draw_kernel(TreeParams P) {
+  const int chunk = blockIdx.x % P.dchunks;
+  const int b = blockIdx.x / P.dchunks;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  __shared__ float s_f[kMaxNodes + 2];
+  __shared__ float sk[2][kWaves];
+  __shared__ int si[2][kWaves];
+  const int u = P.decision[long(b) * 4], m = P.decision[long(b) * 4 + 1];
+  if (u < 0) return;                             // rejected tree: no draw
+  if (t < m + 1) s_f[t] = P.decision_f[long(b) * (kMaxNodes + 2) + t];
   const int q0 = chunk * (kDrawChunk / 4);
   float tv[kDrawQuads][4], dv[kDrawQuads][4];
+  load_chunk<kAligned, kDrawQuads>(trow(P, b, u), P.vocab, q0, tv);
+  if (m > 0) load_chunk<kAligned, kDrawQuads>(drow(P, b, u), P.vocab, q0, dv);
+  __syncthreads();
   float rk = kNegInf, fk = kNegInf;
   int ri = 0x7FFFFFFF, fi = 0x7FFFFFFF;
   const unsigned c3 = unsigned(u) | (kPurposeSample << 16);
-  load_chunk<kAligned, kDrawQuads>(trow(P, b, u), P.vocab, q0, tv);
   if (m > 0) {
-    // every child rejected: residual P_{m-1} - Q, falling back to P_{m-1}
-    load_chunk<kAligned, kDrawQuads>(drow(P, b, u), P.vocab, q0, dv);
-    const float lt = s_lt[u], ld = s_ld[u];
+    const float lt = s_f[0], ld = s_f[1];
 #pragma unroll
     for (int qq = 0; qq < kDrawQuads; ++qq) {
       const int q = q0 + qq * kThreads + t;
@@ -295,13 +364,12 @@ __global__ __launch_bounds__(kThreads) void tree_draw_kernel(TreeParams P) {
         const int x = q * 4 + e;
         const float g = gumbel2(uniform01(r.x[e]));
         const float lq = __builtin_fmaf(dv[qq][e], kLog2e, -ld);
-        const float lp = advance_levels(__builtin_fmaf(tv[qq][e], kLog2e, -lt), lq, s_lz[u], m - 1);
+        const float lp = advance_levels(__builtin_fmaf(tv[qq][e], kLog2e, -lt), lq, s_f + 2, m - 1);
         better(fk, fi, lp + g, x);
         better(rk, ri, residual_log(lp, lq) + g, x);
       }
     }
   } else {
-    // a leaf: the bonus draw from its target (keys shifted by a constant)
 #pragma unroll
     for (int qq = 0; qq < kDrawQuads; ++qq) {
       const int q = q0 + qq * kThreads + t;
@@ -353,21 +421,24 @@ __global__ __launch_bounds__(64) void tree_finish_kernel(TreeParams P) {
 }
 
 struct WsLayout {
-  size_t stats, zpart, cand, total;
+  size_t stats, zpart, cand, decision, decision_f, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 WsLayout ws_layout(const pkv_tree_accept_args* a) {
   const size_t ch = (size_t(a->vocab) + kChunk - 1) / kChunk;
+  const size_t zch = (size_t(a->vocab) + kLevelChunk - 1) / kLevelChunk;
   const size_t dch = (size_t(a->vocab) + kDrawChunk - 1) / kDrawChunk;
   const size_t levels = size_t(a->max_children > 1 ? a->max_children - 1 : 1);
   const size_t rows = size_t(a->batch) * a->n_nodes;
   WsLayout w;
   w.stats = 0;
   w.zpart = align256(rows * 2 * ch * sizeof(float2));
-  w.cand = w.zpart + align256(rows * levels * ch * sizeof(float));
-  w.total = w.cand + size_t(a->batch) * dch * sizeof(int4);
+  w.cand = w.zpart + align256(rows * levels * zch * sizeof(float));
+  w.decision = w.cand + align256(size_t(a->batch) * dch * sizeof(int4));
+  w.decision_f = w.decision + align256(size_t(a->batch) * 4 * sizeof(int));
+  w.total = w.decision_f + size_t(a->batch) * (kMaxNodes + 2) * sizeof(float);
   return w;
 }
 
@@ -380,7 +451,9 @@ pkv_status check_shape(const pkv_tree_accept_args* a) {
   if (a->vocab < 1 || a->vocab > kMaxVocab) return fail(PKV_ERR_INVALID_ARG, "vocab must be in [1, 2^26]");
   const long long ch = (a->vocab + kChunk - 1) / kChunk;
   const long long dch = (a->vocab + kDrawChunk - 1) / kDrawChunk;
-  if (ch * a->batch * a->n_nodes * 2 > 0x7FFFFFFFll || dch * a->batch > 0x7FFFFFFFll)
+  const long long zch = (a->vocab + kLevelChunk - 1) / kLevelChunk;
+  if (ch * a->batch * a->n_nodes * 2 > 0x7FFFFFFFll || dch * a->batch > 0x7FFFFFFFll ||
+      zch * a->batch * (a->n_nodes / 2) > 0x7FFFFFFFll)
     return fail(PKV_ERR_INVALID_ARG, "batch * n_nodes * vocab too large for one launch");
   return PKV_OK;
 }
@@ -424,12 +497,15 @@ extern "C" pkv_status spec_accept_tree(const pkv_tree_accept_args* a, void* stre
   p.stats = reinterpret_cast<float2*>(ws + w.stats);
   p.zpart = reinterpret_cast<float*>(ws + w.zpart);
   p.cand = reinterpret_cast<int4*>(ws + w.cand);
+  p.decision = reinterpret_cast<int*>(ws + w.decision);
+  p.decision_f = reinterpret_cast<float*>(ws + w.decision_f);
   p.batch = a->batch;
   p.n = a->n_nodes;
   p.max_children = a->max_children;
   p.levels = a->max_children > 1 ? a->max_children - 1 : 1;
   p.vocab = a->vocab;
   p.chunks = (a->vocab + kChunk - 1) / kChunk;
+  p.zchunks = (a->vocab + kLevelChunk - 1) / kLevelChunk;
   p.dchunks = (a->vocab + kDrawChunk - 1) / kDrawChunk;
   p.k0 = unsigned(a->seed & 0xFFFFFFFFu);
   p.k1 = unsigned(a->seed >> 32);
@@ -441,8 +517,14 @@ extern "C" pkv_status spec_accept_tree(const pkv_tree_accept_args* a, void* stre
   else hipLaunchKernelGGL(tree_stats_kernel<false>, dim3(rows * 2 * p.chunks), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   for (int j = 1; e == hipSuccess && j < a->max_children; ++j) {
-    if (aligned) hipLaunchKernelGGL(tree_level_kernel<true>, dim3(rows * p.chunks), dim3(kThreads), 0, s, p, j);
-    else hipLaunchKernelGGL(tree_level_kernel<false>, dim3(rows * p.chunks), dim3(kThreads), 0, s, p, j);
+    const int slots = (a->n_nodes - 1) / (j + 1);
+    const dim3 grid(unsigned(a->batch) * slots * p.zchunks);
+    if (aligned) hipLaunchKernelGGL(tree_level_kernel<true>, grid, dim3(kLevelThreads), 0, s, p, j, slots);
+    else hipLaunchKernelGGL(tree_level_kernel<false>, grid, dim3(kLevelThreads), 0, s, p, j, slots);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(tree_decide_kernel, dim3(a->batch), dim3(kThreads), 0, s, p);
     e = hipGetLastError();
   }
   if (e == hipSuccess) {
