@@ -219,9 +219,16 @@ pkv_status spec_tree_ancestor_masks(int32_t n_nodes, const int32_t* parents, uin
  * (atozofsoftwareengineering.blog, eq. A_speculative; the verification
  * tokens' K/V must already be appended, futurestack.online section 2.3.)
  *
+ * Per-sequence draft counts (n_q_seq != NULL): sequence b has n_b =
+ * n_q_seq[b] verification slots (clamped to [1, n_q]), L = N - n_b, and only
+ * slots i < n_b are computed and written (q, anc_mask and out keep their
+ * [batch][n_q] shapes; the other slots are padding, neither read for the
+ * result nor written).  This serves policies that pick gamma per sequence
+ * (paurushmuley.com, dynamic lookahead; atozofsoftwareengineering.blog).
+ *
  * Supported: q_dtype F32 with kv_dtype F32; q_dtype BF16 with kv_dtype BF16
  * or FP8_E4M3; head_dim 64 or 128; page_size 16; n_q*Hq/Hkv <= 64 rows per KV
- * head; n_q <= 64; L >= 0 for every sequence.  Long contexts are split over
+ * head; n_q <= 64; 0 <= L and N < 2^24 for every sequence.  Long contexts are split over
  * workgroups and merged by log-sum-exp in a second kernel (workspace below).
  */
 typedef struct {
@@ -253,6 +260,7 @@ typedef struct {
   size_t workspace_bytes;
   int32_t num_splits;         /* workgroups sharing the work; 0 = as many as the
                                  GPU keeps resident                              */
+  const int32_t* n_q_seq;     /* device [batch] slots per sequence, or NULL (n_q) */
 } pkv_verify_args;
 
 pkv_status spec_verify_workspace_size(const pkv_verify_args* args, size_t* bytes_out);
@@ -275,6 +283,10 @@ pkv_status spec_verify_attention(const pkv_verify_args* args, void* stream);
  * u_x from counter (x/4, b, step, i | 2<<16), word x%4, and takes
  * argmax_x log w(x) - log(-log u_x) (Gumbel-max; ties to the smaller x).
  * u = (floor(word / 2^9) + 0.5) * 2^-23.
+ * Per-sequence draft counts (gammas != NULL): sequence b uses drafts
+ * i < g_b = gammas[b] (clamped to [1, gamma]), k <= g_b, and the bonus comes
+ * from P_{g_b}; the arrays keep their [batch][gamma(+1)] shapes and rows past
+ * g_b are not read for the result.
  * (innvotechnologies.co, eq. alpha_i and eq. E[K]; pipeline diagram
  *  "Rejection Recovery (Resample)".)
  */
@@ -294,6 +306,7 @@ typedef struct {
                                  results; calls that share a workspace must not
                                  overlap in time                                 */
   size_t workspace_bytes;
+  const int32_t* gammas;      /* device [batch] drafts per sequence, or NULL     */
 } pkv_accept_args;
 
 pkv_status spec_accept_workspace_size(const pkv_accept_args* args, size_t* bytes_out);

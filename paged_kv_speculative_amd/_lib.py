@@ -57,6 +57,7 @@ class VerifyArgs(C.Structure):
         ("seq_lens", C.c_void_p), ("batch_slots", C.c_void_p), ("anc_mask", C.c_void_p),
         ("sm_scale", C.c_float), ("out", C.c_void_p), ("lse", C.c_void_p),
         ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t), ("num_splits", C.c_int32),
+        ("n_q_seq", C.c_void_p),
     ]
 
 
@@ -66,7 +67,7 @@ class AcceptArgs(C.Structure):
         ("target_logits", C.c_void_p), ("draft_logits", C.c_void_p),
         ("draft_tokens", C.c_void_p), ("seed", C.c_uint64), ("step", C.c_uint32),
         ("accepted_len", C.c_void_p), ("next_token", C.c_void_p),
-        ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
+        ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t), ("gammas", C.c_void_p),
     ]
 
 

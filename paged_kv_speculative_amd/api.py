@@ -186,24 +186,24 @@ class Pool:
 
     # -- verification over this pool --------------------------------------------
     def prepare_verify(self, q, n_q, slots=None, anc_mask=None, sm_scale=None, buffers=None,
-                       num_splits=0):
+                       num_splits=0, n_q_seq=None):
         return PreparedVerify(q, self.k_pages, self.v_pages, self.block_table, self.seq_lens,
                               n_q=n_q, num_kv_heads=self.num_kv_heads, kv_dtype=self.kv_dtype,
                               k_scale=self.k_scale, v_scale=self.v_scale, batch_slots=slots,
                               anc_mask=anc_mask, sm_scale=sm_scale, buffers=buffers,
-                              num_splits=num_splits)
+                              num_splits=num_splits, n_q_seq=n_q_seq)
 
     def verify(self, q, n_q, slots=None, anc_mask=None, sm_scale=None, buffers=None, num_splits=0,
-               stream=None):
+               n_q_seq=None, stream=None):
         return spec_verify_attention(
             q, self.k_pages, self.v_pages, self.block_table, self.seq_lens, n_q=n_q,
             num_kv_heads=self.num_kv_heads, kv_dtype=self.kv_dtype, k_scale=self.k_scale,
             v_scale=self.v_scale, batch_slots=slots, anc_mask=anc_mask, sm_scale=sm_scale,
-            buffers=buffers, num_splits=num_splits, stream=stream)
+            buffers=buffers, num_splits=num_splits, n_q_seq=n_q_seq, stream=stream)
 
 
 def _verify_args(q, k_pages, v_pages, block_table, seq_lens, n_q, num_kv_heads, kv_dtype, k_scale,
-                 v_scale, batch_slots, anc_mask, sm_scale, num_splits):
+                 v_scale, batch_slots, anc_mask, sm_scale, num_splits, n_q_seq=None):
     B, nq, Hq, d = q.shape
     assert nq == n_q and q.is_contiguous()
     a = VerifyArgs()
@@ -226,6 +226,9 @@ def _verify_args(q, k_pages, v_pages, block_table, seq_lens, n_q, num_kv_heads, 
         a.anc_mask = anc_mask.data_ptr()
     a.sm_scale = float(np.float32(1.0 / np.sqrt(d)) if sm_scale is None else sm_scale)
     a.num_splits = num_splits
+    if n_q_seq is not None:
+        assert n_q_seq.dtype == torch.int32 and n_q_seq.numel() == B and n_q_seq.is_contiguous()
+        a.n_q_seq = n_q_seq.data_ptr()
     return a
 
 
@@ -246,9 +249,9 @@ class VerifyBuffers:
 
 def spec_verify_attention(q, k_pages, v_pages, block_table, seq_lens, *, n_q, num_kv_heads,
                           kv_dtype, k_scale=None, v_scale=None, batch_slots=None, anc_mask=None,
-                          sm_scale=None, buffers=None, num_splits=0, stream=None):
+                          sm_scale=None, buffers=None, num_splits=0, n_q_seq=None, stream=None):
     a = _verify_args(q, k_pages, v_pages, block_table, seq_lens, n_q, num_kv_heads, kv_dtype,
-                     k_scale, v_scale, batch_slots, anc_mask, sm_scale, num_splits)
+                     k_scale, v_scale, batch_slots, anc_mask, sm_scale, num_splits, n_q_seq)
     ws = verify_workspace_size(a)
     if buffers is None:
         B, _, Hq, d = q.shape
@@ -268,9 +271,9 @@ class PreparedVerify:
 
     def __init__(self, q, k_pages, v_pages, block_table, seq_lens, *, n_q, num_kv_heads, kv_dtype,
                  k_scale=None, v_scale=None, batch_slots=None, anc_mask=None, sm_scale=None,
-                 buffers=None, num_splits=0):
+                 buffers=None, num_splits=0, n_q_seq=None):
         a = _verify_args(q, k_pages, v_pages, block_table, seq_lens, n_q, num_kv_heads, kv_dtype,
-                         k_scale, v_scale, batch_slots, anc_mask, sm_scale, num_splits)
+                         k_scale, v_scale, batch_slots, anc_mask, sm_scale, num_splits, n_q_seq)
         ws = verify_workspace_size(a)
         if buffers is None:
             B, _, Hq, d = q.shape
@@ -280,14 +283,14 @@ class PreparedVerify:
         a.workspace, a.workspace_bytes = buffers.workspace.data_ptr(), buffers.workspace.numel()
         self.args, self.buffers = a, buffers
         self._keep = (q, k_pages, v_pages, block_table, seq_lens, k_scale, v_scale, batch_slots,
-                      anc_mask)
+                      anc_mask, n_q_seq)
 
     def __call__(self, stream=None):
         check(lib.spec_verify_attention(C.byref(self.args), _stream(stream)))
         return self.buffers.out, self.buffers.lse
 
 
-def _accept_args(target_logits, draft_logits, draft_tokens, seed, step):
+def _accept_args(target_logits, draft_logits, draft_tokens, seed, step, gammas=None):
     B, g1, V = target_logits.shape
     assert draft_logits.shape == (B, g1 - 1, V) and draft_tokens.shape == (B, g1 - 1)
     assert target_logits.dtype == torch.float32 and draft_logits.dtype == torch.float32
@@ -298,6 +301,9 @@ def _accept_args(target_logits, draft_logits, draft_tokens, seed, step):
     a.target_logits, a.draft_logits = target_logits.data_ptr(), draft_logits.data_ptr()
     a.draft_tokens = draft_tokens.data_ptr()
     a.seed, a.step = int(seed) & 0xFFFFFFFFFFFFFFFF, int(step) & 0xFFFFFFFF
+    if gammas is not None:
+        assert gammas.dtype == torch.int32 and gammas.numel() == B and gammas.is_contiguous()
+        a.gammas = gammas.data_ptr()
     return a
 
 
@@ -314,8 +320,9 @@ class AcceptBuffers:
         self.workspace = torch.empty(max(1, workspace_bytes), dtype=torch.uint8, device=device)
 
 
-def spec_accept(target_logits, draft_logits, draft_tokens, seed, step, buffers=None, stream=None):
-    a = _accept_args(target_logits, draft_logits, draft_tokens, seed, step)
+def spec_accept(target_logits, draft_logits, draft_tokens, seed, step, buffers=None, gammas=None,
+                stream=None):
+    a = _accept_args(target_logits, draft_logits, draft_tokens, seed, step, gammas)
     ws = accept_workspace_size(a)
     if buffers is None:
         buffers = AcceptBuffers(a.batch, ws, target_logits.device)
@@ -330,8 +337,8 @@ class PreparedAccept:
     step counter (and optionally a new seed) and reads the logits and draft
     tokens in place.  Returns (accepted_len, next_token) buffers it owns."""
 
-    def __init__(self, target_logits, draft_logits, draft_tokens, seed, buffers=None):
-        a = _accept_args(target_logits, draft_logits, draft_tokens, seed, 0)
+    def __init__(self, target_logits, draft_logits, draft_tokens, seed, buffers=None, gammas=None):
+        a = _accept_args(target_logits, draft_logits, draft_tokens, seed, 0, gammas)
         ws = accept_workspace_size(a)
         if buffers is None:
             buffers = AcceptBuffers(a.batch, ws, target_logits.device)
@@ -339,7 +346,7 @@ class PreparedAccept:
         a.accepted_len, a.next_token = buffers.accepted_len.data_ptr(), buffers.next_token.data_ptr()
         a.workspace, a.workspace_bytes = buffers.workspace.data_ptr(), buffers.workspace.numel()
         self.args, self.buffers = a, buffers
-        self._keep = (target_logits, draft_logits, draft_tokens)
+        self._keep = (target_logits, draft_logits, draft_tokens, gammas)
 
     def __call__(self, step, seed=None, stream=None):
         self.args.step = int(step) & 0xFFFFFFFF

@@ -49,6 +49,7 @@ struct AcceptParams {
   const float* T;
   const float* Dl;
   const int* tokens;
+  const int* gammas;   // [batch] drafts per sequence, or null (gamma for all)
   int* accepted_len;
   int* next_token;
   float2* stats;       // [batch][2*gamma+1][schunks] (max, sum exp) in base 2
@@ -67,7 +68,12 @@ __global__ __launch_bounds__(kThreads) void accept_stats_kernel(AcceptParams P) 
   const int chunk = blockIdx.x % P.schunks;
   const int r = blockIdx.x / P.schunks;  // b * (2 gamma + 1) + j
   const int rows_per_seq = 2 * P.gamma + 1;
-  const float* row = row_ptr(P, r / rows_per_seq, r % rows_per_seq);
+  const int b = r / rows_per_seq, j = r % rows_per_seq;
+  if (P.gammas) {                                // rows past the sequence's drafts are never used
+    const int gb = min(max(P.gammas[b], 1), P.gamma);
+    if (j <= P.gamma ? j > gb : j - P.gamma - 1 >= gb) return;
+  }
+  const float* row = row_ptr(P, b, j);
   float v[kStatsQuads][4];
   load_chunk<kAligned, kStatsQuads, true>(row, P.vocab, chunk * (kStatsChunk / 4), v);
   float m = kNegInf;
@@ -134,6 +140,7 @@ __global__ __launch_bounds__(kThreads) void accept_draw_kernel(AcceptParams P) {
   __shared__ float sk[2][kWaves];
   __shared__ int si[2][kWaves];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int gb = P.gammas ? min(max(P.gammas[b], 1), P.gamma) : P.gamma;
   // wave 0, lane i < gamma: the logits of draft token x_i (independent of the
   // normalisers, so issued first)
   int x = -1;
@@ -191,13 +198,14 @@ __global__ __launch_bounds__(kThreads) void accept_draw_kernel(AcceptParams P) {
         reject = !(uniform01(r.x[0]) < acc);
       }
     }
-    const unsigned long long rej = __ballot(reject);
+    // a sequence with fewer drafts stops at its count
+    const unsigned long long rej = __ballot(reject || (t >= gb && t < P.gamma));
     if (t == 0) s_k = rej ? __builtin_ctzll(rej) : P.gamma;
   }
   __syncthreads();
   const int k = s_k;
   if (chunk == 0 && t == 0) P.accepted_len[b] = k;
-  const bool residual = k < P.gamma;
+  const bool residual = k < gb;
   const float lt = s_lse[k], ld = residual ? s_lse[P.gamma + 1 + k] : 0.0f;
   const int q0 = chunk * (kDrawChunk / 4);
   float tv[kDrawQuads][4], dv[kDrawQuads][4];
@@ -312,6 +320,7 @@ extern "C" pkv_status spec_accept(const pkv_accept_args* a, void* stream) {
   p.T = a->target_logits;
   p.Dl = a->draft_logits;
   p.tokens = a->draft_tokens;
+  p.gammas = a->gammas;
   p.accepted_len = a->accepted_len;
   p.next_token = a->next_token;
   char* ws = static_cast<char*>(a->workspace);

@@ -75,6 +75,7 @@ struct VerifyParams {
   const int* seq_lens;
   const int* batch_slots;
   const unsigned long long* anc;
+  const int* nq_seq;     // [batch] verification slots per sequence, or null (n_q for all)
   float* out;
   float* lse;
   float* part;           // [n_wg][2][slot_floats] partial (O, max, sum) of split units
@@ -218,6 +219,11 @@ struct PageMeta {
   float ks, vs;          // FP8 scales of the page (per lane, all lanes alike)
 };
 
+// A ring slot's length word: the sequence's length N in bits 0..23 and its
+// number of verification slots in bits 24..30 (0 for a slot past the range).
+constexpr int kNqShift = 24;
+constexpr int kLenMask = (1 << kNqShift) - 1;
+
 // Values every lane of the wave holds alike (read from LDS or computed from
 // such reads): moved to scalar registers so addresses built from them stay
 // scalar.
@@ -319,12 +325,16 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
   const long page_stride = long(P.Hkv) * P.slab_bytes;
   const i32x4 len_rsrc = scalar_rsrc(P.seq_lens, 0xFFFFFFFFu);
   const i32x4 slot_rsrc = scalar_rsrc(P.batch_slots, P.batch_slots ? unsigned(P.batch) * 4u : 0u);
+  // without per-sequence counts the buffer has no records and reads return 0
+  const i32x4 nq_rsrc = scalar_rsrc(P.nq_seq, P.nq_seq ? unsigned(P.batch) * 4u : 0u);
 
   // ---- cursor helpers (all scalar) -----------------------------------------
   auto seq_info = [&](Cursor& c) {
     c.np = uni(s_cum[c.b + 1]) - uni(s_cum[c.b]);
     c.row = P.batch_slots ? s_buffer_load_dword(slot_rsrc, c.b * 4, 0) : c.b;
-    c.n = s_buffer_load_dword(len_rsrc, c.row * 4, 0);
+    const int nq = s_buffer_load_dword(nq_rsrc, c.b * 4, 0);
+    c.n = s_buffer_load_dword(len_rsrc, c.row * 4, 0) |
+          ((nq > 0 ? min(nq, P.n_q) : P.n_q) << kNqShift);
   };
   auto locate = [&](int pos) {
     int a = 0, z = P.batch - 1;
@@ -466,7 +476,7 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
   };
   float m_run[NT], l_run[NT];
   f32x4 acc[DT][NT];
-  int u_b = -1, u_g = 0, u_first = 0, u_last = 0, u_np = 0, u_n = 0, units_done = 0;
+  int u_b = -1, u_g = 0, u_first = 0, u_last = 0, u_np = 0, u_nq = 0, units_done = 0;
 
   auto finalize = [&]() {
     const bool full = u_first == 0 && u_last == u_np - 1;
@@ -478,7 +488,7 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
       l += __shfl_xor(l, 16, 64);
       l += __shfl_xor(l, 32, 64);
       const int rl = nt * 16 + m16, r = row0 + rl;
-      if (local_ok(nt)) {
+      if (local_ok(nt) && r / P.G < u_nq) {       // rows of slots past the sequence's count: not written
         const float inv = full ? 1.0f / l : 1.0f;
         const int i = r / P.G, h = u_g * P.G + r % P.G;
         const long oi = long(u_b * P.n_q + i) * P.Hq + h;
@@ -524,7 +534,7 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
   constexpr bool kSplitP = !FP8;
   auto compute_page = [&](Regs& R, const PageMeta& M) {
     const int tok0 = M.page * 16;
-    const int L = M.n - P.n_q;
+    const int L = (M.n & kLenMask) - (M.n >> kNqShift);
     // scores S^T (lane: row 16nt+m16, tokens tok0 + 4jg .. +3)
     f32x4 sc[NT];
 #pragma unroll
@@ -556,7 +566,7 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
       for (int e = 0; e < 4; ++e) sc[nt][e] *= ksc;
 
     if (tok0 + 16 > L) {                         // page reaches the verification slots or the end
-      const int N = M.n;
+      const int N = M.n & kLenMask;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = tok0 + 4 * jg + e;
@@ -689,7 +699,7 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
       const int i = i0 + r;
       prefetch(ring[(r + PF) % RS], meta[(r + PF) % RS], i + PF);
       const PageMeta& M = meta[r];
-      if (M.n > 0) {
+      if (M.n != 0) {
         const int mb = M.unit >> 16, mg = M.unit & 0xFFFF;
         if (mb != u_b || mg != u_g) {            // a new unit starts at this position
           if (u_b >= 0) finalize();
@@ -710,8 +720,8 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
           u_b = mb;
           u_g = mg;
           u_first = M.page;
-          u_np = (M.n + 15) >> 4;
-          u_n = M.n;
+          u_np = ((M.n & kLenMask) + 15) >> 4;
+          u_nq = M.n >> kNqShift;
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
             m_run[nt] = kNegInf;
@@ -750,6 +760,8 @@ __global__ __launch_bounds__(kThreads) void verify_merge_kernel(VerifyParams P) 
   const int x = blockIdx.y * kThreads + threadIdx.x;
   if (x >= R * (D / 4)) return;
   const int r = x / (D / 4), c4 = x % (D / 4);
+  const int nq_b = P.nq_seq ? min(max(P.nq_seq[b], 1), P.n_q) : P.n_q;
+  if (r / P.G >= nq_b) return;
   // row r is row rl of row group rgi, held by wave (range * rg + rgi)
   const int rgi = r / P.rows_w, rl = r % P.rows_w, RW = P.rows_w;
   const long sf = slot_floats(RW, D);
@@ -843,13 +855,14 @@ __global__ __launch_bounds__(128) void verify_f32_kernel(VerifyParams P) {
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int g = h / P.G;
   const int row_b = P.batch_slots ? P.batch_slots[b] : b;
-  const int N = P.seq_lens[row_b], L = N - P.n_q;
+  const int nq_b = P.nq_seq ? min(max(P.nq_seq[b], 1), P.n_q) : P.n_q;
+  const int N = P.seq_lens[row_b], L = N - nq_b;
   const int* bt = P.block_table + long(row_b) * P.bt_stride;
   __shared__ float s_q[D];
   __shared__ float s_p[128];
   __shared__ float s_red[2];
   const float scale = P.scale_log2;
-  for (int i = 0; i < P.n_q; ++i) {
+  for (int i = 0; i < nq_b; ++i) {
     const long oi = long(b * P.n_q + i) * P.Hq + h;
     __syncthreads();
     for (int c = tid; c < D; c += 128) s_q[c] = static_cast<const float*>(P.q)[oi * D + c];
@@ -1146,6 +1159,7 @@ extern "C" pkv_status spec_verify_attention(const pkv_verify_args* a, void* stre
   p.seq_lens = a->seq_lens;
   p.batch_slots = a->batch_slots;
   p.anc = reinterpret_cast<const unsigned long long*>(a->anc_mask);
+  p.nq_seq = a->n_q_seq;
   p.out = a->out;
   p.lse = a->lse;
   p.cum = static_cast<int*>(a->workspace);
