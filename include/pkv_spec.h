@@ -307,6 +307,9 @@ typedef struct {
                                  overlap in time                                 */
   size_t workspace_bytes;
   const int32_t* gammas;      /* device [batch] drafts per sequence, or NULL     */
+  const uint32_t* step_ptr;   /* device: when not NULL the step counter is read
+                                 from here when the kernels run (a captured HIP
+                                 graph can then be replayed with a new step)     */
 } pkv_accept_args;
 
 pkv_status spec_accept_workspace_size(const pkv_accept_args* args, size_t* bytes_out);
@@ -355,6 +358,7 @@ typedef struct {
                                  16-byte aligned; calls sharing it must not
                                  overlap in time                                 */
   size_t workspace_bytes;
+  const uint32_t* step_ptr;   /* device step counter read at run time, or NULL   */
 } pkv_tree_accept_args;
 
 pkv_status spec_accept_tree_workspace_size(const pkv_tree_accept_args* args, size_t* bytes_out);

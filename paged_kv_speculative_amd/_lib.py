@@ -68,6 +68,7 @@ class AcceptArgs(C.Structure):
         ("draft_tokens", C.c_void_p), ("seed", C.c_uint64), ("step", C.c_uint32),
         ("accepted_len", C.c_void_p), ("next_token", C.c_void_p),
         ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t), ("gammas", C.c_void_p),
+        ("step_ptr", C.c_void_p),
     ]
 
 
@@ -77,7 +78,7 @@ class TreeAcceptArgs(C.Structure):
         ("vocab", C.c_int32), ("target_logits", C.c_void_p), ("draft_logits", C.c_void_p),
         ("parents", C.c_void_p), ("tokens", C.c_void_p), ("seed", C.c_uint64), ("step", C.c_uint32),
         ("accepted_len", C.c_void_p), ("accepted_nodes", C.c_void_p), ("next_token", C.c_void_p),
-        ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
+        ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t), ("step_ptr", C.c_void_p),
     ]
 
 

@@ -335,10 +335,16 @@ def spec_accept(target_logits, draft_logits, draft_tokens, seed, step, buffers=N
 class PreparedAccept:
     """spec_accept with its arguments marshalled once; each call takes the
     step counter (and optionally a new seed) and reads the logits and draft
-    tokens in place.  Returns (accepted_len, next_token) buffers it owns."""
+    tokens in place.  Returns (accepted_len, next_token) buffers it owns.
+    With step_tensor (a device uint32/int32 scalar tensor) the kernels read the
+    step from it when they run, so the launch can be captured in a graph."""
 
-    def __init__(self, target_logits, draft_logits, draft_tokens, seed, buffers=None, gammas=None):
+    def __init__(self, target_logits, draft_logits, draft_tokens, seed, buffers=None, gammas=None,
+                 step_tensor=None):
         a = _accept_args(target_logits, draft_logits, draft_tokens, seed, 0, gammas)
+        if step_tensor is not None:
+            assert step_tensor.numel() == 1 and step_tensor.element_size() == 4
+            a.step_ptr = step_tensor.data_ptr()
         ws = accept_workspace_size(a)
         if buffers is None:
             buffers = AcceptBuffers(a.batch, ws, target_logits.device)
@@ -346,7 +352,7 @@ class PreparedAccept:
         a.accepted_len, a.next_token = buffers.accepted_len.data_ptr(), buffers.next_token.data_ptr()
         a.workspace, a.workspace_bytes = buffers.workspace.data_ptr(), buffers.workspace.numel()
         self.args, self.buffers = a, buffers
-        self._keep = (target_logits, draft_logits, draft_tokens, gammas)
+        self._keep = (target_logits, draft_logits, draft_tokens, gammas, step_tensor)
 
     def __call__(self, step, seed=None, stream=None):
         self.args.step = int(step) & 0xFFFFFFFF

@@ -50,6 +50,7 @@ struct AcceptParams {
   const float* Dl;
   const int* tokens;
   const int* gammas;   // [batch] drafts per sequence, or null (gamma for all)
+  const unsigned* step_ptr;  // device step counter, or null (step below)
   int* accepted_len;
   int* next_token;
   float2* stats;       // [batch][2*gamma+1][schunks] (max, sum exp) in base 2
@@ -108,12 +109,13 @@ __global__ __launch_bounds__(kThreads) void accept_stats_kernel(AcceptParams P) 
 // log2 max(0, P_k - Q_k)(x) + g(x).  Branch-free per logit.
 template <bool kResidual>
 __device__ inline void draw_quads(const float (&tv)[kDrawQuads][4], const float (&dv)[kDrawQuads][4],
-                                  int q0, int b, unsigned c3, float lt, float ld, const AcceptParams& P,
+                                  int q0, int b, unsigned step, unsigned c3, float lt, float ld,
+                                  const AcceptParams& P,
                                   float& rk, int& ri, float& fk, int& fi) {
 #pragma unroll
   for (int u = 0; u < kDrawQuads; ++u) {
     const int q = q0 + u * kThreads + int(threadIdx.x);
-    const Philox4 r = philox4x32_10(unsigned(q), unsigned(b), P.step, c3, P.k0, P.k1);
+    const Philox4 r = philox4x32_10(unsigned(q), unsigned(b), step, c3, P.k0, P.k1);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int x = q * 4 + e;
@@ -132,6 +134,7 @@ __device__ inline void draw_quads(const float (&tv)[kDrawQuads][4], const float 
 
 template <bool kAligned>
 __global__ __launch_bounds__(kThreads) void accept_draw_kernel(AcceptParams P) {
+  const unsigned step = P.step_ptr ? *P.step_ptr : P.step;
   const int chunk = blockIdx.x % P.dchunks;
   const int b = blockIdx.x / P.dchunks;
   const int rows_per_seq = 2 * P.gamma + 1;
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void accept_draw_kernel(AcceptParams P) {
         const float lq = dx * kLog2e - s_lse[P.gamma + 1 + t];
         const float d = lp - lq;
         const float acc = d >= 0.0f ? 1.0f : exp2_hw(d);
-        const Philox4 r = philox4x32_10(0u, unsigned(b), P.step, unsigned(t) | (kPurposeAccept << 16),
+        const Philox4 r = philox4x32_10(0u, unsigned(b), step, unsigned(t) | (kPurposeAccept << 16),
                                         P.k0, P.k1);
         reject = !(uniform01(r.x[0]) < acc);
       }
@@ -215,9 +218,9 @@ __global__ __launch_bounds__(kThreads) void accept_draw_kernel(AcceptParams P) {
   load_chunk<kAligned, kDrawQuads>(row_ptr(P, b, k), P.vocab, q0, tv);
   if (residual) {
     load_chunk<kAligned, kDrawQuads>(row_ptr(P, b, P.gamma + 1 + k), P.vocab, q0, dv);
-    draw_quads<true>(tv, dv, q0, b, c3, lt, ld, P, rk, ri, fk, fi);
+    draw_quads<true>(tv, dv, q0, b, step, c3, lt, ld, P, rk, ri, fk, fi);
   } else {
-    draw_quads<false>(tv, dv, q0, b, c3, lt, ld, P, rk, ri, fk, fi);
+    draw_quads<false>(tv, dv, q0, b, step, c3, lt, ld, P, rk, ri, fk, fi);
   }
   for (int o = 32; o > 0; o >>= 1) {
     better(rk, ri, __shfl_xor(rk, o, 64), __shfl_xor(ri, o, 64));
@@ -321,6 +324,7 @@ extern "C" pkv_status spec_accept(const pkv_accept_args* a, void* stream) {
   p.Dl = a->draft_logits;
   p.tokens = a->draft_tokens;
   p.gammas = a->gammas;
+  p.step_ptr = a->step_ptr;
   p.accepted_len = a->accepted_len;
   p.next_token = a->next_token;
   char* ws = static_cast<char*>(a->workspace);

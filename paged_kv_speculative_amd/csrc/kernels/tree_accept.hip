@@ -71,6 +71,7 @@ struct TreeParams {
   float* decision_f;   // [batch][64 + 2]: the stopping node's lse of T, D and log2 Z_1..Z_{m-1}
   int batch, n, levels, max_children, vocab, chunks, zchunks, dchunks;
   unsigned k0, k1, step;
+  const unsigned* step_ptr;  // device step counter, or null (step above)
 };
 
 __device__ inline const float* trow(const TreeParams& P, int b, int u) {
@@ -239,6 +240,7 @@ __global__ __launch_bounds__(kLevelThreads) void tree_level_kernel(TreeParams P,
 // by ballots to the stopping node.  Writes the accepted branch and, for the
 // draw, the stopping node, its child count and its normalisers.
 __global__ __launch_bounds__(kThreads) void tree_decide_kernel(TreeParams P) {
+  const unsigned step = P.step_ptr ? *P.step_ptr : P.step;
   const int b = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   __shared__ int s_par[kMaxNodes];
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void tree_decide_kernel(TreeParams P) {
       const float lp = advance_levels(__builtin_fmaf(trow(P, b, u)[x], kLog2e, -s_lt[u]), lq, s_lz[u], rank);
       const float d = lp - lq;
       const float a = d >= 0.0f ? 1.0f : exp2_hw(d);
-      const Philox4 r = philox4x32_10(0u, unsigned(b), P.step, unsigned(lane - 1) | (kPurposeAccept << 16),
+      const Philox4 r = philox4x32_10(0u, unsigned(b), step, unsigned(lane - 1) | (kPurposeAccept << 16),
                                       P.k0, P.k1);
       acc = uniform01(r.x[0]) < a;
     }
@@ -336,6 +338,7 @@ __global__ __launch_bounds__(kThreads) void tree_decide_kernel(TreeParams P) {
 // target at a leaf (the bonus).
 template <bool kAligned>
 __global__ __launch_bounds__(kThreads) void tree_draw_kernel(TreeParams P) {
+  const unsigned step = P.step_ptr ? *P.step_ptr : P.step;
   const int chunk = blockIdx.x % P.dchunks;
   const int b = blockIdx.x / P.dchunks;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -358,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void tree_draw_kernel(TreeParams P) {
 #pragma unroll
     for (int qq = 0; qq < kDrawQuads; ++qq) {
       const int q = q0 + qq * kThreads + t;
-      const Philox4 r = philox4x32_10(unsigned(q), unsigned(b), P.step, c3, P.k0, P.k1);
+      const Philox4 r = philox4x32_10(unsigned(q), unsigned(b), step, c3, P.k0, P.k1);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int x = q * 4 + e;
@@ -373,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void tree_draw_kernel(TreeParams P) {
 #pragma unroll
     for (int qq = 0; qq < kDrawQuads; ++qq) {
       const int q = q0 + qq * kThreads + t;
-      const Philox4 r = philox4x32_10(unsigned(q), unsigned(b), P.step, c3, P.k0, P.k1);
+      const Philox4 r = philox4x32_10(unsigned(q), unsigned(b), step, c3, P.k0, P.k1);
 #pragma unroll
       for (int e = 0; e < 4; ++e) better(fk, fi, tv[qq][e] * kLog2e + gumbel2(uniform01(r.x[e])), q * 4 + e);
     }
@@ -510,6 +513,7 @@ extern "C" pkv_status spec_accept_tree(const pkv_tree_accept_args* a, void* stre
   p.k0 = unsigned(a->seed & 0xFFFFFFFFu);
   p.k1 = unsigned(a->seed >> 32);
   p.step = a->step;
+  p.step_ptr = a->step_ptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool aligned = (a->vocab & 3) == 0;
   const unsigned rows = unsigned(a->batch) * a->n_nodes;
