@@ -19,6 +19,8 @@ here:
 The fp32 steps are done in numpy float32 so the integer codes are exactly the
 ones any IEEE-conforming fp32 implementation gets.
 """
+import math
+
 import numpy as np
 
 FP8_MAX = 448.0
@@ -87,3 +89,57 @@ def quantise(x, scale):
     inv = np.float32(np.float32(1.0) / np.float32(scale))
     y = (x * inv).astype(np.float32)
     return encode_rne_sat(y.astype(np.float64))
+
+
+# ----------------------------------------------------------------------------
+# Per-64-element tile scales
+# ----------------------------------------------------------------------------
+# The same page asks for FP8 block scales to be recomputed per 64-element tile
+# (atozofsoftwareengineering.blog, closing checklist, "Precision
+# Benchmarking").  Readings used here:
+#   * a tile is 64 consecutive channels of one token of one KV head (head_dim
+#     128 has two tiles per token), for K and for V separately; every token is
+#     quantised on its own when it is appended, so codes never depend on which
+#     other tokens share its page;
+#   * the scale is a power of two stored as an OCP E8M0 exponent byte
+#     (value 2^(e - 127)), as in the OCP microscaling formats: s = 2^k with k
+#     the smallest integer for which amax / 2^k <= 448 (k = 0 when amax = 0),
+#     k clamped to [-127, 127];
+#   * code: y = x * 2^-k (exact in fp32), then the E4M3 encoder above.
+# Power-of-two scales make decode(code) * s exact in bf16 as well as fp32.
+
+def tile_exponent(amax):
+    """k of the tile scale 2^k for a tile whose largest magnitude is amax."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 0
+    m, E = math.frexp(amax)               # amax = m * 2^E, m in [0.5, 1)
+    k = E - 9 + (1 if m > 0.875 else 0)   # 448 = 0.875 * 2^9
+    return max(-127, min(127, k))
+
+
+def quantise_tiles(x):
+    """x [..., D] fp32 with D a multiple of 64 -> (codes [..., D] uint8,
+    E8M0 exponent bytes [..., D/64] uint8)."""
+    x = np.asarray(x, dtype=np.float32)
+    shp = x.shape
+    D = shp[-1]
+    tiles = x.reshape(-1, D // 64, 64)
+    codes = np.empty(tiles.shape, dtype=np.uint8)
+    exps = np.empty(tiles.shape[:2], dtype=np.uint8)
+    for i in range(tiles.shape[0]):
+        for g in range(tiles.shape[1]):
+            t = tiles[i, g]
+            k = tile_exponent(np.max(np.abs(t)))
+            exps[i, g] = k + 127
+            y = (t * np.float32(2.0 ** -k)).astype(np.float32)
+            codes[i, g] = encode_rne_sat(y.astype(np.float64))
+    return codes.reshape(shp), exps.reshape(shp[:-1] + (D // 64,))
+
+
+def dequantise_tiles(codes, exps):
+    """Inverse of quantise_tiles (fp64): decode(code) * 2^(e - 127)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    D = codes.shape[-1]
+    s = np.ldexp(1.0, np.asarray(exps, dtype=np.int64) - 127)
+    return (decode(codes).reshape(codes.shape[:-1] + (D // 64, 64)) * s[..., None]).reshape(codes.shape)

@@ -24,7 +24,9 @@ Readings where the pages are silent or disagree:
     partly valid last shared page is CoW-copied on the first append;
   * rollback by n truncates the length; pages wholly past the new length lose
     a reference (freed at zero); no data moves;
-  * FP8 pools quantise on append (see oracle.fp8 for the scale rule).
+  * FP8 pools quantise on append (see oracle.fp8 for the scale rule); the
+    "fp8mx" pools quantise every token on its own with a power-of-two scale
+    per 64 channels (oracle.fp8, per-64-element tile scales).
 
 The model stores page contents in a plain [page][head][slot][dim] array (its
 own layout), so gathering a sequence back to contiguous K/V is a loop over the
@@ -50,6 +52,7 @@ class PoolModel:
                  free_order=None):
         self.P, self.S, self.H, self.d = num_pages, page_size, num_kv_heads, head_dim
         self.fp8 = kv_dtype == "fp8"
+        self.mx = kv_dtype == "fp8mx"
         if free_order is None:
             free_order = np.arange(num_pages)
         free_order = [int(p) for p in free_order]
@@ -67,6 +70,11 @@ class PoolModel:
             self.vc = np.zeros_like(self.kc)
             self.ks = np.ones((num_pages, self.H), dtype=np.float32)
             self.vs = np.ones((num_pages, self.H), dtype=np.float32)
+        elif self.mx:
+            self.kc = np.zeros((num_pages, self.H, self.S, self.d), dtype=np.uint8)
+            self.vc = np.zeros_like(self.kc)
+            self.kx = np.full((num_pages, self.H, self.S, self.d // 64), 127, dtype=np.uint8)
+            self.vx = np.full_like(self.kx, 127)
         else:
             self.k = np.full((num_pages, self.H, self.S, self.d), np.nan)
             self.v = np.full((num_pages, self.H, self.S, self.d), np.nan)
@@ -142,7 +150,13 @@ class PoolModel:
             t1 = min(L + n, (blk + 1) * self.S)
             slots = np.arange(t0, t1) - blk * self.S
             src = slice(t0 - L, t1 - L)
-            if self.fp8:
+            if self.mx:
+                kq, ke = fp8.quantise_tiles(np.asarray(k_new[src], dtype=np.float32))
+                vq, ve = fp8.quantise_tiles(np.asarray(v_new[src], dtype=np.float32))
+                for h in range(self.H):
+                    self.kc[p, h, slots], self.kx[p, h, slots] = kq[:, h], ke[:, h]
+                    self.vc[p, h, slots], self.vx[p, h, slots] = vq[:, h], ve[:, h]
+            elif self.fp8:
                 kx = np.asarray(k_new[src], dtype=np.float32)
                 vx = np.asarray(v_new[src], dtype=np.float32)
                 for h in range(self.H):
@@ -158,7 +172,10 @@ class PoolModel:
         self.lens[seq] = L + n
 
     def _copy_page(self, src, dst):
-        if self.fp8:
+        if self.mx:
+            for a in (self.kc, self.vc, self.kx, self.vx):
+                a[dst] = a[src]
+        elif self.fp8:
             self.kc[dst] = self.kc[src]
             self.vc[dst] = self.vc[src]
             self.ks[dst] = self.ks[src]
@@ -210,7 +227,11 @@ class PoolModel:
             pd, od = table[dst // self.S], dst % self.S
             if self.refcount[pd] > 1:
                 raise ValueError("destination page is shared")
-            if self.fp8:
+            if self.mx:
+                # each token carries its own scales: codes and scales move as they are
+                for a in (self.kc, self.vc, self.kx, self.vx):
+                    a[pd, :, od] = a[ps, :, os_]
+            elif self.fp8:
                 for h in range(self.H):
                     for codes, sc in ((self.kc, self.ks), (self.vc, self.vs)):
                         if np.float32(sc[ps, h]).view(np.uint32) == np.float32(sc[pd, h]).view(np.uint32):
@@ -240,7 +261,10 @@ class PoolModel:
         V = np.empty((L, self.H, self.d))
         for t in range(L):
             p, o = table[t // self.S], t % self.S
-            if self.fp8:
+            if self.mx:
+                K[t] = fp8.dequantise_tiles(self.kc[p, :, o], self.kx[p, :, o])
+                V[t] = fp8.dequantise_tiles(self.vc[p, :, o], self.vx[p, :, o])
+            elif self.fp8:
                 K[t] = fp8.decode(self.kc[p, :, o]) * self.ks[p][:, None].astype(np.float64)
                 V[t] = fp8.decode(self.vc[p, :, o]) * self.vs[p][:, None].astype(np.float64)
             else:
