@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--instances", type=int, default=0, help="pool copies used round-robin (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--kv-dtype", choices=["bf16", "fp8", "fp8mx"], default=None,
+                    help="override the workload's KV type (fp8mx: FP8 with a power-of-two scale per "
+                         "64 channels of each token)")
     ap.add_argument("--graph", action="store_true",
                     help="replay verification and acceptance from HIP graphs (measured slower than "
                          "eager launches on MI355X: 177 vs 168 us per step)")
@@ -96,12 +99,14 @@ def kv_bytes(lens, w):
     """Algorithmic KV bytes of one verification call: every K and V element of
     every token of every sequence once (the shared prefix counted once), plus
     the FP8 scales of the pages read."""
-    elem = {"bf16": 2, "f32": 4, "fp8": 1}[w.kv_dtype]
+    elem = {"bf16": 2, "f32": 4, "fp8": 1, "fp8mx": 1}[w.kv_dtype]
     per_tok = w.num_kv_heads * 2 * w.head_dim * elem
     toks = int(np.sum(lens)) - (len(lens) - 1) * w.prefix_len if w.prefix_len else int(np.sum(lens))
     total = toks * per_tok
     if w.kv_dtype == "fp8":
         total += int(np.sum((np.asarray(lens) + 15) // 16)) * w.num_kv_heads * 2 * 4
+    if w.kv_dtype == "fp8mx":                       # one exponent byte per 64 channels of every token
+        total += toks * w.num_kv_heads * 2 * (w.head_dim // 64)
     return total
 
 
@@ -315,7 +320,7 @@ def cpu_baseline(w, budget_s):
             t0 = time.perf_counter()
             n = int(w.seq_lens[b])
             pm = opool.PoolModel(-(-n // 16) + 2, 16, w.num_kv_heads, w.head_dim,
-                                 kv_dtype="fp8" if w.kv_dtype == "fp8" else "f64")
+                                 kv_dtype=w.kv_dtype if w.kv_dtype in ("fp8", "fp8mx") else "f64")
             pm.alloc(0)
             k, v = w.seq_kv(b)
             ctx = int(w.cached_lens[b])
@@ -350,6 +355,8 @@ def main():
     import paged_kv_speculative_amd as api
     from paged_kv_speculative_amd import workloads
     w = workloads.make(args.config)
+    if args.kv_dtype:
+        w.kv_dtype = args.kv_dtype
     r = run_gpu(args, w, torch, api)
     B, nq = w.batch, w.n_q
     ms_step = 1e3 * r["wall_s"] / args.steps
@@ -368,7 +375,7 @@ def main():
         "scaling": "weak",
         "launch": "hip-graph (verification, acceptance)" if args.graph else "eager",
         "vs_baseline": None,
-        "dtype": "bf16" if w.kv_dtype != "fp8" else "fp8-kv/bf16",
+        "dtype": {"fp8": "fp8-kv/bf16", "fp8mx": "fp8-kv(mx64)/bf16"}.get(w.kv_dtype, "bf16"),
         "data": "synthetic",
         "config": {
             "workload": f"{workloads.CONFIG_NAMES[args.config]}: batch {B}, {w.num_q_heads} q / "

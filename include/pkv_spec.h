@@ -61,7 +61,14 @@ typedef enum {
   PKV_ERR_CAPACITY = 9       /* sequence longer than max_pages_per_seq pages     */
 } pkv_status;
 
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
+/* PKV_FP8_E4M3: OCP E4M3 codes with one fp32 scale per (page, KV head).
+ * PKV_FP8_E4M3_MX64: OCP E4M3 codes with a power-of-two scale per 64 channels
+ * of each token, stored as OCP E8M0 exponent bytes (value 2^(e - 127)); the
+ * per-64-element tile scales of atozofsoftwareengineering.blog's closing
+ * checklist ("Precision Benchmarking").  A token's codes depend on that token
+ * alone: s = 2^k, k the smallest integer with amax(tile)/2^k <= 448 (k = 0 for
+ * an all-zero tile), code = round-to-nearest-even(x * 2^-k), saturating. */
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2, PKV_FP8_E4M3_MX64 = 3 } pkv_dtype;
 
 /* ------------------------------------------------------------------------ */
 /* Page pool                                                                 */
@@ -80,7 +87,9 @@ typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
  *   K, V fp32: element (t, c) at t*head_dim + c (plain)
  * (t = slot in page, c = channel).  pkv_page_bytes() gives page_bytes.
  * FP8 is OCP E4M3 ("e4m3fn") with one fp32 scale per (page, KV head) for K
- * and one for V: value = decode(byte) * scale.
+ * and one for V: value = decode(byte) * scale.  FP8_E4M3_MX64 pages use the
+ * FP8 layouts above; their scales are bytes [num_pages][Hkv][16 tokens]
+ * [head_dim/64] for K and for V: value = decode(byte) * 2^(e - 127).
  */
 typedef struct pkv_pool pkv_pool;
 
@@ -94,8 +103,10 @@ typedef struct {
   int32_t max_pages_per_seq;  /* columns of the device block table               */
   void* k_pages;              /* device [num_pages][Hkv][page_bytes]             */
   void* v_pages;              /* device, same shape                              */
-  float* k_scale;             /* device [num_pages][Hkv], FP8 only, else NULL    */
-  float* v_scale;             /* device [num_pages][Hkv], FP8 only, else NULL    */
+  void* k_scale;              /* device: FP8 fp32 [num_pages][Hkv]; FP8_E4M3_MX64
+                                 uint8 [num_pages][Hkv][16][head_dim/64];
+                                 else NULL                                       */
+  void* v_scale;              /* device, same shape as k_scale                   */
   int32_t* block_table;       /* device [max_seqs][max_pages_per_seq]            */
   int32_t* seq_lens;          /* device [max_seqs]; 0 for free rows              */
   const int32_t* free_order;  /* host [num_pages]: a permutation giving each
@@ -135,7 +146,8 @@ pkv_status paged_kv_alloc(pkv_pool* pool, int64_t seq, int64_t share_from, int32
  * Allowed src_dtype: the pool dtype for F32/BF16 pools; PKV_F32 for FP8
  * pools, which quantise with the page's scale (a fresh page gets
  * scale = amax/448 of the tokens this call writes into it, per KV head; a page
- * that already holds tokens keeps its scale and values saturate to +-448).
+ * that already holds tokens keeps its scale and values saturate to +-448);
+ * PKV_F32 for FP8_E4M3_MX64 pools, which quantise every token on its own.
  * The scatter, the block-table entries and the new lengths are written on
  * `stream`; the sources must stay valid until the stream reaches the work. */
 pkv_status paged_kv_append(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
@@ -160,7 +172,8 @@ pkv_status paged_kv_rollback(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs
  * base + 1 + path_len[i] tokens as by paged_kv_rollback.  FP8 pools keep a
  * token's codes when source and destination (page, head) scales are equal bit
  * for bit, and otherwise decode with the source scale and encode with the
- * destination's (fp32, round to nearest even, saturating).  Requirements:
+ * destination's (fp32, round to nearest even, saturating); FP8_E4M3_MX64
+ * tokens move with their own scales.  Requirements:
  * 1 <= n_tree[i] <= min(64, len), path_len[i] <= n_tree[i] - 1, and every page
  * holding a destination position referenced by this sequence only (else
  * PKV_ERR_INVALID_ARG).  All-or-nothing over the call; the moves and the new
@@ -226,8 +239,8 @@ pkv_status spec_tree_ancestor_masks(int32_t n_nodes, const int32_t* parents, uin
  * result nor written).  This serves policies that pick gamma per sequence
  * (paurushmuley.com, dynamic lookahead; atozofsoftwareengineering.blog).
  *
- * Supported: q_dtype F32 with kv_dtype F32; q_dtype BF16 with kv_dtype BF16
- * or FP8_E4M3; head_dim 64 or 128; page_size 16; n_q*Hq/Hkv <= 64 rows per KV
+ * Supported: q_dtype F32 with kv_dtype F32; q_dtype BF16 with kv_dtype BF16,
+ * FP8_E4M3 or FP8_E4M3_MX64; head_dim 64 or 128; page_size 16; n_q*Hq/Hkv <= 64 rows per KV
  * head; n_q <= 64; 0 <= L and N < 2^24 for every sequence.  Long contexts are split over
  * workgroups and merged by log-sum-exp in a second kernel (workspace below).
  */
@@ -243,8 +256,8 @@ typedef struct {
   const void* q;              /* device [batch][n_q][Hq][head_dim]               */
   const void* k_pages;        /* device pool (layout above)                      */
   const void* v_pages;
-  const float* k_scale;       /* device [num_pages][Hkv], FP8 only               */
-  const float* v_scale;
+  const void* k_scale;        /* device, FP8 kinds only (layout at the pool)     */
+  const void* v_scale;
   const int32_t* block_table; /* device                                          */
   int32_t block_table_stride; /* int32 entries per block-table row               */
   const int32_t* seq_lens;    /* device, total length N incl. the n_q tokens     */

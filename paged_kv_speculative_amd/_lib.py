@@ -16,8 +16,8 @@ STATUS_NAMES = {
     4: "PKV_ERR_SEQ_EXISTS", 5: "PKV_ERR_UNSUPPORTED", 6: "PKV_ERR_DEVICE",
     7: "PKV_ERR_WORKSPACE", 8: "PKV_ERR_NO_SLOT", 9: "PKV_ERR_CAPACITY",
 }
-F32, BF16, FP8_E4M3 = 0, 1, 2
-DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
+F32, BF16, FP8_E4M3, FP8_E4M3_MX64 = 0, 1, 2, 3
+DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "fp8mx": FP8_E4M3_MX64}
 
 
 class PkvError(RuntimeError):

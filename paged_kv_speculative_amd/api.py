@@ -76,6 +76,11 @@ class Pool:
             if kv_dtype == "fp8":
                 self.k_scale = torch.ones((num_pages, num_kv_heads), dtype=torch.float32, device=device)
                 self.v_scale = torch.ones((num_pages, num_kv_heads), dtype=torch.float32, device=device)
+            elif kv_dtype == "fp8mx":
+                # E8M0 exponent bytes per (page, head, token, 64-channel tile); 127 = scale 1
+                shp = (num_pages, num_kv_heads, 16, head_dim // 64)
+                self.k_scale = torch.full(shp, 127, dtype=torch.uint8, device=device)
+                self.v_scale = torch.full(shp, 127, dtype=torch.uint8, device=device)
             self.block_table = torch.zeros((max_seqs, max_pages_per_seq), dtype=torch.int32, device=device)
             self.seq_lens = torch.zeros(max_seqs, dtype=torch.int32, device=device)
             desc.k_pages, desc.v_pages = self.k_pages.data_ptr(), self.v_pages.data_ptr()
@@ -100,7 +105,7 @@ class Pool:
         """Fill every page with NaN patterns so reads of unwritten slots show."""
         if self.k_pages is None:
             return
-        if self.kv_dtype == "fp8":
+        if self.kv_dtype in ("fp8", "fp8mx"):
             self.k_pages.fill_(0x7F)
             self.v_pages.fill_(0x7F)
         elif self.kv_dtype == "bf16":
@@ -123,7 +128,7 @@ class Pool:
         na, np_ = _ints(n_tokens, np.int32)
         assert sa.size == na.size
         # with nothing to write the source dtype only has to be a valid one
-        src_dtype, kp, vp = (F32 if self.kv_dtype == "fp8" else DTYPES[self.kv_dtype]), None, None
+        src_dtype, kp, vp = (F32 if self.kv_dtype in ("fp8", "fp8mx") else DTYPES[self.kv_dtype]), None, None
         if self.device is not None and int(na.sum()) > 0:
             assert k_src.is_contiguous() and v_src.is_contiguous() and k_src.dtype == v_src.dtype
             assert k_src.numel() >= int(na.sum()) * self.num_kv_heads * self.head_dim

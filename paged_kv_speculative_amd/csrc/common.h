@@ -56,8 +56,8 @@ static_assert(sizeof(PoolUpdateBatch) <= 4000, "kernel argument block too large"
 struct PoolDevice {
   void* k_pages;
   void* v_pages;
-  float* k_scale;
-  float* v_scale;
+  void* k_scale;         // FP8: fp32 [page][head]; MX64: E8M0 bytes [page][head][token][D/64]
+  void* v_scale;
   int32_t* block_table;
   int32_t* seq_lens;
   const void* k_src;

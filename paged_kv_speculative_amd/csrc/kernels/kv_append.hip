@@ -148,12 +148,12 @@ __device__ void write_fp8(const PoolDevice& dev, const PoolTask& t, int h, int H
     sk = ak == 0.0f ? 1.0f : ak / 448.0f;
     sv = av == 0.0f ? 1.0f : av / 448.0f;
     if ((threadIdx.x & 63) == 0) {
-      dev.k_scale[sidx] = sk;
-      dev.v_scale[sidx] = sv;
+      static_cast<float*>(dev.k_scale)[sidx] = sk;
+      static_cast<float*>(dev.v_scale)[sidx] = sv;
     }
   } else {
-    sk = dev.k_scale[sidx];
-    sv = dev.v_scale[sidx];
+    sk = static_cast<const float*>(dev.k_scale)[sidx];
+    sv = static_cast<const float*>(dev.v_scale)[sidx];
   }
   const float ik = 1.0f / sk, iv = 1.0f / sv;
   unsigned char* kslab = static_cast<unsigned char*>(dev.k_pages) + sidx * pb;
@@ -170,6 +170,72 @@ __device__ void write_fp8(const PoolDevice& dev, const PoolTask& t, int h, int H
     *reinterpret_cast<uint2*>(kslab + k_index_fp8(im[u].slot, im[u].c0, D)) = make_uint2(lo, hi);
 #pragma unroll
     for (int i = 0; i < 8; ++i) vslab[v_index_fp8(im[u].slot, im[u].c0 + i)] = quant_e4m3(vx[u][i], iv);
+  }
+}
+
+// E8M0 exponent byte of the tile scale 2^k for a tile whose largest magnitude
+// is amax: k the smallest integer with amax / 2^k <= 448 = 0.875 * 2^9
+// (amax = m * 2^E with m in [0.5, 1): k = E - 9, plus 1 when m > 0.875),
+// clamped to [-127, 127]; k = 0 for amax = 0.
+__device__ inline int tile_exponent_byte(float amax) {
+  const unsigned b = __float_as_uint(amax);
+  if (amax == 0.0f) return 127;
+  const int e = int(b >> 23) & 0xFF;
+  if (e == 0) return 0;                          // subnormal amax: k = -127
+  const int k = (e - 126) - 9 + ((b & 0x7FFFFF) > 0x600000u ? 1 : 0);
+  return min(max(k, -127), 127) + 127;
+}
+
+// FP8 pool with per-64-channel scales, fp32 source: every token is quantised
+// on its own.  A lane holds 8 channels of one token; the 8 lanes of a
+// 64-channel tile (consecutive items, 8-aligned) reduce its amax by
+// shuffles, and the tile's first lane writes the exponent byte.
+__device__ void write_fp8mx(const PoolDevice& dev, const PoolTask& t, int h, int H, int D, long pb) {
+  const float4* ks = static_cast<const float4*>(dev.k_src);
+  const float4* vs = static_cast<const float4*>(dev.v_src);
+  const int G = D / 64;
+  unsigned char* kslab = static_cast<unsigned char*>(dev.k_pages) + (long(t.page) * H + h) * pb;
+  unsigned char* vslab = static_cast<unsigned char*>(dev.v_pages) + (long(t.page) * H + h) * pb;
+  unsigned char* kexp = static_cast<unsigned char*>(dev.k_scale) + (long(t.page) * H + h) * 16 * G;
+  unsigned char* vexp = static_cast<unsigned char*>(dev.v_scale) + (long(t.page) * H + h) * 16 * G;
+#pragma unroll
+  for (int u = 0; u < kItemsPerLane; ++u) {
+    const Item im = item(t, u, h, H, D);
+    float kx[8], vx[8];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const float4 a = im.ok ? ks[im.src / 4 + p] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 b = im.ok ? vs[im.src / 4 + p] : make_float4(0.f, 0.f, 0.f, 0.f);
+      kx[4 * p + 0] = a.x; kx[4 * p + 1] = a.y; kx[4 * p + 2] = a.z; kx[4 * p + 3] = a.w;
+      vx[4 * p + 0] = b.x; vx[4 * p + 1] = b.y; vx[4 * p + 2] = b.z; vx[4 * p + 3] = b.w;
+    }
+    float ak = 0.0f, av = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ak = fmaxf(ak, fabsf(kx[i]));
+      av = fmaxf(av, fabsf(vx[i]));
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      ak = fmaxf(ak, __shfl_xor(ak, o, 64));
+      av = fmaxf(av, __shfl_xor(av, o, 64));
+    }
+    if (!im.ok) continue;
+    const int ek = tile_exponent_byte(ak), ev = tile_exponent_byte(av);
+    const float ik = ldexpf(1.0f, 127 - ek), iv = ldexpf(1.0f, 127 - ev);
+    unsigned lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= unsigned(quant_e4m3(kx[i], ik)) << (8 * i);
+      hi |= unsigned(quant_e4m3(kx[4 + i], ik)) << (8 * i);
+    }
+    *reinterpret_cast<uint2*>(kslab + k_index_fp8(im.slot, im.c0, D)) = make_uint2(lo, hi);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vslab[v_index_fp8(im.slot, im.c0 + i)] = quant_e4m3(vx[i], iv);
+    if ((im.c0 & 63) == 0) {
+      kexp[im.slot * G + im.c0 / 64] = static_cast<unsigned char>(ek);
+      vexp[im.slot * G + im.c0 / 64] = static_cast<unsigned char>(ev);
+    }
   }
 }
 
@@ -194,8 +260,21 @@ __global__ __launch_bounds__(kThreads) void pool_update_kernel(PoolDevice dev, P
     }
     if (batch.kv_dtype == PKV_FP8_E4M3 && int(threadIdx.x) < nh) {
       const int h = h0 + threadIdx.x;
-      dev.k_scale[long(t.page) * H + h] = dev.k_scale[long(t.cow_src) * H + h];
-      dev.v_scale[long(t.page) * H + h] = dev.v_scale[long(t.cow_src) * H + h];
+      float* ksc = static_cast<float*>(dev.k_scale);
+      float* vsc = static_cast<float*>(dev.v_scale);
+      ksc[long(t.page) * H + h] = ksc[long(t.cow_src) * H + h];
+      vsc[long(t.page) * H + h] = vsc[long(t.cow_src) * H + h];
+    }
+    if (batch.kv_dtype == PKV_FP8_E4M3_MX64) {
+      // the exponent bytes of the copied heads: 16 tokens x D/64 each
+      const int nb = nh * 16 * (D / 64);
+      unsigned char* ke = static_cast<unsigned char*>(dev.k_scale);
+      unsigned char* ve = static_cast<unsigned char*>(dev.v_scale);
+      const long so8 = (long(t.cow_src) * H + h0) * 16 * (D / 64), do8 = (long(t.page) * H + h0) * 16 * (D / 64);
+      for (int i = threadIdx.x; i < nb; i += kThreads) {
+        ke[do8 + i] = ke[so8 + i];
+        ve[do8 + i] = ve[so8 + i];
+      }
     }
     __syncthreads();
   }
@@ -204,6 +283,7 @@ __global__ __launch_bounds__(kThreads) void pool_update_kernel(PoolDevice dev, P
   if (t.n > 0 && h < H) {
     if (batch.kv_dtype == PKV_BF16) write_bf16(dev, t, h, H, D, pb);
     else if (batch.kv_dtype == PKV_F32) write_f32(dev, t, h, H, D, pb);
+    else if (batch.kv_dtype == PKV_FP8_E4M3_MX64) write_fp8mx(dev, t, h, H, D, pb);
     else write_fp8(dev, t, h, H, D, pb);
   }
 
@@ -254,9 +334,29 @@ __global__ __launch_bounds__(kThreads) void pool_move_kernel(PoolDevice dev, Poo
     const PoolMove m = batch.moves[i];
     const int ts = m.slots & 0xFF, td = (m.slots >> 8) & 0xFF;
     const long so = (long(m.src_page) * H + h) * pb, dO = (long(m.dst_page) * H + h) * pb;
-    if (dt == PKV_FP8_E4M3) {
-      const float ks = dev.k_scale[long(m.src_page) * H + h], kd = dev.k_scale[long(m.dst_page) * H + h];
-      const float vs = dev.v_scale[long(m.src_page) * H + h], vd = dev.v_scale[long(m.dst_page) * H + h];
+    if (dt == PKV_FP8_E4M3_MX64) {
+      // codes and the token's own exponent bytes move unchanged
+      for (int c = lane; c < D; c += 64) {
+        const unsigned char kc = k_elem<unsigned char>(K + so, ts, c, D, PKV_FP8_E4M3);
+        const unsigned char vc = v_elem<unsigned char>(V + so, ts, c, D, PKV_FP8_E4M3);
+        k_elem<unsigned char>(K + dO, td, c, D, PKV_FP8_E4M3) = kc;
+        v_elem<unsigned char>(V + dO, td, c, D, PKV_FP8_E4M3) = vc;
+      }
+      const int G = D / 64;
+      if (lane < G) {
+        unsigned char* ke = static_cast<unsigned char*>(dev.k_scale);
+        unsigned char* ve = static_cast<unsigned char*>(dev.v_scale);
+        const long s8 = ((long(m.src_page) * H + h) * 16 + ts) * G + lane;
+        const long d8 = ((long(m.dst_page) * H + h) * 16 + td) * G + lane;
+        const unsigned char kx = ke[s8], vx = ve[s8];
+        ke[d8] = kx;
+        ve[d8] = vx;
+      }
+    } else if (dt == PKV_FP8_E4M3) {
+      const float* ksc = static_cast<const float*>(dev.k_scale);
+      const float* vsc = static_cast<const float*>(dev.v_scale);
+      const float ks = ksc[long(m.src_page) * H + h], kd = ksc[long(m.dst_page) * H + h];
+      const float vs = vsc[long(m.src_page) * H + h], vd = vsc[long(m.dst_page) * H + h];
       for (int c = lane; c < D; c += 64) {
         const unsigned char kc = k_elem<unsigned char>(K + so, ts, c, D, dt);
         const unsigned char vc = v_elem<unsigned char>(V + so, ts, c, D, dt);

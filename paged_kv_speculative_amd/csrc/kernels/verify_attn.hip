@@ -69,8 +69,8 @@ struct VerifyParams {
   const void* q;
   const char* k_pages;
   const char* v_pages;
-  const float* k_scale;
-  const float* v_scale;
+  const void* k_scale;   // FP8: fp32 per (page, KV head); MX: E8M0 bytes [page][head][token][D/64]
+  const void* v_scale;
   const int* block_table;
   const int* seq_lens;
   const int* batch_slots;
@@ -120,6 +120,21 @@ __device__ inline Dw2 fp8x4_to_bf16x4(unsigned w) {
   const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
   const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
   return Dw2{__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b)};
+}
+
+// The same with a per-lane scale multiplied in before the rounding to bf16
+// (gfx950's scaled FP8 conversion).  With power-of-two scales the products
+// are exact in bf16.
+__device__ inline Dw2 fp8x4_to_bf16x4_scaled(unsigned w, float scale) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, true);
+  return Dw2{__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b)};
+}
+
+// 2^(e - 127) of an OCP E8M0 exponent byte e (0..254).
+__device__ inline float e8m0_value(unsigned e) {
+  e = e < 254u ? e : 254u;                       // never written above 254; keeps stale bytes finite
+  return __uint_as_float(e ? e << 23 : 0x00400000u);
 }
 
 __device__ inline u32x4 load16(const void* p) { return *static_cast<const u32x4*>(p); }
@@ -186,13 +201,15 @@ __device__ inline f32x4 mfma_bf16_k16(unsigned a0, unsigned a1, unsigned b0, uns
 // Compile-time shape of the streaming kernel for one (head_dim, row tiles, KV type).
 // W2: the variant that runs two waves per SIMD (at most 256 registers each),
 // with two pages in flight per wave.
-template <int D, int NT, bool FP8, bool W2 = false>
+// MX: FP8 with a power-of-two scale per 64 channels of each token.
+template <int D, int NT, bool FP8, bool W2 = false, bool MX = false>
 struct Shape {
   static constexpr int KS = D / 32;                  // k-steps of the score MFMA (32 channels)
   static constexpr int DT = D / 16;                  // 16-channel tiles of the output
   static constexpr int KL = FP8 ? KS / 2 : KS;       // 16-byte K loads per page
   static constexpr int VL = FP8 ? D / 64 : D / 32;   // 16-byte V loads per page
-  static constexpr int LPP = KL + VL + (FP8 ? 2 : 0); // vector loads per page (FP8: + scales)
+  // vector loads per page (FP8: + two scales; MX: + one K and D/64 V scale words)
+  static constexpr int LPP = KL + VL + (FP8 ? (MX ? 1 + D / 64 : 2) : 0);
   // Q of a unit staged in LDS: QS slots per wave of NT*16 rows x D bf16, plus
   // the unit's n_q ancestor masks
   static constexpr int QS = W2 ? 1 : 2;
@@ -217,6 +234,7 @@ struct PageRegs {
 struct PageMeta {
   int unit, page, n;
   float ks, vs;          // FP8 scales of the page (per lane, all lanes alike)
+  unsigned ksw, vsw[2];  // MX: the lane's words of E8M0 scale bytes (K: its token; V: its four tokens)
 };
 
 // A ring slot's length word: the sequence's length N in bits 0..23 and its
@@ -313,10 +331,11 @@ struct Cursor {
 // SHARED: two waves (row groups) read the same pages at about the same time;
 // their loads keep the default cache policy so the second finds the first's
 // lines in L2.  Otherwise pages stream with the non-temporal policy.
-template <int D, int NT, bool FP8, bool TREE, bool SHARED, bool W2>
+template <int D, int NT, bool FP8, bool TREE, bool SHARED, bool W2, bool MX>
 __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, int hi, int worker,
                              int q_lds_off, int row0) {
-  using SH = Shape<D, NT, FP8, W2>;
+  using SH = Shape<D, NT, FP8, W2, MX>;
+  constexpr int G = D / 64;                      // MX: scale tiles per token
   using Regs = PageRegs<D, FP8>;
   constexpr int KS = SH::KS, DT = SH::DT, PF = SH::PF;
   const int lane = threadIdx.x & 63;
@@ -384,15 +403,30 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
     M.unit = (c.b << 16) | c.g;
     M.page = c.page;
     M.n = valid ? c.n : 0;
-    if (FP8) {
+    if (MX) {
+      // the page-head's E8M0 bytes, [token][tile], K then V: this lane's K
+      // token and tile, and the four tokens of its V operand
+      const long sb = (long(id) * P.Hkv + c.g) * 16 * G;
+      const auto rks = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<unsigned char*>(static_cast<const unsigned char*>(P.k_scale) + sb), 0, valid ? 16 * G : 0,
+          kBufferFlags);
+      const auto rvs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<unsigned char*>(static_cast<const unsigned char*>(P.v_scale) + sb), 0, valid ? 16 * G : 0,
+          kBufferFlags);
+      const int kbyte = m16 * G + ((D / 4) * jg) / 64;
+      M.ksw = unsigned(__builtin_amdgcn_raw_buffer_load_b32(rks, kbyte & ~3, 0, 0));
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        M.vsw[g] = unsigned(__builtin_amdgcn_raw_buffer_load_b32(rvs, 4 * jg * G + 4 * g, 0, 0));
+    } else if (FP8) {
       // the scales come through the vector path, issued after the page's
       // loads: they complete with the page, whereas a scalar load here
       // (a random line of the scale arrays) would be waited for at the
       // next scalar wait, one page later
       const int so = (id * P.Hkv + c.g) * 4;
-      const auto rks = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(P.k_scale), 0, valid ? 0x7FFFFFFF : 0,
+      const auto rks = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(P.k_scale), 0, valid ? 0x7FFFFFFF : 0,
                                                          kBufferFlags);
-      const auto rvs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(P.v_scale), 0, valid ? 0x7FFFFFFF : 0,
+      const auto rvs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(P.v_scale), 0, valid ? 0x7FFFFFFF : 0,
                                                          kBufferFlags);
       M.ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rks, 0, so, 0));
       M.vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rvs, 0, so, 0));
@@ -536,6 +570,8 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
     const int tok0 = M.page * 16;
     const int L = (M.n & kLenMask) - (M.n >> kNqShift);
     // scores S^T (lane: row 16nt+m16, tokens tok0 + 4jg .. +3)
+    float kx = 1.0f;                             // MX: this lane's K scale (its token, its tile)
+    if (MX) kx = e8m0_value((M.ksw >> (8 * ((m16 * G + ((D / 4) * jg) / 64) & 3))) & 0xFFu);
     f32x4 sc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -546,7 +582,8 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
         if (FP8) {
           const u32x4 w = R.k[s >> 1];
           const int o = (s & 1) * 2;
-          const Dw2 a0 = fp8x4_to_bf16x4(w[o]), a1 = fp8x4_to_bf16x4(w[o + 1]);
+          const Dw2 a0 = MX ? fp8x4_to_bf16x4_scaled(w[o], kx) : fp8x4_to_bf16x4(w[o]);
+          const Dw2 a1 = MX ? fp8x4_to_bf16x4_scaled(w[o + 1], kx) : fp8x4_to_bf16x4(w[o + 1]);
           kf = u32x4{a0.lo, a0.hi, a1.lo, a1.hi};
         } else {
           kf = R.k[s];
@@ -556,7 +593,7 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
       sc[nt] = a;
     }
     float ksc = P.scale_log2, vsc = 1.0f;
-    if (FP8) {
+    if (FP8 && !MX) {
       ksc *= M.ks;
       vsc = M.vs;
     }
@@ -600,8 +637,21 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
       }
     }
 
-    // online softmax (base 2, lazy rescale) and the P^T operands
-    unsigned ph[NT][2], pl[NT][2];
+    // MX: the V scales of this lane's four tokens, per tile of channels
+    float vx[G][4];
+    if (MX) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int byte = e * G + g;                  // token 4jg+e, tile g
+          vx[g][e] = e8m0_value((M.vsw[byte >> 2] >> (8 * (byte & 3))) & 0xFFu);
+        }
+    }
+    // online softmax (base 2, lazy rescale) and the P^T operands (MX: one
+    // hi/lo pair per tile of channels, P times the tokens' V scales)
+    constexpr int PG = MX ? G : 1;
+    unsigned ph[NT][2], pl[NT][2], pm[PG][NT][2], pml[PG][NT][2];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const float mx = row_max4(fmaxf(fmaxf(sc[nt][0], sc[nt][1]), fmaxf(sc[nt][2], sc[nt][3])));
@@ -619,11 +669,27 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
 #pragma unroll
       for (int e = 0; e < 4; ++e) p[e] = exp2_fast(sc[nt][e] - m_ref);
       l_run[nt] += (p[0] + p[1]) + (p[2] + p[3]);
-      if (FP8) {
+      if (MX) {
+        // P = hi + lo as for bf16 KV; scaling by a power of two is exact, so
+        // the pair of (P x scale) is the scaled pair of P
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          r[e] = p[e] - __uint_as_float(__float_as_uint(p[e]) & 0xFFFF0000u);
+#pragma unroll
+        for (int g = 0; g < PG; ++g) {
+          pm[g][nt][0] = pack_hi16(p[0] * vx[g][0], p[1] * vx[g][1]);
+          pm[g][nt][1] = pack_hi16(p[2] * vx[g][2], p[3] * vx[g][3]);
+          pml[g][nt][0] = pack_rne_bf16(r[0] * vx[g][0], r[1] * vx[g][1]);
+          pml[g][nt][1] = pack_rne_bf16(r[2] * vx[g][2], r[3] * vx[g][3]);
+        }
+      } else if (FP8) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) p[e] *= vsc;
       }
-      if (kSplitP) {
+      if (MX) {
+        ph[nt][0] = ph[nt][1] = pl[nt][0] = pl[nt][1] = 0u;
+      } else if (kSplitP) {
         // P = hi + lo: hi the truncated upper half, lo the rounded rest
         float r[4];
 #pragma unroll
@@ -655,6 +721,13 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
+        if (MX) {
+          // channels of tile dt lie in 64-channel tile dt / 4
+          const int g = (dt >> 2) % PG;
+          acc[dt][nt] = mfma_bf16_k16(v0, v1, pm[g][nt][0], pm[g][nt][1], acc[dt][nt]);
+          acc[dt][nt] = mfma_bf16_k16(v0, v1, pml[g][nt][0], pml[g][nt][1], acc[dt][nt]);
+          continue;
+        }
         acc[dt][nt] = mfma_bf16_k16(v0, v1, ph[nt][0], ph[nt][1], acc[dt][nt]);
         if (kSplitP) acc[dt][nt] = mfma_bf16_k16(v0, v1, pl[nt][0], pl[nt][1], acc[dt][nt]);
       }
@@ -819,7 +892,7 @@ size_t split_smem(int batch) {
 
 // Each wave is one worker streaming an equal contiguous range of the
 // (sequence, KV head, page) positions.
-template <int D, int NT, bool FP8, bool TREE, bool SHARED, bool W2>
+template <int D, int NT, bool FP8, bool TREE, bool SHARED, bool W2, bool MX>
 __device__ inline void stream_kernel_body(VerifyParams P) {
   extern __shared__ int s_cum[];
   const int cum_words = (P.batch + 1 + 3) & ~3;
@@ -833,19 +906,19 @@ __device__ inline void stream_kernel_body(VerifyParams P) {
   const int range = worker / P.rg, rgi = worker % P.rg;
   if (range >= n_rng) return;
   const int lo = int(range_lo(range, W, n_rng)), hi = int(range_lo(range + 1, W, n_rng));
-  stream_range<D, NT, FP8, TREE, SHARED, W2>(P, s_cum, lo, hi, worker, cum_lds_bytes(P.batch), rgi * P.rows_w);
+  stream_range<D, NT, FP8, TREE, SHARED, W2, MX>(P, s_cum, lo, hi, worker, cum_lds_bytes(P.batch), rgi * P.rows_w);
 }
 
-template <int D, int NT, bool FP8, bool TREE, bool SHARED>
+template <int D, int NT, bool FP8, bool TREE, bool SHARED, bool MX = false>
 __global__ __launch_bounds__(kThreads) void verify_stream_kernel(VerifyParams P) {
-  stream_kernel_body<D, NT, FP8, TREE, SHARED, false>(P);
+  stream_kernel_body<D, NT, FP8, TREE, SHARED, false, MX>(P);
 }
 
 // Two waves per SIMD: each kept within 256 registers.
-template <int D, int NT, bool FP8, bool TREE, bool SHARED>
+template <int D, int NT, bool FP8, bool TREE, bool SHARED, bool MX = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void verify_stream_kernel_w2(VerifyParams P) {
-  stream_kernel_body<D, NT, FP8, TREE, SHARED, true>(P);
+  stream_kernel_body<D, NT, FP8, TREE, SHARED, true, MX>(P);
 }
 
 // fp32 K/V (plain [token][channel] pages): one workgroup per (query head,
@@ -925,7 +998,7 @@ __global__ __launch_bounds__(128) void verify_f32_kernel(VerifyParams P) {
 
 struct Plan {
   int D, NT, rows, n_wg, rg, rows_w;
-  bool fp8, tree, f32;
+  bool fp8, mx, tree, f32;
   size_t cum_bytes, part_bytes;
 };
 
@@ -949,12 +1022,14 @@ pkv_status check_args(const pkv_verify_args* a, Plan* pl) {
   pl->tree = a->anc_mask != nullptr;
   pl->f32 = false;
   pl->fp8 = false;
+  pl->mx = false;
   if (a->kv_dtype == PKV_F32) {
     if (a->q_dtype != PKV_F32) return fail(PKV_ERR_INVALID_ARG, "fp32 KV needs fp32 queries");
     pl->f32 = true;
-  } else if (a->kv_dtype == PKV_BF16 || a->kv_dtype == PKV_FP8_E4M3) {
+  } else if (a->kv_dtype == PKV_BF16 || a->kv_dtype == PKV_FP8_E4M3 || a->kv_dtype == PKV_FP8_E4M3_MX64) {
     if (a->q_dtype != PKV_BF16) return fail(PKV_ERR_INVALID_ARG, "bf16/fp8 KV needs bf16 queries");
-    pl->fp8 = a->kv_dtype == PKV_FP8_E4M3;
+    pl->fp8 = a->kv_dtype != PKV_BF16;
+    pl->mx = a->kv_dtype == PKV_FP8_E4M3_MX64;
     if (pl->fp8 && (!a->k_scale || !a->v_scale)) return fail(PKV_ERR_INVALID_ARG, "FP8 KV needs scales");
     if (pl->rows > 64) return fail(PKV_ERR_UNSUPPORTED, "n_q * Hq/Hkv must be <= 64");
   } else {
@@ -1014,13 +1089,13 @@ size_t split_smem_rt(int D, int NT, int batch) {
 // fast or faster.
 inline bool two_waves(int NT, bool fp8) { return PKV_TWO_WAVES && fp8 && NT <= 2; }
 
-template <int D, int NT, bool FP8, bool TREE, bool SHARED = false>
+template <int D, int NT, bool FP8, bool TREE, bool SHARED = false, bool MX = false>
 const void* split_fn() {
-  return reinterpret_cast<const void*>(&verify_stream_kernel<D, NT, FP8, TREE, SHARED>);
+  return reinterpret_cast<const void*>(&verify_stream_kernel<D, NT, FP8, TREE, SHARED, MX>);
 }
-template <int D, int NT, bool FP8, bool TREE, bool SHARED>
+template <int D, int NT, bool FP8, bool TREE, bool SHARED, bool MX = false>
 const void* split_fn_w2() {
-  return reinterpret_cast<const void*>(&verify_stream_kernel_w2<D, NT, FP8, TREE, SHARED>);
+  return reinterpret_cast<const void*>(&verify_stream_kernel_w2<D, NT, FP8, TREE, SHARED, MX>);
 }
 
 template <int D, int NT>
@@ -1047,6 +1122,16 @@ const void* pick_fn(int NT, bool shared, bool fp8, bool tree) {
   }
 }
 
+// Per-64-channel scales (MX): the two-waves kernels for up to 32 rows per
+// wave, the one-wave kernel for 33..48.
+template <int D>
+const void* pick_fn_mx(int NT, bool shared, bool tree) {
+  if (shared) return tree ? split_fn_w2<D, 2, true, true, true, true>() : split_fn_w2<D, 2, true, false, true, true>();
+  if (NT == 1) return tree ? split_fn_w2<D, 1, true, true, false, true>() : split_fn_w2<D, 1, true, false, false, true>();
+  if (NT == 2) return tree ? split_fn_w2<D, 2, true, true, false, true>() : split_fn_w2<D, 2, true, false, false, true>();
+  return tree ? split_fn<D, 3, true, true, false, true>() : split_fn<D, 3, true, false, false, true>();
+}
+
 pkv_status make_plan(const pkv_verify_args* a, Plan* pl) {
   pkv_status st = check_args(a, pl);
   if (st != PKV_OK) return st;
@@ -1060,7 +1145,9 @@ pkv_status make_plan(const pkv_verify_args* a, Plan* pl) {
                               ? (pl->D == 64 ? (pl->NT == 1 ? split_smem<64, 1, true>(a->batch) : split_smem<64, 2, true>(a->batch))
                                              : (pl->NT == 1 ? split_smem<128, 1, true>(a->batch) : split_smem<128, 2, true>(a->batch)))
                               : split_smem_rt(pl->D, pl->NT, a->batch);
-      const void* fn = pl->D == 64 ? pick_fn<64>(pl->NT, pl->rg > 1, pl->fp8, pl->tree)
+      const void* fn = pl->mx ? (pl->D == 64 ? pick_fn_mx<64>(pl->NT, pl->rg > 1, pl->tree)
+                                             : pick_fn_mx<128>(pl->NT, pl->rg > 1, pl->tree))
+                     : pl->D == 64 ? pick_fn<64>(pl->NT, pl->rg > 1, pl->fp8, pl->tree)
                                    : pick_fn<128>(pl->NT, pl->rg > 1, pl->fp8, pl->tree);
       n = resident_workgroups(fn, smem);
     }
@@ -1071,14 +1158,14 @@ pkv_status make_plan(const pkv_verify_args* a, Plan* pl) {
   return PKV_OK;
 }
 
-template <int D, int NT, bool FP8, bool TREE, bool SHARED>
+template <int D, int NT, bool FP8, bool TREE, bool SHARED, bool MX = false>
 hipError_t launch_split_w2(const VerifyParams& p, hipStream_t st) {
   const size_t smem = split_smem<D, NT, true>(p.batch);
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&verify_stream_kernel_w2<D, NT, FP8, TREE, SHARED>),
+      reinterpret_cast<const void*>(&verify_stream_kernel_w2<D, NT, FP8, TREE, SHARED, MX>),
       hipFuncAttributeMaxDynamicSharedMemorySize, int(split_smem<D, NT, true>(4096)));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((verify_stream_kernel_w2<D, NT, FP8, TREE, SHARED>), dim3(p.n_wg), dim3(kThreads), smem, st, p);
+  hipLaunchKernelGGL((verify_stream_kernel_w2<D, NT, FP8, TREE, SHARED, MX>), dim3(p.n_wg), dim3(kThreads), smem, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((verify_merge_kernel<D>), dim3(p.batch * p.Hkv, (p.rows * (D / 4) + kThreads - 1) / kThreads),
@@ -1086,14 +1173,14 @@ hipError_t launch_split_w2(const VerifyParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int D, int NT, bool FP8, bool TREE, bool SHARED = false>
+template <int D, int NT, bool FP8, bool TREE, bool SHARED = false, bool MX = false>
 hipError_t launch_split(const VerifyParams& p, hipStream_t st) {
   const size_t smem = split_smem<D, NT>(p.batch);
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&verify_stream_kernel<D, NT, FP8, TREE, SHARED>),
+      reinterpret_cast<const void*>(&verify_stream_kernel<D, NT, FP8, TREE, SHARED, MX>),
       hipFuncAttributeMaxDynamicSharedMemorySize, int(split_smem<D, NT>(4096)));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((verify_stream_kernel<D, NT, FP8, TREE, SHARED>), dim3(p.n_wg), dim3(kThreads), smem, st, p);
+  hipLaunchKernelGGL((verify_stream_kernel<D, NT, FP8, TREE, SHARED, MX>), dim3(p.n_wg), dim3(kThreads), smem, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((verify_merge_kernel<D>), dim3(p.batch * p.Hkv, (p.rows * (D / 4) + kThreads - 1) / kThreads),
@@ -1105,6 +1192,15 @@ template <int D, int NT>
 hipError_t dispatch_kv(const VerifyParams& p, bool fp8, bool tree, hipStream_t st) {
   if (fp8) return tree ? launch_split<D, NT, true, true>(p, st) : launch_split<D, NT, true, false>(p, st);
   return tree ? launch_split<D, NT, false, true>(p, st) : launch_split<D, NT, false, false>(p, st);
+}
+
+template <int D>
+hipError_t dispatch_mx(const VerifyParams& p, int NT, bool tree, hipStream_t st) {
+  if (p.rg > 1)
+    return tree ? launch_split_w2<D, 2, true, true, true, true>(p, st) : launch_split_w2<D, 2, true, false, true, true>(p, st);
+  if (NT == 1) return tree ? launch_split_w2<D, 1, true, true, false, true>(p, st) : launch_split_w2<D, 1, true, false, false, true>(p, st);
+  if (NT == 2) return tree ? launch_split_w2<D, 2, true, true, false, true>(p, st) : launch_split_w2<D, 2, true, false, false, true>(p, st);
+  return tree ? launch_split<D, 3, true, true, false, true>(p, st) : launch_split<D, 3, true, false, false, true>(p, st);
 }
 
 template <int D>
@@ -1185,6 +1281,8 @@ extern "C" pkv_status spec_verify_attention(const pkv_verify_args* a, void* stre
     else
       hipLaunchKernelGGL(verify_f32_kernel<128>, dim3(p.Hq, p.batch), dim3(128), 0, s, p);
     e = hipGetLastError();
+  } else if (pl.mx) {
+    e = pl.D == 64 ? dispatch_mx<64>(p, pl.NT, pl.tree, s) : dispatch_mx<128>(p, pl.NT, pl.tree, s);
   } else if (pl.D == 64) {
     e = dispatch_nt<64>(p, pl.NT, pl.fp8, pl.tree, s);
   } else {

@@ -129,7 +129,8 @@ int64_t pkv_page_bytes(pkv_dtype kv_dtype, int32_t page_size, int32_t head_dim) 
   switch (kv_dtype) {
     case PKV_F32: return int64_t(page_size) * head_dim * 4;
     case PKV_BF16: return int64_t(page_size) * head_dim * 2;
-    case PKV_FP8_E4M3: return int64_t(page_size) * head_dim;
+    case PKV_FP8_E4M3:
+    case PKV_FP8_E4M3_MX64: return int64_t(page_size) * head_dim;
     default: return 0;
   }
 }
@@ -140,7 +141,8 @@ pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out) {
   const pkv_pool_desc& d = *desc;
   if (d.num_pages <= 0 || d.num_kv_heads <= 0 || d.max_seqs <= 0 || d.max_pages_per_seq <= 0)
     return fail(PKV_ERR_INVALID_ARG, "pool sizes must be positive");
-  if (d.kv_dtype != PKV_F32 && d.kv_dtype != PKV_BF16 && d.kv_dtype != PKV_FP8_E4M3)
+  if (d.kv_dtype != PKV_F32 && d.kv_dtype != PKV_BF16 && d.kv_dtype != PKV_FP8_E4M3 &&
+      d.kv_dtype != PKV_FP8_E4M3_MX64)
     return fail(PKV_ERR_INVALID_ARG, "unknown kv dtype");
   int64_t pb = pkv_page_bytes(d.kv_dtype, d.page_size, d.head_dim);
   if (pb == 0) return fail(PKV_ERR_UNSUPPORTED, "page_size must be 16 and head_dim 64 or 128");
@@ -148,7 +150,7 @@ pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out) {
   if (any_dev) {
     if (!d.k_pages || !d.v_pages || !d.block_table || !d.seq_lens)
       return fail(PKV_ERR_INVALID_ARG, "device pool needs k_pages, v_pages, block_table, seq_lens");
-    if (d.kv_dtype == PKV_FP8_E4M3 && (!d.k_scale || !d.v_scale))
+    if ((d.kv_dtype == PKV_FP8_E4M3 || d.kv_dtype == PKV_FP8_E4M3_MX64) && (!d.k_scale || !d.v_scale))
       return fail(PKV_ERR_INVALID_ARG, "FP8 pool needs k_scale and v_scale");
   }
   std::vector<int32_t> order(d.num_pages);
@@ -233,7 +235,8 @@ pkv_status paged_kv_append(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
   std::lock_guard<std::mutex> lock(pool->mu);
   const pkv_pool_desc& d = pool->desc;
   if (pool->device) {
-    bool ok = (d.kv_dtype == PKV_FP8_E4M3) ? src_dtype == PKV_F32 : src_dtype == d.kv_dtype;
+    bool ok = (d.kv_dtype == PKV_FP8_E4M3 || d.kv_dtype == PKV_FP8_E4M3_MX64) ? src_dtype == PKV_F32
+                                                                                : src_dtype == d.kv_dtype;
     if (!ok) return fail(PKV_ERR_INVALID_ARG, "source dtype does not match the pool dtype");
   }
   // Validate and count pages by simulating the whole call on a copy of the

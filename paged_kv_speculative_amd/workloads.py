@@ -50,7 +50,7 @@ class Workload:
     num_q_heads: int
     num_kv_heads: int
     head_dim: int
-    kv_dtype: str                 # "f32" | "bf16" | "fp8"
+    kv_dtype: str                 # "f32" | "bf16" | "fp8" | "fp8mx"
     q_dtype: str                  # "f32" | "bf16"
     cached_lens: np.ndarray       # L_b
     prefix_len: int = 0           # tokens shared by every sequence (in common pages)

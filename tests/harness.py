@@ -14,7 +14,7 @@ from oracle import pool as opool
 from paged_kv_speculative_amd import Pool, tree_ancestor_masks
 from paged_kv_speculative_amd.workloads import bf16_to_f32
 
-TOL = {"f32": 2e-3, "bf16": 2e-3, "fp8": 2e-2}
+TOL = {"f32": 2e-3, "bf16": 2e-3, "fp8": 2e-2, "fp8mx": 2e-2}
 
 
 def max_pages(w):
@@ -95,7 +95,7 @@ def oracle_sequence_kv(w, b):
     S = 16
     n = int(w.seq_lens[b])
     pm = opool.PoolModel(-(-n // S) + 2, S, w.num_kv_heads, w.head_dim,
-                         kv_dtype="fp8" if w.kv_dtype == "fp8" else "f64")
+                         kv_dtype=w.kv_dtype if w.kv_dtype in ("fp8", "fp8mx") else "f64")
     pm.alloc(0)
     k, v = w.private_kv(b)
     if w.prefix_len:
