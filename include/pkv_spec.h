@@ -274,6 +274,14 @@ typedef struct {
   int32_t num_splits;         /* workgroups sharing the work; 0 = as many as the
                                  GPU keeps resident                              */
   const int32_t* n_q_seq;     /* device [batch] slots per sequence, or NULL (n_q) */
+  int32_t shared_prefix_pages;/* cascade (bf16 KV): the first this-many block-table
+                                 entries are the same physical pages for every
+                                 sequence of the call (a prefix shared through
+                                 paged_kv_alloc) and hold cached tokens only
+                                 (16 * shared_prefix_pages <= L for every
+                                 sequence); they are attended once for all
+                                 sequences and merged with each sequence's own
+                                 pages.  0 = off                                 */
 } pkv_verify_args;
 
 pkv_status spec_verify_workspace_size(const pkv_verify_args* args, size_t* bytes_out);

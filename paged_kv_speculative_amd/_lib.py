@@ -57,7 +57,7 @@ class VerifyArgs(C.Structure):
         ("seq_lens", C.c_void_p), ("batch_slots", C.c_void_p), ("anc_mask", C.c_void_p),
         ("sm_scale", C.c_float), ("out", C.c_void_p), ("lse", C.c_void_p),
         ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t), ("num_splits", C.c_int32),
-        ("n_q_seq", C.c_void_p),
+        ("n_q_seq", C.c_void_p), ("shared_prefix_pages", C.c_int32),
     ]
 
 

@@ -191,24 +191,27 @@ class Pool:
 
     # -- verification over this pool --------------------------------------------
     def prepare_verify(self, q, n_q, slots=None, anc_mask=None, sm_scale=None, buffers=None,
-                       num_splits=0, n_q_seq=None):
+                       num_splits=0, n_q_seq=None, shared_prefix_pages=0):
         return PreparedVerify(q, self.k_pages, self.v_pages, self.block_table, self.seq_lens,
                               n_q=n_q, num_kv_heads=self.num_kv_heads, kv_dtype=self.kv_dtype,
                               k_scale=self.k_scale, v_scale=self.v_scale, batch_slots=slots,
                               anc_mask=anc_mask, sm_scale=sm_scale, buffers=buffers,
-                              num_splits=num_splits, n_q_seq=n_q_seq)
+                              num_splits=num_splits, n_q_seq=n_q_seq,
+                              shared_prefix_pages=shared_prefix_pages)
 
     def verify(self, q, n_q, slots=None, anc_mask=None, sm_scale=None, buffers=None, num_splits=0,
-               n_q_seq=None, stream=None):
+               n_q_seq=None, shared_prefix_pages=0, stream=None):
         return spec_verify_attention(
             q, self.k_pages, self.v_pages, self.block_table, self.seq_lens, n_q=n_q,
             num_kv_heads=self.num_kv_heads, kv_dtype=self.kv_dtype, k_scale=self.k_scale,
             v_scale=self.v_scale, batch_slots=slots, anc_mask=anc_mask, sm_scale=sm_scale,
-            buffers=buffers, num_splits=num_splits, n_q_seq=n_q_seq, stream=stream)
+            buffers=buffers, num_splits=num_splits, n_q_seq=n_q_seq,
+            shared_prefix_pages=shared_prefix_pages, stream=stream)
 
 
 def _verify_args(q, k_pages, v_pages, block_table, seq_lens, n_q, num_kv_heads, kv_dtype, k_scale,
-                 v_scale, batch_slots, anc_mask, sm_scale, num_splits, n_q_seq=None):
+                 v_scale, batch_slots, anc_mask, sm_scale, num_splits, n_q_seq=None,
+                 shared_prefix_pages=0):
     B, nq, Hq, d = q.shape
     assert nq == n_q and q.is_contiguous()
     a = VerifyArgs()
@@ -234,6 +237,7 @@ def _verify_args(q, k_pages, v_pages, block_table, seq_lens, n_q, num_kv_heads, 
     if n_q_seq is not None:
         assert n_q_seq.dtype == torch.int32 and n_q_seq.numel() == B and n_q_seq.is_contiguous()
         a.n_q_seq = n_q_seq.data_ptr()
+    a.shared_prefix_pages = int(shared_prefix_pages)
     return a
 
 
@@ -254,9 +258,11 @@ class VerifyBuffers:
 
 def spec_verify_attention(q, k_pages, v_pages, block_table, seq_lens, *, n_q, num_kv_heads,
                           kv_dtype, k_scale=None, v_scale=None, batch_slots=None, anc_mask=None,
-                          sm_scale=None, buffers=None, num_splits=0, n_q_seq=None, stream=None):
+                          sm_scale=None, buffers=None, num_splits=0, n_q_seq=None,
+                          shared_prefix_pages=0, stream=None):
     a = _verify_args(q, k_pages, v_pages, block_table, seq_lens, n_q, num_kv_heads, kv_dtype,
-                     k_scale, v_scale, batch_slots, anc_mask, sm_scale, num_splits, n_q_seq)
+                     k_scale, v_scale, batch_slots, anc_mask, sm_scale, num_splits, n_q_seq,
+                     shared_prefix_pages)
     ws = verify_workspace_size(a)
     if buffers is None:
         B, _, Hq, d = q.shape
@@ -276,9 +282,10 @@ class PreparedVerify:
 
     def __init__(self, q, k_pages, v_pages, block_table, seq_lens, *, n_q, num_kv_heads, kv_dtype,
                  k_scale=None, v_scale=None, batch_slots=None, anc_mask=None, sm_scale=None,
-                 buffers=None, num_splits=0, n_q_seq=None):
+                 buffers=None, num_splits=0, n_q_seq=None, shared_prefix_pages=0):
         a = _verify_args(q, k_pages, v_pages, block_table, seq_lens, n_q, num_kv_heads, kv_dtype,
-                         k_scale, v_scale, batch_slots, anc_mask, sm_scale, num_splits, n_q_seq)
+                         k_scale, v_scale, batch_slots, anc_mask, sm_scale, num_splits, n_q_seq,
+                         shared_prefix_pages)
         ws = verify_workspace_size(a)
         if buffers is None:
             B, _, Hq, d = q.shape

@@ -79,9 +79,11 @@ struct VerifyParams {
   float* out;
   float* lse;
   float* part;           // [n_wg][2][slot_floats] partial (O, max, sum) of split units
+  float* prefix_part;    // cascade: [batch][n_q][Hq][D + 2] (O, max, sum) over the shared prefix
   int* cum;              // [batch + 1] page prefix sums (written by workgroup 0)
   long slab_bytes;       // bytes of one (page, KV head) slab
   int batch, n_q, Hq, Hkv, G, rows, bt_stride, n_wg;
+  int pref;              // cascade: leading block-table pages shared by every sequence (0: none)
   int rg;                // row groups: waves that share a range, each taking rows_w rows
   int rows_w;            // rows per wave (rows when rg = 1)
   int min_range;         // fewest page-heads per workgroup range
@@ -253,7 +255,7 @@ __device__ void page_prefix(const VerifyParams& P, int* s_cum, int* s_tmp) {
   if (P.batch <= 64) {                         // one wave: a shuffle scan
     if (tid < 64) {
       int v = 0;
-      if (tid < P.batch) v = (P.seq_lens[P.batch_slots ? P.batch_slots[tid] : tid] + 15) >> 4;
+      if (tid < P.batch) v = max(0, ((P.seq_lens[P.batch_slots ? P.batch_slots[tid] : tid] + 15) >> 4) - P.pref);
       int x = v;
       for (int off = 1; off < 64; off <<= 1) {
         const int y = __shfl_up(x, off, 64);
@@ -270,7 +272,7 @@ __device__ void page_prefix(const VerifyParams& P, int* s_cum, int* s_tmp) {
   int local = 0;
   for (int b = b0; b < b1; ++b) {
     const int row = P.batch_slots ? P.batch_slots[b] : b;
-    local += (P.seq_lens[row] + 15) >> 4;
+    local += max(0, ((P.seq_lens[row] + 15) >> 4) - P.pref);
   }
   s_tmp[tid] = local;
   __syncthreads();
@@ -284,7 +286,7 @@ __device__ void page_prefix(const VerifyParams& P, int* s_cum, int* s_tmp) {
   for (int b = b0; b < b1; ++b) {
     s_cum[b] = run;
     const int row = P.batch_slots ? P.batch_slots[b] : b;
-    run += (P.seq_lens[row] + 15) >> 4;
+    run += max(0, ((P.seq_lens[row] + 15) >> 4) - P.pref);
   }
   if (tid == kThreads - 1) s_cum[P.batch] = s_tmp[tid];
   __syncthreads();
@@ -382,7 +384,7 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
     seq_info(c);
   };
   auto bt_rsrc = [&](const Cursor& c) {
-    return scalar_rsrc(P.block_table + long(c.row) * P.bt_stride, unsigned(c.np) * 4u);
+    return scalar_rsrc(P.block_table + long(c.row) * P.bt_stride + P.pref, unsigned(c.np) * 4u);
   };
 
   // ---- loads ---------------------------------------------------------------
@@ -523,9 +525,21 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
       l += __shfl_xor(l, 32, 64);
       const int rl = nt * 16 + m16, r = row0 + rl;
       if (local_ok(nt) && r / P.G < u_nq) {       // rows of slots past the sequence's count: not written
-        const float inv = full ? 1.0f / l : 1.0f;
         const int i = r / P.G, h = u_g * P.G + r % P.G;
         const long oi = long(u_b * P.n_q + i) * P.Hq + h;
+        // cascade: a unit finished here absorbs the shared prefix's partial
+        // (O, max, sum) of its row, written by the prefix pass
+        float sa = 1.0f, sb = 0.0f, m_out = m_run[nt];
+        const float* pp = nullptr;
+        if (!FP8 && full && P.pref > 0) {
+          pp = P.prefix_part + oi * (D + 2);
+          const float mp = pp[D], lp = pp[D + 1];
+          m_out = fmaxf(m_run[nt], mp);
+          sa = exp2_fast(m_run[nt] - m_out);
+          sb = exp2_fast(mp - m_out);
+          l = l * sa + lp * sb;
+        }
+        const float inv = full ? 1.0f / l : 1.0f;
         float* dst = full ? P.out + oi * D : part + long(rl) * D;
         if (FP8) {
 #pragma unroll
@@ -537,6 +551,19 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
                   make_float4(acc[4 * c][nt][e] * inv, acc[4 * c + 1][nt][e] * inv,
                               acc[4 * c + 2][nt][e] * inv, acc[4 * c + 3][nt][e] * inv);
             }
+        } else if (pp) {
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c) {
+            const int ch = c * 32 + 8 * jg;
+            const float4 p0 = *reinterpret_cast<const float4*>(pp + ch);
+            const float4 p1 = *reinterpret_cast<const float4*>(pp + ch + 4);
+            *reinterpret_cast<float4*>(dst + ch) =
+                make_float4((acc[2 * c][nt][0] * sa + p0.x * sb) * inv, (acc[2 * c + 1][nt][0] * sa + p0.y * sb) * inv,
+                            (acc[2 * c][nt][1] * sa + p0.z * sb) * inv, (acc[2 * c + 1][nt][1] * sa + p0.w * sb) * inv);
+            *reinterpret_cast<float4*>(dst + ch + 4) =
+                make_float4((acc[2 * c][nt][2] * sa + p1.x * sb) * inv, (acc[2 * c + 1][nt][2] * sa + p1.y * sb) * inv,
+                            (acc[2 * c][nt][3] * sa + p1.z * sb) * inv, (acc[2 * c + 1][nt][3] * sa + p1.w * sb) * inv);
+          }
         } else {
 #pragma unroll
           for (int c = 0; c < D / 32; ++c) {
@@ -551,7 +578,7 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
         }
         if (jg == 0) {
           if (full) {
-            if (P.lse) P.lse[oi] = (m_run[nt] + __log2f(l)) * kLn2;
+            if (P.lse) P.lse[oi] = (m_out + __log2f(l)) * kLn2;
           } else {
             part[long(P.rows_w) * D + rl] = m_run[nt];
             part[long(P.rows_w) * D + P.rows_w + rl] = l;
@@ -567,7 +594,7 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
   // to bf16 once (relative error <= 2^-9 per weight).
   constexpr bool kSplitP = !FP8;
   auto compute_page = [&](Regs& R, const PageMeta& M) {
-    const int tok0 = M.page * 16;
+    const int tok0 = (M.page + P.pref) * 16;       // positions past the shared prefix (cascade)
     const int L = (M.n & kLenMask) - (M.n >> kNqShift);
     // scores S^T (lane: row 16nt+m16, tokens tok0 + 4jg .. +3)
     float kx = 1.0f;                             // MX: this lane's K scale (its token, its tile)
@@ -793,7 +820,7 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
           u_b = mb;
           u_g = mg;
           u_first = M.page;
-          u_np = ((M.n & kLenMask) + 15) >> 4;
+          u_np = (((M.n & kLenMask) + 15) >> 4) - P.pref;
           u_nq = M.n >> kNqShift;
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
@@ -821,60 +848,203 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void verify_merge_kernel(VerifyParams P) {
   const int b = blockIdx.x / P.Hkv, g = blockIdx.x % P.Hkv;
   const int* __restrict__ cum = P.cum;
-  const long W = long(P.Hkv) * cum[P.batch];
-  if (W == 0) return;
-  const int np = cum[b + 1] - cum[b];
-  if (np == 0) return;
-  const int n_rng = used_ranges(P, W);
-  const long u0 = long(P.Hkv) * cum[b] + long(g) * np, u1 = u0 + np;
-  const int wf = owner_of(u0, W, n_rng), wl = owner_of(u1 - 1, W, n_rng);
-  if (wf == wl) return;                         // finished in place
   const int R = P.rows;
   const int x = blockIdx.y * kThreads + threadIdx.x;
   if (x >= R * (D / 4)) return;
   const int r = x / (D / 4), c4 = x % (D / 4);
   const int nq_b = P.nq_seq ? min(max(P.nq_seq[b], 1), P.n_q) : P.n_q;
   if (r / P.G >= nq_b) return;
-  // row r is row rl of row group rgi, held by wave (range * rg + rgi)
-  const int rgi = r / P.rows_w, rl = r % P.rows_w, RW = P.rows_w;
-  const long sf = slot_floats(RW, D);
-  // the first range's piece is its second slot when the range began in an
-  // earlier unit; for the others the unit is their first
-  const long first_base = (2L * (long(wf) * P.rg + rgi) + (range_starts_at(wf, W, n_rng, u0) ? 0 : 1)) * sf;
-  const float* __restrict__ part = P.part;
-  constexpr int KB = 8;
-  float M = kNegInf, Ls = 0.0f;
-  float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int w0 = wf; w0 <= wl; w0 += KB) {
-    float mk[KB], lk[KB];
-    float4 v[KB];
-#pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      const int w = min(w0 + u, wl);
-      const long base = w == wf ? first_base : 2L * (long(w) * P.rg + rgi) * sf;
-      mk[u] = part[base + long(RW) * D + rl];
-      lk[u] = part[base + long(RW) * D + RW + rl];
-      v[u] = *reinterpret_cast<const float4*>(part + base + long(rl) * D + 4 * c4);
-    }
-#pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      if (w0 + u > wl) break;
-      const float mn = fmaxf(M, mk[u]);
-      const float ref = mn == kNegInf ? 0.0f : mn;
-      const float a = exp2_fast(M - ref), c = exp2_fast(mk[u] - ref);
-      Ls = Ls * a + lk[u] * c;
-      o.x = o.x * a + v[u].x * c;
-      o.y = o.y * a + v[u].y * c;
-      o.z = o.z * a + v[u].z * c;
-      o.w = o.w * a + v[u].w * c;
-      M = mn;
-    }
-  }
-  const float inv = 1.0f / Ls;
   const int i = r / P.G, h = g * P.G + r % P.G;
   const long oi = long(b * P.n_q + i) * P.Hq + h;
+  // cascade: the shared prefix's partial is the first piece of every row
+  float M = kNegInf, Ls = 0.0f;
+  float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (P.pref > 0) {
+    const float* pp = P.prefix_part + oi * (D + 2);
+    M = pp[D];
+    Ls = pp[D + 1];
+    o = *reinterpret_cast<const float4*>(pp + 4 * c4);
+  }
+  const long W = long(P.Hkv) * cum[P.batch];
+  const int np = cum[b + 1] - cum[b];
+  bool merged = P.pref > 0 && np == 0;           // no positions past the prefix: the prefix alone
+  if (np > 0) {
+    const int n_rng = used_ranges(P, W);
+    const long u0 = long(P.Hkv) * cum[b] + long(g) * np, u1 = u0 + np;
+    const int wf = owner_of(u0, W, n_rng), wl = owner_of(u1 - 1, W, n_rng);
+    if (wf == wl) return;                         // finished in place
+    merged = true;
+    // row r is row rl of row group rgi, held by wave (range * rg + rgi)
+    const int rgi = r / P.rows_w, rl = r % P.rows_w, RW = P.rows_w;
+    const long sf = slot_floats(RW, D);
+    // the first range's piece is its second slot when the range began in an
+    // earlier unit; for the others the unit is their first
+    const long first_base = (2L * (long(wf) * P.rg + rgi) + (range_starts_at(wf, W, n_rng, u0) ? 0 : 1)) * sf;
+    const float* __restrict__ part = P.part;
+    constexpr int KB = 8;
+    for (int w0 = wf; w0 <= wl; w0 += KB) {
+      float mk[KB], lk[KB];
+      float4 v[KB];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int w = min(w0 + u, wl);
+        const long base = w == wf ? first_base : 2L * (long(w) * P.rg + rgi) * sf;
+        mk[u] = part[base + long(RW) * D + rl];
+        lk[u] = part[base + long(RW) * D + RW + rl];
+        v[u] = *reinterpret_cast<const float4*>(part + base + long(rl) * D + 4 * c4);
+      }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        if (w0 + u > wl) break;
+        const float mn = fmaxf(M, mk[u]);
+        const float ref = mn == kNegInf ? 0.0f : mn;
+        const float a = exp2_fast(M - ref), c = exp2_fast(mk[u] - ref);
+        Ls = Ls * a + lk[u] * c;
+        o.x = o.x * a + v[u].x * c;
+        o.y = o.y * a + v[u].y * c;
+        o.z = o.z * a + v[u].z * c;
+        o.w = o.w * a + v[u].w * c;
+        M = mn;
+      }
+    }
+  }
+  if (!merged) return;
+  const float inv = 1.0f / Ls;
   *reinterpret_cast<float4*>(P.out + oi * D + 4 * c4) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
   if (c4 == 0 && P.lse) P.lse[oi] = (M + __log2f(Ls)) * kLn2;
+}
+
+// Shared-prefix pass of the cascade (bf16 KV): the first P.pref pages are the
+// same physical pages for every sequence of the call, and every query sees
+// all of their tokens, so they are attended once for all sequences: a wave
+// takes 32 query rows of one KV head from the flattened (sequence, slot, head)
+// rows (any mix of sequences), streams the prefix pages once (they stay in
+// L2 for the other waves of the head) and writes unnormalised
+// (O, max, sum) per row for the streaming kernel or the merge to absorb.
+// Same tiled layout, MFMA orientation and split-P arithmetic as the
+// streaming kernel, without masks.
+template <int D>
+__global__ __launch_bounds__(kThreads) void verify_prefix_kernel(VerifyParams P) {
+  constexpr int NT = 2, KS = D / 32, DT = D / 16, VL = D / 32;
+  const int g = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int m16 = lane & 15, jg = lane >> 4;
+  const unsigned lane_off = unsigned(m16 * 64 + jg * 16);
+  const int rows_seq = P.n_q * P.G;
+  const long R = long(P.batch) * rows_seq;
+  const long r0 = (long(blockIdx.y) * kWaves + wave) * 32;
+  if (r0 >= R) return;
+  const int row_b0 = P.batch_slots ? P.batch_slots[0] : 0;
+  const int* bt = P.block_table + long(row_b0) * P.bt_stride;
+  // whole pages of the first sequence only (its table has no other entries)
+  const int n_pref = min(P.pref, P.seq_lens[row_b0] >> 4);
+  u32x4 qf[NT][KS];
+  long oi[NT];
+  bool ok[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const long r = r0 + nt * 16 + m16;
+    const long rr = r < R ? r : r0;
+    const int b = int(rr / rows_seq), rem = int(rr % rows_seq);
+    const int i = rem / P.G, h = g * P.G + rem % P.G;
+    const int nq_b = P.nq_seq ? min(max(P.nq_seq[b], 1), P.n_q) : P.n_q;
+    ok[nt] = r < R && i < nq_b;
+    oi[nt] = long(b * P.n_q + i) * P.Hq + h;
+    const unsigned short* qp = static_cast<const unsigned short*>(P.q) + oi[nt] * D + (D / 4) * jg;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[nt][s] = load16(qp + 8 * s);
+  }
+  float m_run[NT], l_run[NT];
+  f32x4 acc[DT][NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m_run[nt] = kNegInf;
+    l_run[nt] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt][nt] = f32x4{0, 0, 0, 0};
+  }
+  const long page_stride = long(P.Hkv) * P.slab_bytes;
+  u32x4 kc[KS], vc[VL], kn[KS], vn[VL];
+  auto load = [&](u32x4 (&k)[KS], u32x4 (&v)[VL], int p) {
+    const int id = p < n_pref ? bt[p] : bt[0];
+    const char* kb = P.k_pages + long(id) * page_stride + long(g) * P.slab_bytes;
+    const char* vb = P.v_pages + long(id) * page_stride + long(g) * P.slab_bytes;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) k[s] = load16(kb + lane_off + s * 1024);
+#pragma unroll
+    for (int c = 0; c < VL; ++c) v[c] = load16(vb + lane_off + c * 1024);
+  };
+  if (n_pref > 0) load(kc, vc, 0);
+  for (int p = 0; p < n_pref; ++p) {
+    if (p + 1 < n_pref) load(kn, vn, p + 1);   // next page in flight while this one is computed
+    f32x4 sc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 a = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) a = mfma_bf16(kc[s], qf[nt][s], a);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[nt][e] = a[e] * P.scale_log2;
+    }
+    unsigned ph[NT][2], pl[NT][2];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float mx = row_max4(fmaxf(fmaxf(sc[nt][0], sc[nt][1]), fmaxf(sc[nt][2], sc[nt][3])));
+      const bool grow = mx > m_run[nt] + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mx : m_run[nt];
+        const float alpha = grow ? exp2_fast(m_run[nt] - m_new) : 1.0f;
+        l_run[nt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt][nt] *= alpha;
+        m_run[nt] = m_new;
+      }
+      float pv[4], rv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pv[e] = exp2_fast(sc[nt][e] - m_run[nt]);
+      l_run[nt] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rv[e] = pv[e] - __uint_as_float(__float_as_uint(pv[e]) & 0xFFFF0000u);
+      ph[nt][0] = pack_hi16(pv[0], pv[1]);
+      ph[nt][1] = pack_hi16(pv[2], pv[3]);
+      pl[nt][0] = pack_rne_bf16(rv[0], rv[1]);
+      pl[nt][1] = pack_rne_bf16(rv[2], rv[3]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int w = (dt & 1) * 2;
+      const unsigned v0 = vc[dt >> 1][w], v1 = vc[dt >> 1][w + 1];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[dt][nt] = mfma_bf16_k16(v0, v1, ph[nt][0], ph[nt][1], acc[dt][nt]);
+        acc[dt][nt] = mfma_bf16_k16(v0, v1, pl[nt][0], pl[nt][1], acc[dt][nt]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kc[s] = kn[s];
+#pragma unroll
+    for (int c = 0; c < VL; ++c) vc[c] = vn[c];
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float l = l_run[nt];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (!ok[nt]) continue;
+    float* dst = P.prefix_part + oi[nt] * (D + 2);
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      const int ch = c * 32 + 8 * jg;
+      *reinterpret_cast<float4*>(dst + ch) =
+          make_float4(acc[2 * c][nt][0], acc[2 * c + 1][nt][0], acc[2 * c][nt][1], acc[2 * c + 1][nt][1]);
+      *reinterpret_cast<float4*>(dst + ch + 4) =
+          make_float4(acc[2 * c][nt][2], acc[2 * c + 1][nt][2], acc[2 * c][nt][3], acc[2 * c + 1][nt][3]);
+    }
+    if (jg == 0) {
+      dst[D] = m_run[nt];
+      dst[D + 1] = l;
+    }
+  }
 }
 
 // Dynamic LDS of the streaming kernel: page prefix sums and scan scratch,
@@ -999,7 +1169,7 @@ __global__ __launch_bounds__(128) void verify_f32_kernel(VerifyParams P) {
 struct Plan {
   int D, NT, rows, n_wg, rg, rows_w;
   bool fp8, mx, tree, f32;
-  size_t cum_bytes, part_bytes;
+  size_t cum_bytes, part_bytes, prefix_bytes;
 };
 
 pkv_status check_args(const pkv_verify_args* a, Plan* pl) {
@@ -1014,6 +1184,9 @@ pkv_status check_args(const pkv_verify_args* a, Plan* pl) {
   if (a->block_table_stride < 1) return fail(PKV_ERR_INVALID_ARG, "block_table_stride must be >= 1");
   if (!a->q || !a->k_pages || !a->v_pages || !a->block_table || !a->seq_lens)
     return fail(PKV_ERR_INVALID_ARG, "null device pointer");
+  if (a->shared_prefix_pages < 0) return fail(PKV_ERR_INVALID_ARG, "shared_prefix_pages must be >= 0");
+  if (a->shared_prefix_pages > 0 && a->kv_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "the shared-prefix pass supports bf16 KV");
   if (a->num_splits < 0 || a->num_splits > 1024)
     return fail(PKV_ERR_INVALID_ARG, "num_splits must be in [0, 1024]");
   const int G = a->num_q_heads / a->num_kv_heads;
@@ -1137,6 +1310,9 @@ pkv_status make_plan(const pkv_verify_args* a, Plan* pl) {
   if (st != PKV_OK) return st;
   pl->cum_bytes = 0;
   pl->part_bytes = 0;
+  pl->prefix_bytes = a->shared_prefix_pages > 0
+                         ? size_t(a->batch) * a->n_q * a->num_q_heads * (a->head_dim + 2) * sizeof(float)
+                         : 0;
   pl->n_wg = 0;
   if (!pl->f32) {
     int n = a->num_splits;
@@ -1153,7 +1329,7 @@ pkv_status make_plan(const pkv_verify_args* a, Plan* pl) {
     }
     pl->n_wg = n;
     pl->cum_bytes = ((size_t(a->batch) + 1) * sizeof(int) + 255) & ~size_t(255);
-    pl->part_bytes = size_t(n) * kWaves * 2 * size_t(pl->rows_w) * (pl->D + 2) * sizeof(float);
+    pl->part_bytes = (size_t(n) * kWaves * 2 * size_t(pl->rows_w) * (pl->D + 2) * sizeof(float) + 255) & ~size_t(255);
   }
   return PKV_OK;
 }
@@ -1233,7 +1409,7 @@ extern "C" pkv_status spec_verify_workspace_size(const pkv_verify_args* args, si
   Plan pl;
   pkv_status st = make_plan(args, &pl);
   if (st != PKV_OK) return st;
-  *bytes_out = pl.cum_bytes + pl.part_bytes;
+  *bytes_out = pl.cum_bytes + pl.part_bytes + pl.prefix_bytes;
   return PKV_OK;
 }
 
@@ -1242,7 +1418,7 @@ extern "C" pkv_status spec_verify_attention(const pkv_verify_args* a, void* stre
   pkv_status st = make_plan(a, &pl);
   if (st != PKV_OK) return st;
   if (!a->out) return fail(PKV_ERR_INVALID_ARG, "null output pointer");
-  const size_t need = pl.cum_bytes + pl.part_bytes;
+  const size_t need = pl.cum_bytes + pl.part_bytes + pl.prefix_bytes;
   if (need > 0 && (!a->workspace || a->workspace_bytes < need))
     return fail(PKV_ERR_WORKSPACE, "workspace smaller than spec_verify_workspace_size");
   VerifyParams p{};
@@ -1260,6 +1436,10 @@ extern "C" pkv_status spec_verify_attention(const pkv_verify_args* a, void* stre
   p.lse = a->lse;
   p.cum = static_cast<int*>(a->workspace);
   p.part = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + pl.cum_bytes);
+  p.prefix_part = pl.prefix_bytes ? reinterpret_cast<float*>(static_cast<char*>(a->workspace) + pl.cum_bytes +
+                                                             pl.part_bytes)
+                                  : nullptr;
+  p.pref = a->shared_prefix_pages;
   p.min_range = a->num_splits == 0 ? 8 : 1;
   p.slab_bytes = pkv_page_bytes(a->kv_dtype, a->page_size, a->head_dim);
   p.batch = a->batch;
@@ -1283,10 +1463,18 @@ extern "C" pkv_status spec_verify_attention(const pkv_verify_args* a, void* stre
     e = hipGetLastError();
   } else if (pl.mx) {
     e = pl.D == 64 ? dispatch_mx<64>(p, pl.NT, pl.tree, s) : dispatch_mx<128>(p, pl.NT, pl.tree, s);
-  } else if (pl.D == 64) {
-    e = dispatch_nt<64>(p, pl.NT, pl.fp8, pl.tree, s);
   } else {
-    e = dispatch_nt<128>(p, pl.NT, pl.fp8, pl.tree, s);
+    e = hipSuccess;
+    if (p.pref > 0) {
+      // cascade: the shared prefix once for all sequences, before the tails
+      const long rows = long(p.batch) * p.n_q * p.G;
+      const dim3 grid(p.Hkv, unsigned((rows + 32 * kWaves - 1) / (32 * kWaves)));
+      if (pl.D == 64) hipLaunchKernelGGL(verify_prefix_kernel<64>, grid, dim3(kThreads), 0, s, p);
+      else hipLaunchKernelGGL(verify_prefix_kernel<128>, grid, dim3(kThreads), 0, s, p);
+      e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = pl.D == 64 ? dispatch_nt<64>(p, pl.NT, pl.fp8, pl.tree, s)
+                                        : dispatch_nt<128>(p, pl.NT, pl.fp8, pl.tree, s);
   }
   if (e != hipSuccess) return fail(PKV_ERR_DEVICE, std::string("verify launch: ") + hipGetErrorString(e));
   return PKV_OK;

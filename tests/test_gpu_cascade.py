@@ -1,0 +1,81 @@
+"""Cascade attention over a shared prefix (shared_prefix_pages): the prefix
+pages common to every sequence are attended once for all sequences and merged
+with each sequence's own pages.  Checked against the oracle (which gathers
+every sequence's full K/V and knows nothing of the sharing), for the split
+counts that put units in place and across workers, at full size, with
+per-sequence draft counts, and against the plain call."""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_speculative_amd import PkvError
+from paged_kv_speculative_amd import workloads as wl
+import harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("splits", [0, 1, 7, 64])
+def test_cascade_matches_oracle(splits):
+    w = wl.make(5, small=True)
+    g = H.GpuSide(w)
+    pref = w.prefix_len // 16
+    O, L = g.verify(shared_prefix_pages=pref, num_splits=splits)
+    O_ref, L_ref = H.oracle_verify(w, range(w.batch))
+    H.compare(O.cpu().numpy(), L.cpu().numpy(), O_ref, L_ref, H.TOL["bf16"])
+
+
+def test_cascade_equals_plain_call():
+    w = wl.make(5, small=True, batch=9)
+    g = H.GpuSide(w)
+    O1, L1 = (x.clone() for x in g.verify())
+    O2, L2 = g.verify(shared_prefix_pages=w.prefix_len // 16)
+    O1, L1, O2, L2 = (x.cpu().numpy() for x in (O1, L1, O2, L2))
+    rms = float(np.sqrt(np.mean(O1.astype(np.float64) ** 2)))
+    assert np.max(np.abs(O1 - O2)) <= 1e-4 * rms and np.max(np.abs(L1 - L2)) <= 1e-4
+    # a shorter shared part (the first page only) is a valid cascade as well
+    O3, L3 = g.verify(shared_prefix_pages=1)
+    assert np.max(np.abs(O1 - O3.cpu().numpy())) <= 1e-4 * rms
+
+
+def test_cascade_full_size_sampled():
+    w = wl.make(5)
+    print(f"cascade full: B={w.batch} prefix={w.prefix_len}", flush=True)
+    g = H.GpuSide(w)
+    O, L = g.verify(shared_prefix_pages=w.prefix_len // 16)
+    O, L = O.cpu().numpy(), L.cpu().numpy()
+    rng = np.random.default_rng(5)
+    sample = sorted(set([0, w.batch - 1, int(np.argmax(w.seq_lens))] + list(rng.choice(w.batch, 2, replace=False))))
+    O_ref, L_ref = H.oracle_verify(w, sample)
+    H.compare(O[sample], L[sample], O_ref, L_ref, H.TOL["bf16"])
+
+
+def test_cascade_with_per_sequence_counts():
+    """Per-sequence slot counts with the cascade: only slots i < n_b are
+    computed and written."""
+    w = wl.make(5, small=True)
+    g = H.GpuSide(w)
+    nq = torch.tensor([5, 1, 3, 5, 2, 4][:w.batch], dtype=torch.int32, device="cuda")
+    from paged_kv_speculative_amd import VerifyBuffers
+    B, n_q, Hq, d = g.q.shape
+    buf = VerifyBuffers(B, n_q, Hq, d, 1 << 27, "cuda")
+    buf.out.fill_(7.0)
+    O, L = g.verify(shared_prefix_pages=w.prefix_len // 16, n_q_seq=nq, buffers=buf)
+    # with n_b slots the last n_b tokens are the verification slots and the
+    # tokens before them are context: the oracle run per sequence with n_b
+    from oracle import attention as oa
+    qf = w.q_f32().astype(np.float64)
+    O, L = O.cpu().numpy(), L.cpu().numpy()
+    for b in range(B):
+        n_b = int(nq[b])
+        K, V = H.oracle_sequence_kv(w, b)
+        Or, Lr = oa.verify_attention(qf[b:b + 1, :n_b], [K], [V], n_b, None, float(w.sm_scale))
+        H.compare(O[b:b + 1, :n_b], L[b:b + 1, :n_b], Or, Lr, H.TOL["bf16"])
+        assert np.all(O[b, n_b:] == 7.0)
+
+
+def test_cascade_rejects_fp8():
+    w = wl.make(4, small=True, batch=2)
+    g = H.GpuSide(w)
+    with pytest.raises(PkvError):
+        g.verify(shared_prefix_pages=1)
