@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--kv-dtype", choices=["bf16", "fp8", "fp8mx"], default=None,
                     help="override the workload's KV type (fp8mx: FP8 with a power-of-two scale per "
                          "64 channels of each token)")
+    ap.add_argument("--no-cascade", action="store_true",
+                    help="attend a shared prefix once per sequence instead of once for all sequences")
     ap.add_argument("--graph", action="store_true",
                     help="replay verification and acceptance from HIP graphs (measured slower than "
                          "eager launches on MI355X: 177 vs 168 us per step)")
@@ -178,6 +180,14 @@ class Instance:
         self.graph_v = self.graph_a = self.accept_graph_call = None
 
 
+def cascade_pages(args, w):
+    """Whole pages of the shared prefix attended once for all sequences
+    (bf16 KV; off with --no-cascade)."""
+    if args.no_cascade or not w.prefix_len or w.kv_dtype != "bf16":
+        return 0
+    return w.prefix_len // 16
+
+
 def run_gpu(args, w, torch, api):
     B, nq, gam = w.batch, w.n_q, w.gamma
     total_steps = args.steps + args.warmup
@@ -186,7 +196,8 @@ def run_gpu(args, w, torch, api):
     R = min(R, 8)
     insts = [Instance(w, -(-total_steps // R) + 1, torch, api, r) for r in range(R)]
     for I in insts:
-        I.verify = I.pool.prepare_verify(I.q, nq, anc_mask=I.anc, sm_scale=w.sm_scale)
+        I.verify = I.pool.prepare_verify(I.q, nq, anc_mask=I.anc, sm_scale=w.sm_scale,
+                                         shared_prefix_pages=cascade_pages(args, w))
         if I.accept:
             I.accept_call = api.PreparedAccept(I.T, I.D, I.x, seed=12345)
             if args.graph:       # the captured launch reads its step counter from device memory
@@ -384,6 +395,7 @@ def main():
                         f"n_q {nq} ({'tree' if w.tree_parents else 'chain'})"
                         + (f", acceptance over vocab {w.accept_vocab}" if w.accept_vocab else ""),
             "batch": B, "n_q": nq, "gamma": w.gamma, "instances": r["instances"],
+            "shared_prefix_pages": cascade_pages(args, w),
         },
         "verify_attn": {
             "kv_gbps": achieved,

@@ -916,41 +916,42 @@ __global__ __launch_bounds__(kThreads) void verify_merge_kernel(VerifyParams P) 
 
 // Shared-prefix pass of the cascade (bf16 KV): the first P.pref pages are the
 // same physical pages for every sequence of the call, and every query sees
-// all of their tokens, so they are attended once for all sequences: a wave
-// takes 32 query rows of one KV head from the flattened (sequence, slot, head)
-// rows (any mix of sequences), streams the prefix pages once (they stay in
-// L2 for the other waves of the head) and writes unnormalised
-// (O, max, sum) per row for the streaming kernel or the merge to absorb.
-// Same tiled layout, MFMA orientation and split-P arithmetic as the
-// streaming kernel, without masks.
+// all of their tokens, so they are attended once for all sequences.  A
+// workgroup takes 32 query rows of one KV head from the flattened (sequence,
+// slot, head) rows (any mix of sequences); its four waves take a quarter of
+// the prefix pages each (the pages stay in L2 for the other workgroups of
+// the head) and combine their (max, sum, O) through LDS into one
+// unnormalised (O, max, sum) per row, which the streaming kernel or the
+// merge absorbs.  Same tiled layout, MFMA orientation and split-P arithmetic
+// as the streaming kernel, without masks.
+constexpr int kPrefixRows = 32;
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void verify_prefix_kernel(VerifyParams P) {
   constexpr int NT = 2, KS = D / 32, DT = D / 16, VL = D / 32;
+  constexpr int RS = D + 4;                      // LDS floats per (wave, row): O, max, sum (16-byte rows)
+  __shared__ float s_part[kWaves][kPrefixRows][RS];
   const int g = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int m16 = lane & 15, jg = lane >> 4;
   const unsigned lane_off = unsigned(m16 * 64 + jg * 16);
   const int rows_seq = P.n_q * P.G;
   const long R = long(P.batch) * rows_seq;
-  const long r0 = (long(blockIdx.y) * kWaves + wave) * 32;
-  if (r0 >= R) return;
+  const long r0 = long(blockIdx.y) * kPrefixRows;
   const int row_b0 = P.batch_slots ? P.batch_slots[0] : 0;
   const int* bt = P.block_table + long(row_b0) * P.bt_stride;
   // whole pages of the first sequence only (its table has no other entries)
   const int n_pref = min(P.pref, P.seq_lens[row_b0] >> 4);
+  const int p_lo = int(long(n_pref) * wave / kWaves), p_hi = int(long(n_pref) * (wave + 1) / kWaves);
   u32x4 qf[NT][KS];
-  long oi[NT];
-  bool ok[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const long r = r0 + nt * 16 + m16;
     const long rr = r < R ? r : r0;
     const int b = int(rr / rows_seq), rem = int(rr % rows_seq);
     const int i = rem / P.G, h = g * P.G + rem % P.G;
-    const int nq_b = P.nq_seq ? min(max(P.nq_seq[b], 1), P.n_q) : P.n_q;
-    ok[nt] = r < R && i < nq_b;
-    oi[nt] = long(b * P.n_q + i) * P.Hq + h;
-    const unsigned short* qp = static_cast<const unsigned short*>(P.q) + oi[nt] * D + (D / 4) * jg;
+    const long oi = long(b * P.n_q + i) * P.Hq + h;
+    const unsigned short* qp = static_cast<const unsigned short*>(P.q) + oi * D + (D / 4) * jg;
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[nt][s] = load16(qp + 8 * s);
   }
@@ -966,7 +967,7 @@ __global__ __launch_bounds__(kThreads) void verify_prefix_kernel(VerifyParams P)
   const long page_stride = long(P.Hkv) * P.slab_bytes;
   u32x4 kc[KS], vc[VL], kn[KS], vn[VL];
   auto load = [&](u32x4 (&k)[KS], u32x4 (&v)[VL], int p) {
-    const int id = p < n_pref ? bt[p] : bt[0];
+    const int id = bt[p];
     const char* kb = P.k_pages + long(id) * page_stride + long(g) * P.slab_bytes;
     const char* vb = P.v_pages + long(id) * page_stride + long(g) * P.slab_bytes;
 #pragma unroll
@@ -974,9 +975,9 @@ __global__ __launch_bounds__(kThreads) void verify_prefix_kernel(VerifyParams P)
 #pragma unroll
     for (int c = 0; c < VL; ++c) v[c] = load16(vb + lane_off + c * 1024);
   };
-  if (n_pref > 0) load(kc, vc, 0);
-  for (int p = 0; p < n_pref; ++p) {
-    if (p + 1 < n_pref) load(kn, vn, p + 1);   // next page in flight while this one is computed
+  if (p_lo < p_hi) load(kc, vc, p_lo);
+  for (int p = p_lo; p < p_hi; ++p) {
+    if (p + 1 < p_hi) load(kn, vn, p + 1);     // next page in flight while this one is computed
     f32x4 sc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -1025,13 +1026,13 @@ __global__ __launch_bounds__(kThreads) void verify_prefix_kernel(VerifyParams P)
 #pragma unroll
     for (int c = 0; c < VL; ++c) vc[c] = vn[c];
   }
+  // this wave's (O, max, sum) per row into LDS
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float l = l_run[nt];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    if (!ok[nt]) continue;
-    float* dst = P.prefix_part + oi[nt] * (D + 2);
+    float* dst = s_part[wave][nt * 16 + m16];
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
       const int ch = c * 32 + 8 * jg;
@@ -1044,6 +1045,42 @@ __global__ __launch_bounds__(kThreads) void verify_prefix_kernel(VerifyParams P)
       dst[D] = m_run[nt];
       dst[D + 1] = l;
     }
+  }
+  __syncthreads();
+  // the four waves' pieces combined: thread t takes row t / 8 and 16 channels
+  const int row = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * (D / 8);
+  const long r = r0 + row;
+  if (r >= R) return;
+  const int b = int(r / rows_seq), rem = int(r % rows_seq);
+  const int i = rem / P.G, h = g * P.G + rem % P.G;
+  const int nq_b = P.nq_seq ? min(max(P.nq_seq[b], 1), P.n_q) : P.n_q;
+  if (i >= nq_b) return;
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_part[w][row][D]);
+  const float ref = M == kNegInf ? 0.0f : M;
+  float sc[kWaves], Ls = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    sc[w] = exp2_fast(s_part[w][row][D] - ref);
+    Ls += s_part[w][row][D + 1] * sc[w];
+  }
+  float* dst = P.prefix_part + (long(b * P.n_q + i) * P.Hq + h) * (D + 2);
+  for (int c = c0; c < c0 + D / 8; c += 4) {
+    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float4 v = *reinterpret_cast<const float4*>(&s_part[w][row][c]);
+      o.x += v.x * sc[w];
+      o.y += v.y * sc[w];
+      o.z += v.z * sc[w];
+      o.w += v.w * sc[w];
+    }
+    *reinterpret_cast<float4*>(dst + c) = o;
+  }
+  if ((threadIdx.x & 7) == 0) {
+    dst[D] = M;
+    dst[D + 1] = Ls;
   }
 }
 
@@ -1468,7 +1505,7 @@ extern "C" pkv_status spec_verify_attention(const pkv_verify_args* a, void* stre
     if (p.pref > 0) {
       // cascade: the shared prefix once for all sequences, before the tails
       const long rows = long(p.batch) * p.n_q * p.G;
-      const dim3 grid(p.Hkv, unsigned((rows + 32 * kWaves - 1) / (32 * kWaves)));
+      const dim3 grid(p.Hkv, unsigned((rows + kPrefixRows - 1) / kPrefixRows));
       if (pl.D == 64) hipLaunchKernelGGL(verify_prefix_kernel<64>, grid, dim3(kThreads), 0, s, p);
       else hipLaunchKernelGGL(verify_prefix_kernel<128>, grid, dim3(kThreads), 0, s, p);
       e = hipGetLastError();
