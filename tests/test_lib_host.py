@@ -251,3 +251,33 @@ def test_commit_path_errors_change_nothing():
     assert lp.table(0) == before
     lp.commit_path([0], [6], [[1, 2]])             # in place: no move, truncation only
     assert lp.table(0)[1] == 27
+
+
+def test_argument_checks_of_newer_fields():
+    """Host-side validation (no device work): FP8 tile pools, the cascade
+    and tree-acceptance shapes."""
+    lib = _lib.lib
+    assert lib.pkv_page_bytes(3, 16, 128) == 2048 and lib.pkv_page_bytes(3, 16, 64) == 1024
+    pool = Pool(32, 2, 128, "fp8mx", max_seqs=2, max_pages_per_seq=8)
+    pool.alloc(0)
+    pool.append([0], [40])
+    assert pool.table(0)[1] == 40
+    a = _lib.VerifyArgs()
+    a.batch, a.n_q, a.num_q_heads, a.num_kv_heads, a.head_dim, a.page_size = 2, 5, 8, 2, 128, 16
+    a.q_dtype, a.kv_dtype = _lib.BF16, _lib.FP8_E4M3
+    a.q = a.k_pages = a.v_pages = a.block_table = a.seq_lens = a.k_scale = a.v_scale = 16
+    a.block_table_stride = 8
+    n = C.c_size_t()
+    a.shared_prefix_pages = 1
+    assert lib.spec_verify_workspace_size(C.byref(a), C.byref(n)) == 5       # cascade needs bf16 KV
+    a.kv_dtype, a.shared_prefix_pages = _lib.BF16, -1
+    assert lib.spec_verify_workspace_size(C.byref(a), C.byref(n)) == 1
+    t = _lib.TreeAcceptArgs()
+    t.batch, t.n_nodes, t.max_children, t.vocab = 2, 16, 4, 1000
+    assert lib.spec_accept_tree_workspace_size(C.byref(t), C.byref(n)) == 0 and n.value > 0
+    for field, bad in (("n_nodes", 1), ("n_nodes", 65), ("max_children", 0), ("max_children", 16),
+                       ("vocab", 0)):
+        t2 = _lib.TreeAcceptArgs()
+        t2.batch, t2.n_nodes, t2.max_children, t2.vocab = 2, 16, 4, 1000
+        setattr(t2, field, bad)
+        assert lib.spec_accept_tree_workspace_size(C.byref(t2), C.byref(n)) == 1, field
