@@ -357,8 +357,8 @@ def cpu_baseline(w, budget_s):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the verification step shards by sequence or KV head with no exchange; see DESIGN.md)",
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(the verification step would shard by sequence or KV head with no exchange)",
               file=sys.stderr)
         sys.exit(2)
     import torch
