@@ -13,14 +13,14 @@
 //  * Work is the list of (sequence, KV head, page) triples in that order.  A
 //    fixed number of workgroups (what the GPU keeps resident) each take an
 //    equal contiguous range of it ("stream-K"), so long and short contexts
-//    balance exactly.  A range covers whole (sequence, KV head) units, which
-//    are finished in place, and at most two pieces of units, which are
-//    written as partial (max, sum, unnormalised O) and merged by a second
-//    kernel with a log-sum-exp combine.
+//    balance exactly.  Each wave is one worker with its own range (with more
+//    than 48 query rows per KV head, two waves take the same range, 32 rows
+//    each).  A range covers whole (sequence, KV head) units, which are
+//    finished in place, and at most two pieces of units, which are written
+//    as partial (max, sum, unnormalised O) and merged by a second kernel
+//    with a log-sum-exp combine.
 //  * One (sequence, KV head) unit serves all n_q * G query rows that read the
 //    same pages (G = Hq/Hkv): every KV byte is read once per call.
-//  * Four waves of a workgroup share a range's page pairs; each keeps its
-//    own online-softmax state and the four are combined through LDS.
 //  * A page of one KV head is one slab in a tiled layout (layout.h) so each
 //    16-byte load instruction of a wave reads one contiguous kilobyte and
 //    the lanes' registers are already MFMA operands: no LDS staging.
