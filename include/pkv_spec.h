@@ -98,7 +98,8 @@ typedef struct {
   int32_t page_size;          /* tokens per page; must be 16                     */
   int32_t num_kv_heads;       /* Hkv >= 1                                        */
   int32_t head_dim;           /* 64 or 128                                       */
-  pkv_dtype kv_dtype;         /* PKV_F32, PKV_BF16 or PKV_FP8_E4M3               */
+  pkv_dtype kv_dtype;         /* PKV_F32, PKV_BF16, PKV_FP8_E4M3 or
+                                 PKV_FP8_E4M3_MX64                               */
   int32_t max_seqs;           /* rows of the device block table (live sequences) */
   int32_t max_pages_per_seq;  /* columns of the device block table               */
   void* k_pages;              /* device [num_pages][Hkv][page_bytes]             */

@@ -12,7 +12,9 @@ position yields one more token (the "+1" of eq. eta).
 Readings where the pages are silent or disagree:
   * P and Q are plain softmaxes of the logits (temperature 1);
   * the acceptance test is u_i < min(1, P/Q) with u_i a counter-based uniform
-    (oracle.philox.accept_uniform);
+    (oracle.philox.accept_uniform); a draft token outside [0, V) is not a
+    token of the target's vocabulary, so P(x_i) = 0 and it is rejected at its
+    position (the same reading as for draft trees below);
   * on rejection at position k the token is drawn from the residual
     R(x) = max(0, P_k(x) - Q_k(x)) normalised, which is what makes the output
     follow the target distribution exactly (futurestack.online, section 2.1,
@@ -60,10 +62,13 @@ def accept_one(T, D, x, seed, step, b):
     margins = []
     k = gamma
     for i in range(gamma):
-        lp = log_softmax(T[i])
-        lq = log_softmax(D[i])
-        ratio = np.exp(lp[x[i]] - lq[x[i]])
-        a = min(1.0, ratio)
+        xi = int(x[i])
+        if 0 <= xi < V:
+            lp = log_softmax(T[i])
+            lq = log_softmax(D[i])
+            a = min(1.0, float(np.exp(lp[xi] - lq[xi])))
+        else:
+            a = 0.0             # a token outside the vocabulary has P = 0: always rejected
         u = philox.accept_uniform(seed, step, b, i)
         margins.append(abs(u - a))
         if not u < a:

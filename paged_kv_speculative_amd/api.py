@@ -214,10 +214,17 @@ def _verify_args(q, k_pages, v_pages, block_table, seq_lens, n_q, num_kv_heads, 
                  shared_prefix_pages=0):
     B, nq, Hq, d = q.shape
     assert nq == n_q and q.is_contiguous()
+    if q.dtype not in _TORCH_SRC:
+        raise TypeError(f"q must be float32 or bfloat16, not {q.dtype}")
+    for name, t in (("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table),
+                    ("seq_lens", seq_lens), ("k_scale", k_scale), ("v_scale", v_scale),
+                    ("batch_slots", batch_slots), ("anc_mask", anc_mask), ("n_q_seq", n_q_seq)):
+        if t is not None and t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}: all tensors must be on one device")
     a = VerifyArgs()
     a.batch, a.n_q, a.num_q_heads, a.num_kv_heads, a.head_dim = B, n_q, Hq, num_kv_heads, d
     a.page_size = PAGE_SIZE
-    a.q_dtype = F32 if q.dtype == torch.float32 else BF16
+    a.q_dtype = _TORCH_SRC[q.dtype]
     a.kv_dtype = DTYPES[kv_dtype]
     a.q, a.k_pages, a.v_pages = q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr()
     if k_scale is not None:
@@ -305,6 +312,9 @@ class PreparedVerify:
 def _accept_args(target_logits, draft_logits, draft_tokens, seed, step, gammas=None):
     B, g1, V = target_logits.shape
     assert draft_logits.shape == (B, g1 - 1, V) and draft_tokens.shape == (B, g1 - 1)
+    for name, t in (("draft_logits", draft_logits), ("draft_tokens", draft_tokens), ("gammas", gammas)):
+        if t is not None and t.device != target_logits.device:
+            raise ValueError(f"{name} is on {t.device}, target_logits on {target_logits.device}")
     assert target_logits.dtype == torch.float32 and draft_logits.dtype == torch.float32
     assert draft_tokens.dtype == torch.int32
     assert target_logits.is_contiguous() and draft_logits.is_contiguous() and draft_tokens.is_contiguous()

@@ -48,6 +48,16 @@
 
 namespace pkv {
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Scalar (SMEM) buffer load of one dword, bound to the LLVM intrinsic (clang
+// has no builtin for it; declared with external linkage so the binding is an
+// ordinary external declaration).  Block-table entries are read through the
+// scalar unit so that waiting for them never waits for the vector loads of
+// K/V in flight (vector-memory counters retire in order).
+__device__ int s_buffer_load_dword(i32x4 rsrc, int offset, int cachepolicy)
+    __asm("llvm.amdgcn.s.buffer.load.i32");
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -141,33 +151,25 @@ __device__ inline float e8m0_value(unsigned e) {
 
 __device__ inline u32x4 load16(const void* p) { return *static_cast<const u32x4*>(p); }
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
 // global -> LDS copies through the load path (global_load_lds): lane l's
 // 16 (or 4) bytes land at LDS address lds + 16 l (4 l).  Written as inline
 // assembly so that the compiler tracks nothing for them: as a builtin, every
 // later scalar load would wait for all vector memory operations (it treats
 // the copy as a store that may alias them).  The caller orders the LDS reads
-// of the data with an explicit vmcnt wait.
+// of the data with an explicit vmcnt wait.  The LDS base goes in through an
+// M0 operand ("{m0}"), so the compiler sets M0 itself and knows its value is
+// only read here.
 __device__ inline void copy16_to_lds(const void* src, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds) : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds) : "memory");
 }
 __device__ inline void copy4_to_lds(const void* src, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(src), "s"(lds) : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(src), "{m0}"(lds) : "memory");
 }
 // LDS address (offset in the workgroup's LDS) of a pointer into __shared__
 // memory: the low half of its flat address.
 __device__ inline unsigned lds_addr(const void* p) {
   return unsigned(reinterpret_cast<unsigned long long>(p));
 }
-
-// Scalar (SMEM) buffer load of one dword.  Block-table entries and FP8 scales
-// are read through the scalar unit so that waiting for them never waits for
-// the vector loads of K/V in flight (vector-memory counters retire in order).
-__device__ int s_buffer_load_dword(i32x4 rsrc, int offset, int cachepolicy)
-    __asm("llvm.amdgcn.s.buffer.load.i32");
 
 // Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format,
 // no swizzle): with stride 0, num_records counts bytes.
@@ -346,16 +348,17 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
   const long page_stride = long(P.Hkv) * P.slab_bytes;
   const i32x4 len_rsrc = scalar_rsrc(P.seq_lens, 0xFFFFFFFFu);
   const i32x4 slot_rsrc = scalar_rsrc(P.batch_slots, P.batch_slots ? unsigned(P.batch) * 4u : 0u);
-  // without per-sequence counts the buffer has no records and reads return 0
   const i32x4 nq_rsrc = scalar_rsrc(P.nq_seq, P.nq_seq ? unsigned(P.batch) * 4u : 0u);
 
   // ---- cursor helpers (all scalar) -----------------------------------------
   auto seq_info = [&](Cursor& c) {
     c.np = uni(s_cum[c.b + 1]) - uni(s_cum[c.b]);
     c.row = P.batch_slots ? s_buffer_load_dword(slot_rsrc, c.b * 4, 0) : c.b;
-    const int nq = s_buffer_load_dword(nq_rsrc, c.b * 4, 0);
-    c.n = s_buffer_load_dword(len_rsrc, c.row * 4, 0) |
-          ((nq > 0 ? min(nq, P.n_q) : P.n_q) << kNqShift);
+    // per-sequence counts are clamped to [1, n_q] (zero and negative counts
+    // give one slot, as in the merge kernel); without them every sequence
+    // has n_q
+    const int nq = P.nq_seq ? min(max(s_buffer_load_dword(nq_rsrc, c.b * 4, 0), 1), P.n_q) : P.n_q;
+    c.n = s_buffer_load_dword(len_rsrc, c.row * 4, 0) | (nq << kNqShift);
   };
   auto locate = [&](int pos) {
     int a = 0, z = P.batch - 1;

@@ -495,8 +495,8 @@ pkv_status paged_kv_block_table(const pkv_pool* cpool, int64_t seq, int32_t* pag
   const Seq& s = it->second;
   if (pages_out) {
     if (max_pages < 0) return fail(PKV_ERR_INVALID_ARG, "negative max_pages");
-    size_t n = std::min<size_t>(size_t(max_pages), s.pages.size());
-    std::memcpy(pages_out, s.pages.data(), n * sizeof(int32_t));
+    const size_t n = std::min<size_t>(size_t(max_pages), s.pages.size());
+    if (n > 0) std::memcpy(pages_out, s.pages.data(), n * sizeof(int32_t));   // an empty table may have no storage
   }
   if (n_pages_out) *n_pages_out = int32_t(s.pages.size());
   if (len_out) *len_out = s.len;

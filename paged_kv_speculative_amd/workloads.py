@@ -101,6 +101,20 @@ class Workload:
             k, v = np.concatenate([pk, k]), np.concatenate([pv, v])
         return k, v
 
+    def step_kv(self, step):
+        """K, V [B, n_q, Hkv, d] of the n_q tokens a later verification step
+        appends (float32; bf16-valued for bf16 KV)."""
+        x = [self._tokens(61 + 2 * step, b, self.n_q) for b in range(self.batch)]
+        y = [self._tokens(62 + 2 * step, b, self.n_q) for b in range(self.batch)]
+        return np.stack(x), np.stack(y)
+
+    def step_q(self, step):
+        """Queries [B, n_q, Hq, d] of a later verification step (bf16 bit
+        patterns for bf16 queries)."""
+        x = _rng(self.seed, 71, step).standard_normal(
+            (self.batch, self.n_q, self.num_q_heads, self.head_dim), dtype=np.float32)
+        return bf16_bits(x) if self.q_dtype == "bf16" else x
+
     # -- queries and masks ----------------------------------------------------
     def q(self):
         x = _rng(self.seed, 31).standard_normal(

@@ -140,6 +140,24 @@ def test_special_cases():
     assert np.all(k == 1)
 
 
+@pytest.mark.parametrize("bad_token", [-1, "V", "V+5"])
+def test_out_of_vocabulary_drafts_match_oracle(bad_token):
+    """Draft tokens -1, V and V+5 at a random position of each sequence: the
+    kernel's decisions and resampled tokens equal the oracle's, which rejects
+    such a token at its position."""
+    rng = np.random.default_rng(21)
+    B, g, V = 48, 4, 3000
+    T = (rng.standard_normal((B, g + 1, V)) * 2).astype(np.float32)
+    D = T[:, :g] + (rng.standard_normal((B, g, V)) * 0.4).astype(np.float32)
+    x = rng.integers(0, V, (B, g)).astype(np.int32)
+    pos = rng.integers(0, g, B)
+    bad = {"V": V, "V+5": V + 5}.get(bad_token, bad_token)
+    x[np.arange(B), pos] = bad
+    k, tok, ties = _check_against_oracle(T, D, x, seed=17, step=3)
+    assert ties <= 1
+    assert np.all(k <= pos)
+
+
 def test_prepared_accept_matches():
     from paged_kv_speculative_amd import PreparedAccept
     rng = np.random.default_rng(11)

@@ -85,6 +85,36 @@ def test_ragged_verify_matches_oracle(cfg, splits):
         assert np.all(O[b, n_b:] == 12345.0) and np.all(L[b, n_b:] == 12345.0), b
 
 
+@pytest.mark.parametrize("splits", [0, 1, 7])
+def test_ragged_zero_and_negative_counts(splits):
+    """Counts of 0 and below are clamped to one slot (the documented [1, n_q]
+    range): the result equals a call with those sequences' counts set to 1,
+    bitwise, and the oracle with one query slot."""
+    w = wl.make(2, small=True, batch=6)
+    nqs = np.array([0, 5, -3, 2, 1, -2147483648], dtype=np.int32)
+    print(f"ragged clamp splits {splits} n_b {nqs.tolist()}", flush=True)
+    clamped = np.clip(nqs, 1, w.n_q)
+    pool, Ks, Vs = _ragged_side(w, clamped)
+    q = _q(w)
+    B, nq, Hq, d = q.shape
+    outs = []
+    for counts in (nqs, clamped):
+        buf = VerifyBuffers(B, nq, Hq, d, 1 << 27, "cuda")
+        buf.out.fill_(12345.0)
+        buf.lse.fill_(12345.0)
+        O, L = pool.verify(q, nq, sm_scale=w.sm_scale, buffers=buf, num_splits=splits,
+                           n_q_seq=torch.from_numpy(counts).cuda())
+        outs.append((O.cpu().numpy(), L.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    O, L = outs[0]
+    qf = w.q_f32().astype(np.float64)
+    for b in range(B):
+        n_b = int(clamped[b])
+        Or, Lr = oa.verify_attention(qf[b:b + 1, :n_b], [Ks[b]], [Vs[b]], n_b, None, float(w.sm_scale))
+        H.compare(O[b:b + 1, :n_b], L[b:b + 1, :n_b], Or, Lr, H.TOL["bf16"])
+        assert np.all(O[b, n_b:] == 12345.0) and np.all(L[b, n_b:] == 12345.0), b
+
+
 def test_full_counts_equal_no_counts_bitwise():
     w = wl.make(2, small=True, batch=6)
     g = H.GpuSide(w)

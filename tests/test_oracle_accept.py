@@ -126,3 +126,34 @@ def test_special_cases():
     toks2[2] = (toks[2] + 1) % V
     r = oc.accept_one(Th, Dh2, toks2, 1, 0, 0)
     assert r["k"] == 2 and r["token"] == toks[2]
+
+
+def test_out_of_vocabulary_draft_is_a_zero_probability_token():
+    """A draft token outside [0, V) is no token of the target's vocabulary:
+    the rule must treat it as a token the target gives probability 0, which
+    min(1, P/Q) rejects with certainty; the next token is then the resample at
+    that position.  Pinned against a real in-vocabulary token whose target
+    probability is exactly 0 (the same decisions, the same draw)."""
+    rng = np.random.default_rng(12)
+    V, gamma = 40, 4
+    for trial in range(30):
+        T = rng.standard_normal((gamma + 1, V)) * 2
+        D = rng.standard_normal((gamma, V)) * 2
+        D[:2] = T[:2]                         # positions 0 and 1 always accepted
+        z = int(rng.integers(0, V))
+        Tz = T.copy()
+        Tz[2, z] = -np.inf                    # P_2(z) = 0 exactly
+        x = rng.integers(0, V, gamma)
+        x[2] = z
+        ref = oc.accept_one(Tz, D, x, 4, trial, trial)
+        assert ref["k"] == 2 and ref["source"] == "residual"
+        for bad in (-1, V, V + 7, -(2 ** 31)):
+            xb = x.copy()
+            xb[2] = bad
+            # the rejected position's residual uses P_2 = softmax(Tz[2]) only
+            # through tokens other than z; the OOV case reads T unchanged, so
+            # compare against the same zero-probability target row
+            got = oc.accept_one(Tz, D, xb, 4, trial, trial)
+            assert (got["k"], got["token"], got["source"]) == (ref["k"], ref["token"], ref["source"])
+            got_plain = oc.accept_one(T, D, xb, 4, trial, trial)
+            assert got_plain["k"] == 2
