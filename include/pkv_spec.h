@@ -288,6 +288,19 @@ typedef struct {
 pkv_status spec_verify_workspace_size(const pkv_verify_args* args, size_t* bytes_out);
 pkv_status spec_verify_attention(const pkv_verify_args* args, void* stream);
 
+/* spec_verify_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the scratch taken from a
+ * static array the library holds on each GPU it runs on (80 MiB per GPU,
+ * 83886080 bytes, kept until the process ends) instead of args->workspace,
+ * which is ignored.  The call itself allocates nothing.  A call whose scratch
+ * (spec_verify_workspace_size) exceeds 80 MiB returns PKV_ERR_WORKSPACE and
+ * enqueues nothing; fewer num_splits need less.  Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (other streams,
+ * other threads) race and give wrong results; calls ordered on one stream are
+ * safe.  Nothing in the array needs to start at zero. */
+pkv_status spec_verify_attention_static(const pkv_verify_args* args, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Acceptance                                                                */
 /* ------------------------------------------------------------------------ */

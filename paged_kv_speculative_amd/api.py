@@ -281,6 +281,26 @@ def spec_verify_attention(q, k_pages, v_pages, block_table, seq_lens, *, n_q, nu
     return buffers.out, buffers.lse
 
 
+def spec_verify_attention_static(q, k_pages, v_pages, block_table, seq_lens, *, n_q, num_kv_heads,
+                                 kv_dtype, out, lse, k_scale=None, v_scale=None, batch_slots=None,
+                                 anc_mask=None, sm_scale=None, num_splits=0, n_q_seq=None,
+                                 shared_prefix_pages=0, stream=None):
+    """spec_verify_attention with the library's static scratch: nothing is
+    allocated, the caller passes the outputs `out` [B, n_q, Hq, d] and `lse`
+    [B, n_q, Hq] (float32, on q's device).  Calls that overlap in time on one
+    GPU share the scratch and race."""
+    a = _verify_args(q, k_pages, v_pages, block_table, seq_lens, n_q, num_kv_heads, kv_dtype,
+                     k_scale, v_scale, batch_slots, anc_mask, sm_scale, num_splits, n_q_seq,
+                     shared_prefix_pages)
+    B, _, Hq, d = q.shape
+    assert out.dtype == torch.float32 and out.shape == (B, n_q, Hq, d) and out.is_contiguous()
+    assert lse.dtype == torch.float32 and lse.shape == (B, n_q, Hq) and lse.is_contiguous()
+    assert out.device == q.device and lse.device == q.device
+    a.out, a.lse = out.data_ptr(), lse.data_ptr()
+    check(lib.spec_verify_attention_static(C.byref(a), _stream(stream)))
+    return out, lse
+
+
 class PreparedVerify:
     """spec_verify_attention with its arguments marshalled once.  The launch
     reads the tensors given here (queries, pages, block table, lengths) at

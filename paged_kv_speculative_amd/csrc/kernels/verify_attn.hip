@@ -1453,14 +1453,14 @@ extern "C" pkv_status spec_verify_workspace_size(const pkv_verify_args* args, si
   return PKV_OK;
 }
 
-extern "C" pkv_status spec_verify_attention(const pkv_verify_args* a, void* stream) {
-  Plan pl;
-  pkv_status st = make_plan(a, &pl);
-  if (st != PKV_OK) return st;
-  if (!a->out) return fail(PKV_ERR_INVALID_ARG, "null output pointer");
-  const size_t need = pl.cum_bytes + pl.part_bytes + pl.prefix_bytes;
-  if (need > 0 && (!a->workspace || a->workspace_bytes < need))
-    return fail(PKV_ERR_WORKSPACE, "workspace smaller than spec_verify_workspace_size");
+namespace pkv {
+namespace {
+
+// Launches a planned call with its scratch at `ws` (at least the plan's
+// bytes): the page prefix sums, the partial results of split units and the
+// cascade's prefix partials.  None of it has to start at zero: every word
+// the merge reads is written earlier in the same call.
+pkv_status verify_launch(const pkv_verify_args* a, const Plan& pl, void* ws, void* stream) {
   VerifyParams p{};
   p.q = a->q;
   p.k_pages = static_cast<const char*>(a->k_pages);
@@ -1474,9 +1474,9 @@ extern "C" pkv_status spec_verify_attention(const pkv_verify_args* a, void* stre
   p.nq_seq = a->n_q_seq;
   p.out = a->out;
   p.lse = a->lse;
-  p.cum = static_cast<int*>(a->workspace);
-  p.part = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + pl.cum_bytes);
-  p.prefix_part = pl.prefix_bytes ? reinterpret_cast<float*>(static_cast<char*>(a->workspace) + pl.cum_bytes +
+  p.cum = static_cast<int*>(ws);
+  p.part = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.cum_bytes);
+  p.prefix_part = pl.prefix_bytes ? reinterpret_cast<float*>(static_cast<char*>(ws) + pl.cum_bytes +
                                                              pl.part_bytes)
                                   : nullptr;
   p.pref = a->shared_prefix_pages;
@@ -1518,4 +1518,65 @@ extern "C" pkv_status spec_verify_attention(const pkv_verify_args* a, void* stre
   }
   if (e != hipSuccess) return fail(PKV_ERR_DEVICE, std::string("verify launch: ") + hipGetErrorString(e));
   return PKV_OK;
+}
+
+// Scratch of spec_verify_attention_static: one array per GPU, held by the
+// library until the process ends (uninitialised device data, so the shared
+// library's file does not grow with it).  Host code never uses the array's
+// name as an address: each device's address comes from hipGetSymbolAddress,
+// taken once per device with that device current.
+constexpr size_t kStaticScratchBytes = size_t(80) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, or null with the status.
+pkv_status static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return fail(PKV_ERR_DEVICE, "no current HIP device for the static scratch");
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return fail(PKV_ERR_DEVICE, std::string("static scratch address: ") + hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" pkv_status spec_verify_attention(const pkv_verify_args* a, void* stream) {
+  Plan pl;
+  pkv_status st = make_plan(a, &pl);
+  if (st != PKV_OK) return st;
+  if (!a->out) return fail(PKV_ERR_INVALID_ARG, "null output pointer");
+  const size_t need = pl.cum_bytes + pl.part_bytes + pl.prefix_bytes;
+  if (need > 0 && (!a->workspace || a->workspace_bytes < need))
+    return fail(PKV_ERR_WORKSPACE, "workspace smaller than spec_verify_workspace_size");
+  return verify_launch(a, pl, a->workspace, stream);
+}
+
+extern "C" pkv_status spec_verify_attention_static(const pkv_verify_args* a, void* stream) {
+  Plan pl;
+  pkv_status st = make_plan(a, &pl);
+  if (st != PKV_OK) return st;
+  if (!a->out) return fail(PKV_ERR_INVALID_ARG, "null output pointer");
+  const size_t need = pl.cum_bytes + pl.part_bytes + pl.prefix_bytes;
+  if (need > kStaticScratchBytes)
+    return fail(PKV_ERR_WORKSPACE, "call needs " + std::to_string(need) + " bytes of scratch; the static scratch holds " +
+                                       std::to_string(kStaticScratchBytes) + " (fewer num_splits need less)");
+  void* ws = nullptr;
+  if (need > 0 && (st = static_scratch(&ws)) != PKV_OK) return st;
+  return verify_launch(a, pl, ws, stream);
 }
