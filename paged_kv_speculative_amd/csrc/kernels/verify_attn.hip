@@ -58,6 +58,11 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ int s_buffer_load_dword(i32x4 rsrc, int offset, int cachepolicy)
     __asm("llvm.amdgcn.s.buffer.load.i32");
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+// Eight consecutive dwords through the scalar unit (one request).
+__device__ i32x8 s_buffer_load_dwordx8(i32x4 rsrc, int offset, int cachepolicy)
+    __asm("llvm.amdgcn.s.buffer.load.v8i32");
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -251,13 +256,26 @@ constexpr int kLenMask = (1 << kNqShift) - 1;
 // scalar.
 __device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Exclusive prefix of pages per sequence into s_cum[0..batch].
-__device__ void page_prefix(const VerifyParams& P, int* s_cum, int* s_tmp) {
+// Verification slots of sequence b: n_q, or its own count clamped to [1, n_q].
+__device__ inline int seq_slots(const VerifyParams& P, int b) {
+  return P.nq_seq ? min(max(P.nq_seq[b], 1), P.n_q) : P.n_q;
+}
+
+// Exclusive prefix of pages per sequence into s_cum[0..batch], and per
+// sequence its block-table row and length word (N | n_b << kNqShift) into
+// s_seq[2b], s_seq[2b + 1], so that the streaming loop reads them from LDS.
+__device__ void page_prefix(const VerifyParams& P, int* s_cum, int* s_tmp, int* s_seq) {
   const int tid = threadIdx.x;
   if (P.batch <= 64) {                         // one wave: a shuffle scan
     if (tid < 64) {
       int v = 0;
-      if (tid < P.batch) v = max(0, ((P.seq_lens[P.batch_slots ? P.batch_slots[tid] : tid] + 15) >> 4) - P.pref);
+      if (tid < P.batch) {
+        const int row = P.batch_slots ? P.batch_slots[tid] : tid;
+        const int N = P.seq_lens[row];
+        v = max(0, ((N + 15) >> 4) - P.pref);
+        s_seq[2 * tid] = row;
+        s_seq[2 * tid + 1] = N | (seq_slots(P, tid) << kNqShift);
+      }
       int x = v;
       for (int off = 1; off < 64; off <<= 1) {
         const int y = __shfl_up(x, off, 64);
@@ -274,7 +292,10 @@ __device__ void page_prefix(const VerifyParams& P, int* s_cum, int* s_tmp) {
   int local = 0;
   for (int b = b0; b < b1; ++b) {
     const int row = P.batch_slots ? P.batch_slots[b] : b;
-    local += max(0, ((P.seq_lens[row] + 15) >> 4) - P.pref);
+    const int N = P.seq_lens[row];
+    local += max(0, ((N + 15) >> 4) - P.pref);
+    s_seq[2 * b] = row;
+    s_seq[2 * b + 1] = N | (seq_slots(P, b) << kNqShift);
   }
   s_tmp[tid] = local;
   __syncthreads();
@@ -287,8 +308,7 @@ __device__ void page_prefix(const VerifyParams& P, int* s_cum, int* s_tmp) {
   int run = s_tmp[tid] - local;
   for (int b = b0; b < b1; ++b) {
     s_cum[b] = run;
-    const int row = P.batch_slots ? P.batch_slots[b] : b;
-    run += max(0, ((P.seq_lens[row] + 15) >> 4) - P.pref);
+    run += max(0, (((s_seq[2 * b + 1] & kLenMask) + 15) >> 4) - P.pref);
   }
   if (tid == kThreads - 1) s_cum[P.batch] = s_tmp[tid];
   __syncthreads();
@@ -336,8 +356,8 @@ struct Cursor {
 // their loads keep the default cache policy so the second finds the first's
 // lines in L2.  Otherwise pages stream with the non-temporal policy.
 template <int D, int NT, bool FP8, bool TREE, bool SHARED, bool W2, bool MX>
-__device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, int hi, int worker,
-                             int q_lds_off, int row0) {
+__device__ void stream_range(const VerifyParams& P, const int* s_cum, const int* s_seq, int lo, int hi,
+                             int worker, int q_lds_off, int row0) {
   using SH = Shape<D, NT, FP8, W2, MX>;
   constexpr int G = D / 64;                      // MX: scale tiles per token
   using Regs = PageRegs<D, FP8>;
@@ -346,19 +366,13 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
   const int m16 = lane & 15, jg = lane >> 4;
   const unsigned lane_off = unsigned(m16 * 64 + jg * 16);
   const long page_stride = long(P.Hkv) * P.slab_bytes;
-  const i32x4 len_rsrc = scalar_rsrc(P.seq_lens, 0xFFFFFFFFu);
-  const i32x4 slot_rsrc = scalar_rsrc(P.batch_slots, P.batch_slots ? unsigned(P.batch) * 4u : 0u);
-  const i32x4 nq_rsrc = scalar_rsrc(P.nq_seq, P.nq_seq ? unsigned(P.batch) * 4u : 0u);
-
   // ---- cursor helpers (all scalar) -----------------------------------------
+  // A sequence's page count, block-table row and length word come from LDS
+  // (page_prefix), so moving to the next unit waits for no global load.
   auto seq_info = [&](Cursor& c) {
     c.np = uni(s_cum[c.b + 1]) - uni(s_cum[c.b]);
-    c.row = P.batch_slots ? s_buffer_load_dword(slot_rsrc, c.b * 4, 0) : c.b;
-    // per-sequence counts are clamped to [1, n_q] (zero and negative counts
-    // give one slot, as in the merge kernel); without them every sequence
-    // has n_q
-    const int nq = P.nq_seq ? min(max(s_buffer_load_dword(nq_rsrc, c.b * 4, 0), 1), P.n_q) : P.n_q;
-    c.n = s_buffer_load_dword(len_rsrc, c.row * 4, 0) | (nq << kNqShift);
+    c.row = uni(s_seq[2 * c.b]);
+    c.n = uni(s_seq[2 * c.b + 1]);
   };
   auto locate = [&](int pos) {
     int a = 0, z = P.batch - 1;
@@ -776,8 +790,20 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
   PageMeta meta[RS];
   Cursor c = locate(lo);
   const int len = hi - lo;
-  int id_pend = s_buffer_load_dword(bt_rsrc(c), c.page * 4, 0);
-  auto prefetch = [&](Regs& R, PageMeta& M, int rel) {
+  // The page ids of the first positions come from one scalar load of eight
+  // consecutive block-table entries of the starting unit (inside the unit's
+  // row, so never past its valid entries); later ids are fetched one
+  // position ahead.  Without this the prologue waited for PF dependent loads.
+  const bool win = c.np >= 8;
+  const int wb = win ? min(c.page, c.np - 8) : 0;
+  const i32x8 ids8 = win ? s_buffer_load_dwordx8(bt_rsrc(c), wb * 4, 0) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  const int b_start = c.b, g_start = c.g;
+  auto next_id = [&](const Cursor& cc, bool prologue) {
+    if (prologue && win && cc.b == b_start && cc.g == g_start && cc.page - wb < 8) return ids8[cc.page - wb];
+    return s_buffer_load_dword(bt_rsrc(cc), cc.page * 4, 0);
+  };
+  int id_pend = next_id(c, true);
+  auto prefetch = [&](Regs& R, PageMeta& M, int rel, bool prologue = false) {
     const bool valid = rel < len;
     if (valid && (c.page == 0 || rel == 0)) {  // a new unit enters the window: stage its Q
       if (pf_units - cm_units < QS) {
@@ -791,11 +817,11 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, int lo, in
     load_page(R, M, c, id_pend, valid);
     if (rel + 1 < len) {
       advance(c);
-      id_pend = s_buffer_load_dword(bt_rsrc(c), c.page * 4, 0);
+      id_pend = next_id(c, prologue);
     }
   };
 #pragma unroll
-  for (int r = 0; r < PF; ++r) prefetch(ring[r], meta[r], r);
+  for (int r = 0; r < PF; ++r) prefetch(ring[r], meta[r], r, true);
   for (int i0 = 0; i0 < len; i0 += RS) {
 #pragma unroll
     for (int r = 0; r < RS; ++r) {
@@ -855,7 +881,7 @@ __global__ __launch_bounds__(kThreads) void verify_merge_kernel(VerifyParams P) 
   const int x = blockIdx.y * kThreads + threadIdx.x;
   if (x >= R * (D / 4)) return;
   const int r = x / (D / 4), c4 = x % (D / 4);
-  const int nq_b = P.nq_seq ? min(max(P.nq_seq[b], 1), P.n_q) : P.n_q;
+  const int nq_b = seq_slots(P, b);
   if (r / P.G >= nq_b) return;
   const int i = r / P.G, h = g * P.G + r % P.G;
   const long oi = long(b * P.n_q + i) * P.Hq + h;
@@ -1056,7 +1082,7 @@ __global__ __launch_bounds__(kThreads) void verify_prefix_kernel(VerifyParams P)
   if (r >= R) return;
   const int b = int(r / rows_seq), rem = int(r % rows_seq);
   const int i = rem / P.G, h = g * P.G + rem % P.G;
-  const int nq_b = P.nq_seq ? min(max(P.nq_seq[b], 1), P.n_q) : P.n_q;
+  const int nq_b = seq_slots(P, b);
   if (i >= nq_b) return;
   float M = kNegInf;
 #pragma unroll
@@ -1087,11 +1113,13 @@ __global__ __launch_bounds__(kThreads) void verify_prefix_kernel(VerifyParams P)
   }
 }
 
-// Dynamic LDS of the streaming kernel: page prefix sums and scan scratch,
-// then every wave's Q slots, then their ancestor-mask slots.
+// Dynamic LDS of the streaming kernel: page prefix sums, scan scratch and
+// per-sequence (row, length word) pairs, then every wave's Q slots, then
+// their ancestor-mask slots.
 __host__ __device__ inline int cum_lds_bytes(int batch) {
   const int cum_words = (batch + 1 + 3) & ~3;
-  return (cum_words + kThreads) * 4;
+  const int seq_words = (2 * batch + 3) & ~3;
+  return (cum_words + kThreads + seq_words) * 4;
 }
 
 template <int D, int NT, bool W2 = false>
@@ -1106,7 +1134,8 @@ template <int D, int NT, bool FP8, bool TREE, bool SHARED, bool W2, bool MX>
 __device__ inline void stream_kernel_body(VerifyParams P) {
   extern __shared__ int s_cum[];
   const int cum_words = (P.batch + 1 + 3) & ~3;
-  page_prefix(P, s_cum, s_cum + cum_words);
+  int* s_seq = s_cum + cum_words + kThreads;
+  page_prefix(P, s_cum, s_cum + cum_words, s_seq);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= P.batch; i += kThreads) P.cum[i] = s_cum[i];
   const int W = P.Hkv * uni(s_cum[P.batch]);
@@ -1116,7 +1145,8 @@ __device__ inline void stream_kernel_body(VerifyParams P) {
   const int range = worker / P.rg, rgi = worker % P.rg;
   if (range >= n_rng) return;
   const int lo = int(range_lo(range, W, n_rng)), hi = int(range_lo(range + 1, W, n_rng));
-  stream_range<D, NT, FP8, TREE, SHARED, W2, MX>(P, s_cum, lo, hi, worker, cum_lds_bytes(P.batch), rgi * P.rows_w);
+  stream_range<D, NT, FP8, TREE, SHARED, W2, MX>(P, s_cum, s_seq, lo, hi, worker, cum_lds_bytes(P.batch),
+                                                 rgi * P.rows_w);
 }
 
 template <int D, int NT, bool FP8, bool TREE, bool SHARED, bool MX = false>
@@ -1138,7 +1168,7 @@ __global__ __launch_bounds__(128) void verify_f32_kernel(VerifyParams P) {
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int g = h / P.G;
   const int row_b = P.batch_slots ? P.batch_slots[b] : b;
-  const int nq_b = P.nq_seq ? min(max(P.nq_seq[b], 1), P.n_q) : P.n_q;
+  const int nq_b = seq_slots(P, b);
   const int N = P.seq_lens[row_b], L = N - nq_b;
   const int* bt = P.block_table + long(row_b) * P.bt_stride;
   __shared__ float s_q[D];
