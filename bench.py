@@ -7,6 +7,8 @@ A step is one pass of the whole path over the batch, as a serving loop runs it:
   4. paged_kv_rollback     commit 1+k tokens, drop the rejected gamma-k
 For a draft-tree workload steps 3 and 4 are spec_accept_tree (accepted branch)
 and paged_kv_commit_path (the branch's K/V moved into place, the rest dropped).
+With --fused, steps 1 and 2 are one spec_verify_attention_append call (the
+verification kernels write the new tokens themselves).
 (the accepted lengths are read back to the host each step, as a serving loop
 must to emit tokens).  Inputs are resident in HBM before the timed region.
 Several independent pool instances are used round-robin so that no step finds
@@ -48,6 +50,9 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="replay verification and acceptance from HIP graphs (measured slower than "
                          "eager launches on MI355X: 177 vs 168 us per step)")
+    ap.add_argument("--fused", action="store_true",
+                    help="append the new tokens inside the verification launch "
+                         "(spec_verify_attention_append) instead of a separate paged_kv_append")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="kept for the counter commands; the 1 GiB reference copy always runs after the steps")
     return ap.parse_args()
@@ -175,7 +180,7 @@ class Instance:
             probs = torch.softmax(self.D.reshape(-1, V), -1)
             self.x = torch.multinomial(probs, 1, generator=g).reshape(B, gam).to(torch.int32)
             del probs
-        self.verify = self.accept_call = None
+        self.verify = self.verify_append = self.accept_call = None
         self.step_t = torch.zeros(1, dtype=torch.int32, device="cuda")
         self.graph_v = self.graph_a = self.accept_graph_call = None
 
@@ -198,6 +203,11 @@ def run_gpu(args, w, torch, api):
     for I in insts:
         I.verify = I.pool.prepare_verify(I.q, nq, anc_mask=I.anc, sm_scale=w.sm_scale,
                                          shared_prefix_pages=cascade_pages(args, w))
+        if args.fused:
+            shp = (B, nq, w.num_kv_heads, w.head_dim)
+            I.verify_append = I.pool.prepare_verify_append(
+                np.arange(B), I.q, I.knew.view(shp), I.vnew.view(shp), anc_mask=I.anc, sm_scale=w.sm_scale,
+                buffers=I.verify.buffers, shared_prefix_pages=cascade_pages(args, w))
         if I.accept:
             I.accept_call = api.PreparedAccept(I.T, I.D, I.x, seed=12345)
             if args.graph:       # the captured launch reads its step counter from device memory
@@ -217,11 +227,14 @@ def run_gpu(args, w, torch, api):
 
     def step(s):
         I = insts[s % R]
-        I.pool.append(seq_ids, n_new, I.knew, I.vnew)
+        if not args.fused:
+            I.pool.append(seq_ids, n_new, I.knew, I.vnew)
         I.lens += nq
         step_lens.append(I.lens.copy())
         ev[s][0].record()
-        if I.graph_v is not None:
+        if args.fused:
+            I.verify_append()
+        elif I.graph_v is not None:
             I.graph_v.replay()
         else:
             I.verify()
@@ -422,6 +435,10 @@ def cpu_baseline(cfg, kv_dtype, budget_s, max_workers=16):
 
 def main():
     args = parse()
+    if args.fused and args.graph:
+        print("--fused does its pool bookkeeping on the host at every call: it is not replayed from a graph",
+              file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
               "(the verification step would shard by sequence or KV head with no exchange)",
@@ -453,7 +470,8 @@ def main():
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
-        "launch": "hip-graph (verification, acceptance)" if args.graph else "eager",
+        "launch": ("hip-graph (verification, acceptance)" if args.graph else "eager")
+                  + (", append fused into verification" if args.fused else ""),
         "vs_baseline": None,
         "dtype": {"fp8": "fp8-kv/bf16", "fp8mx": "fp8-kv(mx64)/bf16"}.get(w.kv_dtype, "bf16"),
         "data": "synthetic",

@@ -288,6 +288,28 @@ typedef struct {
 pkv_status spec_verify_workspace_size(const pkv_verify_args* args, size_t* bytes_out);
 pkv_status spec_verify_attention(const pkv_verify_args* args, void* stream);
 
+/* Append and verify in one launch (atozofsoftwareengineering.blog, diagram
+ * "Speculative Decoding Memory Pipeline": FP8 pages flow straight into the
+ * fused verification attention).  Equivalent to
+ *   paged_kv_append(pool, n_seqs, seqs, {n_q, ..., n_q}, k_new, v_new, src, stream)
+ *   spec_verify_attention(args, stream)
+ * except that the verification kernels quantise and write the new tokens
+ * themselves and attend them from registers, so the step runs one kernel
+ * launch fewer.  The pool's bookkeeping happens on the host before the launch
+ * as for paged_kv_append (same pages, same codes and scales, bit for bit).
+ * k_new, v_new: device [n_seqs][n_q][Hkv][head_dim], 16-byte aligned; bf16 for
+ * bf16 pools, fp32 for the FP8 kinds.  args must describe this pool (its
+ * page, scale, block-table and length arrays, its dtype and shape) with
+ * batch == n_seqs, sequence i in block-table row i, batch_slots and n_q_seq
+ * NULL, 1 <= n_q <= 16 and n_seqs <= 768; its workspace is sized by
+ * spec_verify_workspace_size.  A sequence whose partly filled tail page is
+ * shared (copy-on-write) or an fp32 pool returns PKV_ERR_UNSUPPORTED; every
+ * check happens before anything changes (PKV_ERR_DEVICE after a failed launch
+ * leaves the host bookkeeping advanced, as paged_kv_append). */
+pkv_status spec_verify_attention_append(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
+                                        const void* k_new, const void* v_new, const pkv_verify_args* args,
+                                        void* stream);
+
 /* spec_verify_attention for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same kernels and results, with the scratch taken from a

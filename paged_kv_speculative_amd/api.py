@@ -199,6 +199,25 @@ class Pool:
                               num_splits=num_splits, n_q_seq=n_q_seq,
                               shared_prefix_pages=shared_prefix_pages)
 
+    def verify_append(self, seqs, q, k_new, v_new, anc_mask=None, sm_scale=None, buffers=None,
+                      num_splits=0, shared_prefix_pages=0, stream=None):
+        """Append n_q = q.shape[1] tokens to every sequence of `seqs` (sequence
+        i in block-table row i) and verify them, in one launch
+        (spec_verify_attention_append).  k_new, v_new: [B, n_q, Hkv, d],
+        bfloat16 for a bf16 pool, float32 for the FP8 kinds."""
+        if k_new.data_ptr() % 16:
+            k_new = k_new.clone()
+        if v_new.data_ptr() % 16:
+            v_new = v_new.clone()
+        return self.prepare_verify_append(seqs, q, k_new, v_new, anc_mask, sm_scale, buffers, num_splits,
+                                          shared_prefix_pages)(stream)
+
+    def prepare_verify_append(self, seqs, q, k_new, v_new, anc_mask=None, sm_scale=None, buffers=None,
+                              num_splits=0, shared_prefix_pages=0):
+        return PreparedVerifyAppend(self, seqs, q, k_new, v_new, anc_mask=anc_mask, sm_scale=sm_scale,
+                                    buffers=buffers, num_splits=num_splits,
+                                    shared_prefix_pages=shared_prefix_pages)
+
     def verify(self, q, n_q, slots=None, anc_mask=None, sm_scale=None, buffers=None, num_splits=0,
                n_q_seq=None, shared_prefix_pages=0, stream=None):
         return spec_verify_attention(
@@ -326,6 +345,45 @@ class PreparedVerify:
 
     def __call__(self, stream=None):
         check(lib.spec_verify_attention(C.byref(self.args), _stream(stream)))
+        return self.buffers.out, self.buffers.lse
+
+
+class PreparedVerifyAppend:
+    """Pool.verify_append with its arguments marshalled once: each call
+    appends the tokens held in k_new, v_new (read at call time) to every
+    listed sequence and verifies the queries in q; returns (out, lse) from
+    the buffers it owns."""
+
+    def __init__(self, pool, seqs, q, k_new, v_new, *, anc_mask=None, sm_scale=None, buffers=None,
+                 num_splits=0, shared_prefix_pages=0):
+        B, n_q, _, d = q.shape
+        want = torch.bfloat16 if pool.kv_dtype == "bf16" else torch.float32
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            if t.dtype != want or tuple(t.shape) != (B, n_q, pool.num_kv_heads, d) or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {want} tensor of shape "
+                                 f"{(B, n_q, pool.num_kv_heads, d)}")
+            if t.device != q.device:
+                raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+            if t.data_ptr() % 16:
+                raise ValueError(f"{name} must be 16-byte aligned")
+        self._seqs, self._seqs_p = _ints(seqs, np.int64)
+        assert self._seqs.size == B
+        a = _verify_args(q, pool.k_pages, pool.v_pages, pool.block_table, pool.seq_lens, n_q,
+                         pool.num_kv_heads, pool.kv_dtype, pool.k_scale, pool.v_scale, None, anc_mask,
+                         sm_scale, num_splits, None, shared_prefix_pages)
+        ws = verify_workspace_size(a)
+        if buffers is None:
+            buffers = VerifyBuffers(B, n_q, q.shape[2], d, ws, q.device)
+        assert buffers.workspace.numel() >= ws
+        a.out, a.lse = buffers.out.data_ptr(), buffers.lse.data_ptr()
+        a.workspace, a.workspace_bytes = buffers.workspace.data_ptr(), buffers.workspace.numel()
+        self.args, self.buffers, self.pool = a, buffers, pool
+        self._kp, self._vp = _ptr(k_new), _ptr(v_new)
+        self._keep = (q, k_new, v_new, anc_mask)
+
+    def __call__(self, stream=None):
+        check(lib.spec_verify_attention_append(self.pool._h, self._seqs.size, self._seqs_p, self._kp, self._vp,
+                                               C.byref(self.args), _stream(stream)))
         return self.buffers.out, self.buffers.lse
 
 

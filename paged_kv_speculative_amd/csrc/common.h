@@ -92,4 +92,26 @@ static_assert(sizeof(PoolMoveBatch) <= 4000, "kernel argument block too large");
 pkv_status launch_pool_update(const PoolDevice& dev, const PoolUpdateBatch& batch, void* stream);
 pkv_status launch_pool_moves(const PoolDevice& dev, const PoolMoveBatch& batch, void* stream);
 
+// Appended tokens of a fused append + verification launch
+// (spec_verify_attention_append): the pool's bookkeeping is done on the
+// host; the verification kernels quantise and write the n_q new tokens of
+// every sequence, attend them from registers, and then write each sequence's
+// new block-table entry and length.  new_page[b] is the page taken by the
+// call for logical page ceil(old_len / 16) of sequence b (-1 when the new
+// tokens fit in the sequence's last page); at most one per sequence (n_q <=
+// 16).  Sources are [batch][n_q][Hkv][head_dim]: bf16 for bf16 pools, fp32
+// for the FP8 kinds.
+constexpr int kFusedMaxBatch = 768;
+constexpr int kFusedMaxTokens = 16;
+
+struct FusedAppend {
+  const void* k_new;
+  const void* v_new;
+  int32_t new_page[kFusedMaxBatch];
+};
+
+// Implemented in kernels/verify_attn.hip: the verification launch of a
+// fused call (arguments already checked by the pool).
+pkv_status verify_fused_launch(const pkv_verify_args* args, const FusedAppend& fused, void* stream);
+
 }  // namespace pkv

@@ -134,7 +134,20 @@ pkv_status launch_pool_moves(const PoolDevice& dev, const PoolMoveBatch& batch, 
   return PKV_OK;
 }
 
+// The fused append + verification call refuses fp32 pools (the only kind
+// this check builds) before it sizes a workspace or launches: reaching either
+// stand-in is a failure.
+pkv_status verify_fused_launch(const pkv_verify_args*, const FusedAppend&, void*) {
+  require(false, "fused launch reached for an fp32 pool");
+  return PKV_ERR_DEVICE;
+}
+
 }  // namespace pkv
+
+extern "C" pkv_status spec_verify_workspace_size(const pkv_verify_args*, size_t*) {
+  require(false, "verification workspace query reached for an fp32 pool");
+  return PKV_ERR_DEVICE;
+}
 
 namespace {
 
@@ -361,6 +374,11 @@ void serial_phase(uint64_t seed, int n_ops) {
               "sequence listed twice");
       int32_t row = -1;
       require(paged_kv_alloc(hx.pool, s, -1, 0, &row, nullptr) == PKV_ERR_SEQ_EXISTS, "alloc existing");
+      pkv_verify_args va{};
+      va.batch = 1;
+      va.n_q = 1;
+      require(spec_verify_attention_append(hx.pool, 1, &s, buf, buf, &va, nullptr) == PKV_ERR_UNSUPPORTED,
+              "fused append on an fp32 pool");
       expect_fail = true;
     }
     if (expect_fail) {

@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include "../common.h"
+#include "fp8_codec.h"
 #include "layout.h"
 
 namespace pkv {
@@ -30,13 +31,6 @@ __device__ inline float wave_max(float v) {
   return v;
 }
 
-__device__ inline unsigned char quant_e4m3(float x, float inv) {
-  float y = x * inv;
-  y = fminf(fmaxf(y, -448.0f), 448.0f);
-  // hardware OCP E4M3 conversion, round to nearest even
-  unsigned packed = __builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false);
-  return static_cast<unsigned char>(packed & 0xFF);
-}
 
 // Item it of a task (token it / G, channel group it % G) for the calling lane.
 struct Item {
@@ -145,8 +139,8 @@ __device__ void write_fp8(const PoolDevice& dev, const PoolTask& t, int h, int H
   if (t.flags & kFresh) {
     ak = wave_max(ak);
     av = wave_max(av);
-    sk = ak == 0.0f ? 1.0f : ak / 448.0f;
-    sv = av == 0.0f ? 1.0f : av / 448.0f;
+    sk = fresh_page_scale(ak);
+    sv = fresh_page_scale(av);
     if ((threadIdx.x & 63) == 0) {
       static_cast<float*>(dev.k_scale)[sidx] = sk;
       static_cast<float*>(dev.v_scale)[sidx] = sv;
@@ -171,19 +165,6 @@ __device__ void write_fp8(const PoolDevice& dev, const PoolTask& t, int h, int H
 #pragma unroll
     for (int i = 0; i < 8; ++i) vslab[v_index_fp8(im[u].slot, im[u].c0 + i)] = quant_e4m3(vx[u][i], iv);
   }
-}
-
-// E8M0 exponent byte of the tile scale 2^k for a tile whose largest magnitude
-// is amax: k the smallest integer with amax / 2^k <= 448 = 0.875 * 2^9
-// (amax = m * 2^E with m in [0.5, 1): k = E - 9, plus 1 when m > 0.875),
-// clamped to [-127, 127]; k = 0 for amax = 0.
-__device__ inline int tile_exponent_byte(float amax) {
-  const unsigned b = __float_as_uint(amax);
-  if (amax == 0.0f) return 127;
-  const int e = int(b >> 23) & 0xFF;
-  if (e == 0) return 0;                          // subnormal amax: k = -127
-  const int k = (e - 126) - 9 + ((b & 0x7FFFFF) > 0x600000u ? 1 : 0);
-  return min(max(k, -127), 127) + 127;
 }
 
 // FP8 pool with per-64-channel scales, fp32 source: every token is quantised

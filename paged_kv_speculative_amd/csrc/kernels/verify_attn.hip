@@ -45,6 +45,8 @@
 #include <tuple>
 
 #include "../common.h"
+#include "fp8_codec.h"
+#include "layout.h"
 
 namespace pkv {
 
@@ -96,6 +98,15 @@ struct VerifyParams {
   float* part;           // [n_wg][2][slot_floats] partial (O, max, sum) of split units
   float* prefix_part;    // cascade: [batch][n_q][Hq][D + 2] (O, max, sum) over the shared prefix
   int* cum;              // [batch + 1] page prefix sums (written by workgroup 0)
+  // fused append (spec_verify_attention_append): the pages hold the cached
+  // tokens only, every one visible; a unit finished by one wave writes its
+  // normalised O to out and its log2-sum-exp to unit_lse [batch][n_q][Hq]
+  // (not lse) for the merge, which adds the new tokens; old_len [batch]
+  // keeps the cached lengths
+  int fused;
+  int kv_kind;           // pkv_dtype of the pool
+  float* unit_lse;
+  int* old_len;
   long slab_bytes;       // bytes of one (page, KV head) slab
   int batch, n_q, Hq, Hkv, G, rows, bt_stride, n_wg;
   int pref;              // cascade: leading block-table pages shared by every sequence (0: none)
@@ -274,7 +285,7 @@ __device__ void page_prefix(const VerifyParams& P, int* s_cum, int* s_tmp, int* 
         const int N = P.seq_lens[row];
         v = max(0, ((N + 15) >> 4) - P.pref);
         s_seq[2 * tid] = row;
-        s_seq[2 * tid + 1] = N | (seq_slots(P, tid) << kNqShift);
+        s_seq[2 * tid + 1] = N | ((P.fused ? 0 : seq_slots(P, tid)) << kNqShift);
       }
       int x = v;
       for (int off = 1; off < 64; off <<= 1) {
@@ -295,7 +306,7 @@ __device__ void page_prefix(const VerifyParams& P, int* s_cum, int* s_tmp, int* 
     const int N = P.seq_lens[row];
     local += max(0, ((N + 15) >> 4) - P.pref);
     s_seq[2 * b] = row;
-    s_seq[2 * b + 1] = N | (seq_slots(P, b) << kNqShift);
+    s_seq[2 * b + 1] = N | ((P.fused ? 0 : seq_slots(P, b)) << kNqShift);
   }
   s_tmp[tid] = local;
   __syncthreads();
@@ -541,14 +552,17 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, const int*
       l += __shfl_xor(l, 16, 64);
       l += __shfl_xor(l, 32, 64);
       const int rl = nt * 16 + m16, r = row0 + rl;
-      if (local_ok(nt) && r / P.G < u_nq) {       // rows of slots past the sequence's count: not written
+      // rows of slots past the sequence's count are not written (fused
+      // calls have no per-sequence counts: every row)
+      if (local_ok(nt) && (P.fused || r / P.G < u_nq)) {
         const int i = r / P.G, h = u_g * P.G + r % P.G;
         const long oi = long(u_b * P.n_q + i) * P.Hq + h;
         // cascade: a unit finished here absorbs the shared prefix's partial
-        // (O, max, sum) of its row, written by the prefix pass
+        // (O, max, sum) of its row, written by the prefix pass (fused calls
+        // leave that to the merge)
         float sa = 1.0f, sb = 0.0f, m_out = m_run[nt];
         const float* pp = nullptr;
-        if (!FP8 && full && P.pref > 0) {
+        if (!FP8 && full && P.pref > 0 && !P.fused) {
           pp = P.prefix_part + oi * (D + 2);
           const float mp = pp[D], lp = pp[D + 1];
           m_out = fmaxf(m_run[nt], mp);
@@ -595,7 +609,8 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, const int*
         }
         if (jg == 0) {
           if (full) {
-            if (P.lse) P.lse[oi] = (m_out + __log2f(l)) * kLn2;
+            if (P.fused) P.unit_lse[oi] = m_run[nt] + __log2f(l);
+            else if (P.lse) P.lse[oi] = (m_out + __log2f(l)) * kLn2;
           } else {
             part[long(P.rows_w) * D + rl] = m_run[nt];
             part[long(P.rows_w) * D + P.rows_w + rl] = l;
@@ -867,22 +882,82 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, const int*
   if (u_b >= 0) finalize();
 }
 
+// Adds (max, sum, O) of one piece to a running log-sum-exp combine (base 2).
+__device__ inline void lse_combine(float& M, float& Ls, float4& o, float m, float l, const float4& v) {
+  const float mn = fmaxf(M, m);
+  const float ref = mn == kNegInf ? 0.0f : mn;
+  const float a = exp2_fast(M - ref), c = exp2_fast(m - ref);
+  Ls = Ls * a + l * c;
+  o.x = o.x * a + v.x * c;
+  o.y = o.y * a + v.y * c;
+  o.z = o.z * a + v.z * c;
+  o.w = o.w * a + v.w * c;
+  M = mn;
+}
+
+// The streamed pieces of unit (b, g), row r (output row oi), channels
+// 4 c4 .. 4 c4 + 3, combined into (M, Ls, o).  Returns false when the unit
+// was finished in place by one worker (nothing to merge; in a fused call
+// that worker left its normalised O in out and its log2-sum-exp in
+// unit_lse, which are then combined and true returned).
+// The pieces of a split unit are the slots of the workers whose ranges
+// overlap it, found in closed form; each thread issues the loads of up to
+// eight pieces (their maxima, sums and its float4 of O) before combining
+// them.
+template <int D>
+__device__ bool merge_stream_pieces(const VerifyParams& P, int b, int g, int r, long oi, int c4, float& M,
+                                    float& Ls, float4& o) {
+  const int* __restrict__ cum = P.cum;
+  const long W = long(P.Hkv) * cum[P.batch];
+  const int np = cum[b + 1] - cum[b];
+  if (np == 0) return true;                       // no pages past the prefix: nothing streamed
+  const int n_rng = used_ranges(P, W);
+  const long u0 = long(P.Hkv) * cum[b] + long(g) * np, u1 = u0 + np;
+  const int wf = owner_of(u0, W, n_rng), wl = owner_of(u1 - 1, W, n_rng);
+  if (wf == wl) {                                 // finished in place
+    if (!P.fused) return false;
+    lse_combine(M, Ls, o, P.unit_lse[oi], 1.0f, *reinterpret_cast<const float4*>(P.out + oi * D + 4 * c4));
+    return true;
+  }
+  // row r is row rl of row group rgi, held by wave (range * rg + rgi)
+  const int rgi = r / P.rows_w, rl = r % P.rows_w, RW = P.rows_w;
+  const long sf = slot_floats(RW, D);
+  // the first range's piece is its second slot when the range began in an
+  // earlier unit; for the others the unit is their first
+  const long first_base = (2L * (long(wf) * P.rg + rgi) + (range_starts_at(wf, W, n_rng, u0) ? 0 : 1)) * sf;
+  const float* __restrict__ part = P.part;
+  constexpr int KB = 8;
+  for (int w0 = wf; w0 <= wl; w0 += KB) {
+    float mk[KB], lk[KB];
+    float4 v[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int w = min(w0 + u, wl);
+      const long base = w == wf ? first_base : 2L * (long(w) * P.rg + rgi) * sf;
+      mk[u] = part[base + long(RW) * D + rl];
+      lk[u] = part[base + long(RW) * D + RW + rl];
+      v[u] = *reinterpret_cast<const float4*>(part + base + long(rl) * D + 4 * c4);
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      if (w0 + u > wl) break;
+      lse_combine(M, Ls, o, mk[u], lk[u], v[u]);
+    }
+  }
+  return true;
+}
+
 // Merge of the units split over workers.  Block (unit, y) owns 256
 // consecutive float4s of the unit's [rows][D] output; a unit finished in
-// place by one worker is skipped.  The pieces of a unit are the slots of the
-// workers whose ranges overlap it, found in closed form; each thread issues
-// the loads of up to eight pieces (their maxima, sums and its float4 of O)
-// before combining them with the log-sum-exp rule.
+// place by one worker is skipped.
 template <int D>
 __global__ __launch_bounds__(kThreads) void verify_merge_kernel(VerifyParams P) {
   const int b = blockIdx.x / P.Hkv, g = blockIdx.x % P.Hkv;
-  const int* __restrict__ cum = P.cum;
   const int R = P.rows;
   const int x = blockIdx.y * kThreads + threadIdx.x;
   if (x >= R * (D / 4)) return;
   const int r = x / (D / 4), c4 = x % (D / 4);
-  const int nq_b = seq_slots(P, b);
-  if (r / P.G >= nq_b) return;
+  if (r / P.G >= seq_slots(P, b)) return;
   const int i = r / P.G, h = g * P.G + r % P.G;
   const long oi = long(b * P.n_q + i) * P.Hq + h;
   // cascade: the shared prefix's partial is the first piece of every row
@@ -894,53 +969,283 @@ __global__ __launch_bounds__(kThreads) void verify_merge_kernel(VerifyParams P) 
     Ls = pp[D + 1];
     o = *reinterpret_cast<const float4*>(pp + 4 * c4);
   }
-  const long W = long(P.Hkv) * cum[P.batch];
-  const int np = cum[b + 1] - cum[b];
-  bool merged = P.pref > 0 && np == 0;           // no positions past the prefix: the prefix alone
-  if (np > 0) {
-    const int n_rng = used_ranges(P, W);
-    const long u0 = long(P.Hkv) * cum[b] + long(g) * np, u1 = u0 + np;
-    const int wf = owner_of(u0, W, n_rng), wl = owner_of(u1 - 1, W, n_rng);
-    if (wf == wl) return;                         // finished in place
-    merged = true;
-    // row r is row rl of row group rgi, held by wave (range * rg + rgi)
-    const int rgi = r / P.rows_w, rl = r % P.rows_w, RW = P.rows_w;
-    const long sf = slot_floats(RW, D);
-    // the first range's piece is its second slot when the range began in an
-    // earlier unit; for the others the unit is their first
-    const long first_base = (2L * (long(wf) * P.rg + rgi) + (range_starts_at(wf, W, n_rng, u0) ? 0 : 1)) * sf;
-    const float* __restrict__ part = P.part;
-    constexpr int KB = 8;
-    for (int w0 = wf; w0 <= wl; w0 += KB) {
-      float mk[KB], lk[KB];
-      float4 v[KB];
-#pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        const int w = min(w0 + u, wl);
-        const long base = w == wf ? first_base : 2L * (long(w) * P.rg + rgi) * sf;
-        mk[u] = part[base + long(RW) * D + rl];
-        lk[u] = part[base + long(RW) * D + RW + rl];
-        v[u] = *reinterpret_cast<const float4*>(part + base + long(rl) * D + 4 * c4);
-      }
-#pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        if (w0 + u > wl) break;
-        const float mn = fmaxf(M, mk[u]);
-        const float ref = mn == kNegInf ? 0.0f : mn;
-        const float a = exp2_fast(M - ref), c = exp2_fast(mk[u] - ref);
-        Ls = Ls * a + lk[u] * c;
-        o.x = o.x * a + v[u].x * c;
-        o.y = o.y * a + v[u].y * c;
-        o.z = o.z * a + v[u].z * c;
-        o.w = o.w * a + v[u].w * c;
-        M = mn;
-      }
-    }
-  }
-  if (!merged) return;
+  const bool split = merge_stream_pieces<D>(P, b, g, r, oi, c4, M, Ls, o);
+  // without a prefix, a unit finished in place (or a unit with no pages at
+  // all) was written by the streaming kernel
+  if (!split || (P.pref == 0 && P.cum[b + 1] == P.cum[b])) return;
   const float inv = 1.0f / Ls;
   *reinterpret_cast<float4*>(P.out + oi * D + 4 * c4) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
   if (c4 == 0 && P.lse) P.lse[oi] = (M + __log2f(Ls)) * kLn2;
+}
+
+// Fused append (spec_verify_attention_append), after the streaming kernel.
+// Block (unit (b, g), y) owns the same 256 float4s of the unit's [rows][D]
+// output as the plain merge.  Every block of the unit encodes the unit's n_q
+// new tokens exactly as the pool-update kernel encodes an append (same page
+// scales and codes; fp8_codec.h), keeps their values as attended (decoded)
+// in LDS, and computes its rows' attention piece over them (the chain or tree
+// mask among the new tokens) in fp32; that piece is combined with the
+// streamed pieces of the cached tokens and the cascade's prefix piece.  Block
+// y = 0 writes the codes and scales into the pool, and for head 0 the
+// sequence's new block-table entry and length (nothing in this launch reads
+// them after the streaming kernel, which used the cached lengths).  The
+// blocks of a unit compute the same scales from the same values, so the
+// copies agree bit for bit.
+template <int D>
+__global__ __launch_bounds__(kThreads) void verify_fused_merge_kernel(VerifyParams P, FusedAppend F) {
+  constexpr int NT = kFusedMaxTokens, IT = D / 8;     // new tokens; 8-channel items per token
+  constexpr int NRB = kThreads / (D / 4);             // output rows per block
+  constexpr int KP = D + 4;                           // LDS row pitch (16-byte rows, banks staggered)
+  __shared__ __align__(16) float s_k[NT][KP];        // new K, V as attended (decoded), fp32
+  __shared__ __align__(16) float s_v[NT][KP];
+  __shared__ __align__(16) float s_q[NRB][KP];
+  __shared__ float s_w[NRB][NT];                      // scores, then weights
+  __shared__ float s_m[NRB], s_l[NRB];
+  __shared__ float s_amax[2][2][kWaves];              // [page of the call][K, V][wave]
+  const int b = blockIdx.x / P.Hkv, g = blockIdx.x % P.Hkv, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int nq = P.n_q, G = P.G, R = P.rows, row = b;
+  const int r0 = blockIdx.y * NRB, nrb = min(NRB, R - r0);
+  const bool writer = blockIdx.y == 0;
+  const int N0 = P.old_len[b], N = N0 + nq;
+  const int np_old = (N0 + 15) >> 4, pa = N0 >> 4;    // pages pa and pa + 1 can take new tokens
+  const bool fp8 = P.kv_kind == PKV_FP8_E4M3, mx = P.kv_kind == PKV_FP8_E4M3_MX64;
+  auto page_id = [&](int p) { return p < np_old ? P.block_table[long(row) * P.bt_stride + p] : F.new_page[b]; };
+
+  // ---- loads: the new tokens' items (token j, channels c0 .. c0 + 7) and
+  // this block's query rows, issued before the streamed pieces are read ----
+  const int j = tid / IT, c0 = (tid % IT) * 8;
+  const bool ok = j < nq;
+  float kx[8], vx[8];
+  const long src = (long(b * nq + (ok ? j : 0)) * P.Hkv + g) * D + c0;
+  if (fp8 || mx) {
+    const float4* ks = static_cast<const float4*>(F.k_new) + src / 4;
+    const float4* vs = static_cast<const float4*>(F.v_new) + src / 4;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const float4 a = ok ? ks[h2] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 c = ok ? vs[h2] : make_float4(0.f, 0.f, 0.f, 0.f);
+      kx[4 * h2] = a.x; kx[4 * h2 + 1] = a.y; kx[4 * h2 + 2] = a.z; kx[4 * h2 + 3] = a.w;
+      vx[4 * h2] = c.x; vx[4 * h2 + 1] = c.y; vx[4 * h2 + 2] = c.z; vx[4 * h2 + 3] = c.w;
+    }
+  } else {
+    const uint4 a = ok ? *reinterpret_cast<const uint4*>(static_cast<const unsigned short*>(F.k_new) + src)
+                       : make_uint4(0, 0, 0, 0);
+    const uint4 c = ok ? *reinterpret_cast<const uint4*>(static_cast<const unsigned short*>(F.v_new) + src)
+                       : make_uint4(0, 0, 0, 0);
+    const unsigned wa[4] = {a.x, a.y, a.z, a.w}, wc[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kx[e] = __uint_as_float((wa[e / 2] >> (16 * (e % 2))) << 16);
+      vx[e] = __uint_as_float((wc[e / 2] >> (16 * (e % 2))) << 16);
+    }
+  }
+  // query rows r0 .. r0 + nrb - 1: thread -> (row, 8 channels)
+  const int qr = tid / IT, qc = (tid % IT) * 8;
+  uint4 qbits = make_uint4(0, 0, 0, 0);
+  if (qr < nrb) {
+    const int rr = r0 + qr, i = rr / G, h = g * G + rr % G;
+    qbits = *reinterpret_cast<const uint4*>(static_cast<const unsigned short*>(P.q) +
+                                            (long(b * nq + i) * P.Hq + h) * D + qc);
+  }
+  // ---- streamed pieces and the prefix piece of this thread's float4 ------------
+  const int x = blockIdx.y * kThreads + tid;
+  const bool out_ok = x < R * (D / 4);
+  const int rr = out_ok ? x / (D / 4) : r0, c4 = x % (D / 4), rl = rr - r0;
+  const int oi_i = rr / G, oi_h = g * G + rr % G;
+  const long oi = long(b * nq + oi_i) * P.Hq + oi_h;
+  float M = kNegInf, Ls = 0.0f;
+  float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (out_ok) {
+    if (P.pref > 0) {
+      const float* pp = P.prefix_part + oi * (D + 2);
+      M = pp[D];
+      Ls = pp[D + 1];
+      o = *reinterpret_cast<const float4*>(pp + 4 * c4);
+    }
+    merge_stream_pieces<D>(P, b, g, rr, oi, c4, M, Ls, o);
+  }
+  // ---- encode the new tokens ---------------------------------------------------
+  const int t = N0 + (ok ? j : 0), pj = t >> 4, slot = t & 15;
+  // page-head scales: a page first written by this call takes amax / 448 of
+  // the values written into it (per K and V), an older page keeps its scale
+  float sk_pg = 1.0f, sv_pg = 1.0f;
+  if (fp8) {
+    float ak = 0.0f, av = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ak = fmaxf(ak, fabsf(kx[e]));
+      av = fmaxf(av, fabsf(vx[e]));
+    }
+    float red[2][2];
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      red[q2][0] = ok && pj == pa + q2 ? ak : 0.0f;
+      red[q2][1] = ok && pj == pa + q2 ? av : 0.0f;
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv)
+        for (int o2 = 32; o2 > 0; o2 >>= 1) red[q2][kv] = fmaxf(red[q2][kv], __shfl_xor(red[q2][kv], o2, 64));
+    }
+    if (lane == 0)
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        s_amax[q2][0][wave] = red[q2][0];
+        s_amax[q2][1][wave] = red[q2][1];
+      }
+    __syncthreads();
+    const int q2 = pj - pa;
+    const bool fresh = (pj << 4) >= N0;
+    const int id = page_id(pj);
+    if (fresh) {
+      float mk = 0.0f, mv = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        mk = fmaxf(mk, s_amax[q2][0][w]);
+        mv = fmaxf(mv, s_amax[q2][1][w]);
+      }
+      sk_pg = fresh_page_scale(mk);
+      sv_pg = fresh_page_scale(mv);
+    } else {
+      sk_pg = static_cast<const float*>(P.k_scale)[long(id) * P.Hkv + g];
+      sv_pg = static_cast<const float*>(P.v_scale)[long(id) * P.Hkv + g];
+    }
+    // the item holding slot 0 of a page this call starts writes its scales
+    if (writer && ok && fresh && slot == 0 && c0 == 0) {
+      const_cast<float*>(static_cast<const float*>(P.k_scale))[long(id) * P.Hkv + g] = sk_pg;
+      const_cast<float*>(static_cast<const float*>(P.v_scale))[long(id) * P.Hkv + g] = sv_pg;
+    }
+  }
+  if (ok) {
+    const int id = page_id(pj);
+    char* kslab = const_cast<char*>(P.k_pages) + (long(id) * P.Hkv + g) * P.slab_bytes;
+    char* vslab = const_cast<char*>(P.v_pages) + (long(id) * P.Hkv + g) * P.slab_bytes;
+    float kd[8], vd[8];
+    if (fp8 || mx) {
+      float ik = 1.0f / sk_pg, iv = 1.0f / sv_pg, dk = sk_pg, dv = sv_pg;
+      if (mx) {
+        // one power-of-two scale per 64 channels of the token: the tile's
+        // eight items are eight consecutive threads
+        float ak = 0.0f, av = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ak = fmaxf(ak, fabsf(kx[e]));
+          av = fmaxf(av, fabsf(vx[e]));
+        }
+#pragma unroll
+        for (int o2 = 1; o2 < 8; o2 <<= 1) {
+          ak = fmaxf(ak, __shfl_xor(ak, o2, 64));
+          av = fmaxf(av, __shfl_xor(av, o2, 64));
+        }
+        const int ek = tile_exponent_byte(ak), ev = tile_exponent_byte(av);
+        ik = ldexpf(1.0f, 127 - ek);
+        iv = ldexpf(1.0f, 127 - ev);
+        dk = ldexpf(1.0f, ek - 127);
+        dv = ldexpf(1.0f, ev - 127);
+        if (writer && (c0 & 63) == 0) {
+          const long eo = ((long(id) * P.Hkv + g) * 16 + slot) * (D / 64) + c0 / 64;
+          const_cast<unsigned char*>(static_cast<const unsigned char*>(P.k_scale))[eo] = static_cast<unsigned char>(ek);
+          const_cast<unsigned char*>(static_cast<const unsigned char*>(P.v_scale))[eo] = static_cast<unsigned char>(ev);
+        }
+      }
+      unsigned lo = 0, hi = 0;
+      unsigned char cv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const unsigned char ck = quant_e4m3(kx[e], ik);
+        cv[e] = quant_e4m3(vx[e], iv);
+        if (e < 4) lo |= unsigned(ck) << (8 * e);
+        else hi |= unsigned(ck) << (8 * (e - 4));
+        kd[e] = dequant_e4m3(ck) * dk;
+        vd[e] = dequant_e4m3(cv[e]) * dv;
+      }
+      if (writer) {
+        *reinterpret_cast<uint2*>(kslab + k_index_fp8(slot, c0, D)) = make_uint2(lo, hi);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) reinterpret_cast<unsigned char*>(vslab)[v_index_fp8(slot, c0 + e)] = cv[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        kd[e] = kx[e];
+        vd[e] = vx[e];
+      }
+      if (writer) {
+        unsigned kw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          kw[e] = (__float_as_uint(kx[2 * e]) >> 16) | (__float_as_uint(kx[2 * e + 1]) & 0xFFFF0000u);
+        *reinterpret_cast<uint4*>(kslab + 2 * k_index_bf16(slot, c0, D)) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+        unsigned short* vs16 = reinterpret_cast<unsigned short*>(vslab);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vs16[v_index_bf16(slot, c0 + e)] = static_cast<unsigned short>(__float_as_uint(vx[e]) >> 16);
+      }
+    }
+    *reinterpret_cast<float4*>(&s_k[j][c0]) = make_float4(kd[0], kd[1], kd[2], kd[3]);
+    *reinterpret_cast<float4*>(&s_k[j][c0 + 4]) = make_float4(kd[4], kd[5], kd[6], kd[7]);
+    *reinterpret_cast<float4*>(&s_v[j][c0]) = make_float4(vd[0], vd[1], vd[2], vd[3]);
+    *reinterpret_cast<float4*>(&s_v[j][c0 + 4]) = make_float4(vd[4], vd[5], vd[6], vd[7]);
+  }
+  if (qr < nrb) {
+    const unsigned wq[4] = {qbits.x, qbits.y, qbits.z, qbits.w};
+    float qf[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[e] = __uint_as_float((wq[e / 2] >> (16 * (e % 2))) << 16);
+    *reinterpret_cast<float4*>(&s_q[qr][qc]) = make_float4(qf[0], qf[1], qf[2], qf[3]);
+    *reinterpret_cast<float4*>(&s_q[qr][qc + 4]) = make_float4(qf[4], qf[5], qf[6], qf[7]);
+  }
+  __syncthreads();
+  // ---- scores of this block's rows over the new tokens -------------------------
+  for (int y = tid; y < nrb * nq; y += kThreads) {
+    const int ql = y / nq, jj = y % nq, i = (r0 + ql) / G;
+    const bool vis = P.anc ? ((P.anc[long(b) * nq + i] >> jj) & 1ull) != 0 : jj <= i;
+    float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll 8
+    for (int c = 0; c < D; c += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(&s_q[ql][c]);
+      const float4 k = *reinterpret_cast<const float4*>(&s_k[jj][c]);
+      d0 = fmaf(a.x, k.x, d0);
+      d1 = fmaf(a.y, k.y, d1);
+      d0 = fmaf(a.z, k.z, d0);
+      d1 = fmaf(a.w, k.w, d1);
+    }
+    s_w[ql][jj] = vis ? (d0 + d1) * P.scale_log2 : kNegInf;
+  }
+  __syncthreads();
+  if (tid < nrb) {
+    float m = kNegInf;
+    for (int jj = 0; jj < nq; ++jj) m = fmaxf(m, s_w[tid][jj]);
+    const float ref = m == kNegInf ? 0.0f : m;
+    float l = 0.0f;
+    for (int jj = 0; jj < nq; ++jj) {
+      const float w = exp2_fast(s_w[tid][jj] - ref);
+      s_w[tid][jj] = w;
+      l += w;
+    }
+    s_m[tid] = m;
+    s_l[tid] = l;
+  }
+  __syncthreads();
+  // ---- combine and write -----------------------------------------------------------
+  if (out_ok) {
+    float4 on = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int jj = 0; jj < nq; ++jj) {
+      const float w = s_w[rl][jj];
+      const float4 v = *reinterpret_cast<const float4*>(&s_v[jj][4 * c4]);
+      on.x = fmaf(w, v.x, on.x);
+      on.y = fmaf(w, v.y, on.y);
+      on.z = fmaf(w, v.z, on.z);
+      on.w = fmaf(w, v.w, on.w);
+    }
+    lse_combine(M, Ls, o, s_m[rl], s_l[rl], on);
+    const float inv = 1.0f / Ls;
+    *reinterpret_cast<float4*>(P.out + oi * D + 4 * c4) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+    if (c4 == 0 && P.lse) P.lse[oi] = (M + __log2f(Ls)) * kLn2;
+  }
+  // ---- the sequence's new length and block-table entry ---------------------------
+  if (writer && g == 0 && tid == 0) {
+    const_cast<int*>(P.seq_lens)[row] = N;
+    if (F.new_page[b] >= 0) const_cast<int*>(P.block_table)[long(row) * P.bt_stride + np_old] = F.new_page[b];
+  }
 }
 
 // Shared-prefix pass of the cascade (bf16 KV): the first P.pref pages are the
@@ -1136,8 +1441,11 @@ __device__ inline void stream_kernel_body(VerifyParams P) {
   const int cum_words = (P.batch + 1 + 3) & ~3;
   int* s_seq = s_cum + cum_words + kThreads;
   page_prefix(P, s_cum, s_cum + cum_words, s_seq);
-  if (blockIdx.x == 0)
+  if (blockIdx.x == 0) {
     for (int i = threadIdx.x; i <= P.batch; i += kThreads) P.cum[i] = s_cum[i];
+    if (P.fused)
+      for (int i = threadIdx.x; i < P.batch; i += kThreads) P.old_len[i] = s_seq[2 * i + 1] & kLenMask;
+  }
   const int W = P.Hkv * uni(s_cum[P.batch]);
   if (W == 0) return;
   const int worker = blockIdx.x * kWaves + uni(threadIdx.x >> 6);
@@ -1239,7 +1547,8 @@ __global__ __launch_bounds__(128) void verify_f32_kernel(VerifyParams P) {
 struct Plan {
   int D, NT, rows, n_wg, rg, rows_w;
   bool fp8, mx, tree, f32;
-  size_t cum_bytes, part_bytes, prefix_bytes;
+  size_t cum_bytes, part_bytes, prefix_bytes, fused_bytes;
+  size_t bytes() const { return cum_bytes + part_bytes + prefix_bytes + fused_bytes; }
 };
 
 pkv_status check_args(const pkv_verify_args* a, Plan* pl) {
@@ -1384,6 +1693,13 @@ pkv_status make_plan(const pkv_verify_args* a, Plan* pl) {
                          ? size_t(a->batch) * a->n_q * a->num_q_heads * (a->head_dim + 2) * sizeof(float)
                          : 0;
   pl->n_wg = 0;
+  // a call that spec_verify_attention_append can take also sizes its
+  // per-row log2-sum-exp of units finished in place and the cached lengths
+  const bool fusable = !pl->f32 && a->n_q <= kFusedMaxTokens && a->batch <= kFusedMaxBatch && !a->n_q_seq &&
+                       !a->batch_slots;
+  pl->fused_bytes = fusable ? ((size_t(a->batch) * a->n_q * a->num_q_heads * sizeof(float) + 255) & ~size_t(255)) +
+                                  ((size_t(a->batch) * sizeof(int) + 255) & ~size_t(255))
+                            : 0;
   if (!pl->f32) {
     int n = a->num_splits;
     if (n == 0) {
@@ -1412,10 +1728,6 @@ hipError_t launch_split_w2(const VerifyParams& p, hipStream_t st) {
       hipFuncAttributeMaxDynamicSharedMemorySize, int(split_smem<D, NT, true>(4096)));
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((verify_stream_kernel_w2<D, NT, FP8, TREE, SHARED, MX>), dim3(p.n_wg), dim3(kThreads), smem, st, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((verify_merge_kernel<D>), dim3(p.batch * p.Hkv, (p.rows * (D / 4) + kThreads - 1) / kThreads),
-                     dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 
@@ -1427,10 +1739,16 @@ hipError_t launch_split(const VerifyParams& p, hipStream_t st) {
       hipFuncAttributeMaxDynamicSharedMemorySize, int(split_smem<D, NT>(4096)));
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((verify_stream_kernel<D, NT, FP8, TREE, SHARED, MX>), dim3(p.n_wg), dim3(kThreads), smem, st, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((verify_merge_kernel<D>), dim3(p.batch * p.Hkv, (p.rows * (D / 4) + kThreads - 1) / kThreads),
-                     dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+// The merge after the streaming kernel: of the split units, or, in a fused
+// call, of every unit with its new tokens (which it also writes).
+template <int D>
+hipError_t launch_merge(const VerifyParams& p, const FusedAppend* f, hipStream_t st) {
+  const dim3 grid(p.batch * p.Hkv, (p.rows * (D / 4) + kThreads - 1) / kThreads);
+  if (f) hipLaunchKernelGGL((verify_fused_merge_kernel<D>), grid, dim3(kThreads), 0, st, p, *f);
+  else hipLaunchKernelGGL((verify_merge_kernel<D>), grid, dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 
@@ -1479,7 +1797,7 @@ extern "C" pkv_status spec_verify_workspace_size(const pkv_verify_args* args, si
   Plan pl;
   pkv_status st = make_plan(args, &pl);
   if (st != PKV_OK) return st;
-  *bytes_out = pl.cum_bytes + pl.part_bytes + pl.prefix_bytes;
+  *bytes_out = pl.bytes();
   return PKV_OK;
 }
 
@@ -1487,11 +1805,15 @@ namespace pkv {
 namespace {
 
 // Launches a planned call with its scratch at `ws` (at least the plan's
-// bytes): the page prefix sums, the partial results of split units and the
-// cascade's prefix partials.  None of it has to start at zero: every word
-// the merge reads is written earlier in the same call.
-pkv_status verify_launch(const pkv_verify_args* a, const Plan& pl, void* ws, void* stream) {
+// bytes): the page prefix sums, the partial results of split units, the
+// cascade's prefix partials and, for a fused call (f not null), the
+// log2-sum-exp of units finished in place and the cached lengths.  None of
+// it has to start at zero: every word the merge reads is written earlier in
+// the same call.
+pkv_status verify_launch(const pkv_verify_args* a, const Plan& pl, void* ws, void* stream,
+                         const FusedAppend* f = nullptr) {
   VerifyParams p{};
+  char* w = static_cast<char*>(ws);
   p.q = a->q;
   p.k_pages = static_cast<const char*>(a->k_pages);
   p.v_pages = static_cast<const char*>(a->v_pages);
@@ -1504,11 +1826,17 @@ pkv_status verify_launch(const pkv_verify_args* a, const Plan& pl, void* ws, voi
   p.nq_seq = a->n_q_seq;
   p.out = a->out;
   p.lse = a->lse;
-  p.cum = static_cast<int*>(ws);
-  p.part = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.cum_bytes);
-  p.prefix_part = pl.prefix_bytes ? reinterpret_cast<float*>(static_cast<char*>(ws) + pl.cum_bytes +
-                                                             pl.part_bytes)
-                                  : nullptr;
+  p.cum = reinterpret_cast<int*>(w);
+  p.part = reinterpret_cast<float*>(w + pl.cum_bytes);
+  p.prefix_part = pl.prefix_bytes ? reinterpret_cast<float*>(w + pl.cum_bytes + pl.part_bytes) : nullptr;
+  if (f) {
+    char* fw = w + pl.cum_bytes + pl.part_bytes + pl.prefix_bytes;
+    p.fused = 1;
+    p.unit_lse = reinterpret_cast<float*>(fw);
+    p.old_len = reinterpret_cast<int*>(fw + ((size_t(a->batch) * a->n_q * a->num_q_heads * sizeof(float) + 255) &
+                                             ~size_t(255)));
+  }
+  p.kv_kind = a->kv_dtype;
   p.pref = a->shared_prefix_pages;
   p.min_range = a->num_splits == 0 ? 8 : 1;
   p.slab_bytes = pkv_page_bytes(a->kv_dtype, a->page_size, a->head_dim);
@@ -1546,6 +1874,7 @@ pkv_status verify_launch(const pkv_verify_args* a, const Plan& pl, void* ws, voi
     if (e == hipSuccess) e = pl.D == 64 ? dispatch_nt<64>(p, pl.NT, pl.fp8, pl.tree, s)
                                         : dispatch_nt<128>(p, pl.NT, pl.fp8, pl.tree, s);
   }
+  if (e == hipSuccess && !pl.f32) e = pl.D == 64 ? launch_merge<64>(p, f, s) : launch_merge<128>(p, f, s);
   if (e != hipSuccess) return fail(PKV_ERR_DEVICE, std::string("verify launch: ") + hipGetErrorString(e));
   return PKV_OK;
 }
@@ -1591,7 +1920,7 @@ extern "C" pkv_status spec_verify_attention(const pkv_verify_args* a, void* stre
   pkv_status st = make_plan(a, &pl);
   if (st != PKV_OK) return st;
   if (!a->out) return fail(PKV_ERR_INVALID_ARG, "null output pointer");
-  const size_t need = pl.cum_bytes + pl.part_bytes + pl.prefix_bytes;
+  const size_t need = pl.bytes();
   if (need > 0 && (!a->workspace || a->workspace_bytes < need))
     return fail(PKV_ERR_WORKSPACE, "workspace smaller than spec_verify_workspace_size");
   return verify_launch(a, pl, a->workspace, stream);
@@ -1602,11 +1931,19 @@ extern "C" pkv_status spec_verify_attention_static(const pkv_verify_args* a, voi
   pkv_status st = make_plan(a, &pl);
   if (st != PKV_OK) return st;
   if (!a->out) return fail(PKV_ERR_INVALID_ARG, "null output pointer");
-  const size_t need = pl.cum_bytes + pl.part_bytes + pl.prefix_bytes;
+  const size_t need = pl.bytes();
   if (need > kStaticScratchBytes)
     return fail(PKV_ERR_WORKSPACE, "call needs " + std::to_string(need) + " bytes of scratch; the static scratch holds " +
                                        std::to_string(kStaticScratchBytes) + " (fewer num_splits need less)");
   void* ws = nullptr;
   if (need > 0 && (st = static_scratch(&ws)) != PKV_OK) return st;
   return verify_launch(a, pl, ws, stream);
+}
+
+pkv_status pkv::verify_fused_launch(const pkv_verify_args* a, const FusedAppend& f, void* stream) {
+  Plan pl;
+  pkv_status st = make_plan(a, &pl);
+  if (st != PKV_OK) return st;
+  if (pl.f32 || pl.fused_bytes == 0) return fail(PKV_ERR_UNSUPPORTED, "call cannot be fused");
+  return verify_launch(a, pl, a->workspace, stream, &f);
 }

@@ -344,6 +344,70 @@ pkv_status paged_kv_append(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
   return sink.status;
 }
 
+pkv_status spec_verify_attention_append(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
+                                        const void* k_new, const void* v_new, const pkv_verify_args* args,
+                                        void* stream) {
+  if (!pool || !args) return fail(PKV_ERR_INVALID_ARG, "null pool or arguments");
+  if (!pool->device) return fail(PKV_ERR_INVALID_ARG, "the fused call needs a pool with device memory");
+  const pkv_pool_desc& d = pool->desc;
+  if (d.kv_dtype == PKV_F32) return fail(PKV_ERR_UNSUPPORTED, "the fused call supports bf16 and FP8 pools");
+  if (n_seqs < 1 || n_seqs > kFusedMaxBatch || n_seqs != args->batch)
+    return fail(PKV_ERR_INVALID_ARG, "n_seqs must equal args->batch and be in [1, 768]");
+  if (args->n_q < 1 || args->n_q > kFusedMaxTokens)
+    return fail(PKV_ERR_UNSUPPORTED, "the fused call appends 1..16 tokens per sequence");
+  if (args->n_q_seq || args->batch_slots)
+    return fail(PKV_ERR_UNSUPPORTED, "the fused call takes no per-sequence counts or batch slots");
+  if (!seqs || !k_new || !v_new) return fail(PKV_ERR_INVALID_ARG, "null sequence list or sources");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
+    return fail(PKV_ERR_INVALID_ARG, "source arrays must be 16-byte aligned");
+  if (args->kv_dtype != d.kv_dtype || args->num_kv_heads != d.num_kv_heads || args->head_dim != d.head_dim ||
+      args->page_size != d.page_size || args->k_pages != d.k_pages || args->v_pages != d.v_pages ||
+      args->k_scale != d.k_scale || args->v_scale != d.v_scale || args->block_table != d.block_table ||
+      args->seq_lens != d.seq_lens || args->block_table_stride != d.max_pages_per_seq)
+    return fail(PKV_ERR_INVALID_ARG, "the verification arguments must describe this pool");
+  size_t need = 0;
+  pkv_status st = spec_verify_workspace_size(args, &need);
+  if (st != PKV_OK) return st;
+  if (!args->out) return fail(PKV_ERR_INVALID_ARG, "null output pointer");
+  if (need > 0 && (!args->workspace || args->workspace_bytes < need))
+    return fail(PKV_ERR_WORKSPACE, "workspace smaller than spec_verify_workspace_size");
+  std::lock_guard<std::mutex> lock(pool->mu);
+  // validate every sequence before anything changes (all-or-nothing)
+  thread_local std::vector<Seq*> touched;
+  touched.clear();
+  const uint64_t stamp = ++pool->calls;
+  const int32_t n = args->n_q;
+  int64_t pages_needed = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    auto it = pool->seqs.find(seqs[i]);
+    if (it == pool->seqs.end()) return fail(PKV_ERR_UNKNOWN_SEQ, "append to unknown sequence");
+    Seq& s = it->second;
+    if (s.stamp == stamp) return fail(PKV_ERR_INVALID_ARG, "sequence listed twice");
+    s.stamp = stamp;
+    if (s.row != i) return fail(PKV_ERR_INVALID_ARG, "sequence i of the fused call must use block-table row i");
+    const int64_t total = ceil_div(int64_t(s.len) + n, kPageSize);
+    if (total > d.max_pages_per_seq) return fail(PKV_ERR_CAPACITY, "sequence exceeds max_pages_per_seq");
+    if (s.len % kPageSize && pool->refcount[s.pages[s.len / kPageSize]] > 1)
+      return fail(PKV_ERR_UNSUPPORTED, "the fused call does not copy shared pages (use paged_kv_append)");
+    pages_needed += total - int64_t(s.pages.size());
+    touched.push_back(&s);
+  }
+  if (pages_needed > int64_t(pool->free_ranks.size())) return fail(PKV_ERR_OUT_OF_PAGES, "page pool exhausted");
+  FusedAppend f;
+  f.k_new = k_new;
+  f.v_new = v_new;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    Seq& s = *touched[i];
+    f.new_page[i] = -1;
+    while (int64_t(s.pages.size()) < ceil_div(int64_t(s.len) + n, kPageSize)) {
+      s.pages.push_back(pool->take_page());
+      f.new_page[i] = s.pages.back();          // n <= 16: at most one new page
+    }
+    s.len += n;
+  }
+  return verify_fused_launch(args, f, stream);
+}
+
 pkv_status paged_kv_rollback(pkv_pool* pool, int32_t n_seqs, const int64_t* seqs,
                              const int32_t* n_tokens, void* stream) {
   if (!pool) return fail(PKV_ERR_INVALID_ARG, "null pool");

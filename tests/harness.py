@@ -12,7 +12,8 @@ import torch
 from oracle import attention as oa
 from oracle import pool as opool
 from paged_kv_speculative_amd import Pool, tree_ancestor_masks
-from paged_kv_speculative_amd.workloads import bf16_to_f32
+from paged_kv_speculative_amd.workloads import bf16_bits, bf16_to_f32
+from layout_ref import detile_k, detile_v
 
 TOL = {"f32": 2e-3, "bf16": 2e-3, "fp8": 2e-2, "fp8mx": 2e-2}
 
@@ -31,7 +32,7 @@ def _to_torch(x, kv_dtype, device):
 class GpuSide:
     """The workload's pool filled through paged_kv_alloc/append, plus queries."""
 
-    def __init__(self, w, device="cuda", free_order=None, chunk_tokens=32768):
+    def __init__(self, w, device="cuda", free_order=None, chunk_tokens=32768, verify_tokens=True):
         self.w = w
         order = w.free_order if free_order is None else free_order
         self.pool = Pool(w.num_pages, w.num_kv_heads, w.head_dim, w.kv_dtype, max_seqs=w.batch,
@@ -50,7 +51,8 @@ class GpuSide:
             for b in range(B):
                 self.pool.alloc(b)
         self._append_private(range(B), context=True, chunk_tokens=chunk_tokens)
-        self._append_private(range(B), context=False, chunk_tokens=chunk_tokens)
+        if verify_tokens:
+            self._append_private(range(B), context=False, chunk_tokens=chunk_tokens)
         q = w.q()
         if w.q_dtype == "bf16":
             self.q = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).to(device)
@@ -87,6 +89,25 @@ class GpuSide:
 
     def verify(self, **kw):
         return self.pool.verify(self.q, self.w.n_q, anc_mask=self.anc, sm_scale=self.w.sm_scale, **kw)
+
+    def new_kv(self):
+        """K, V [B, n_q, Hkv, d] of the verification tokens, as the fused call
+        takes them (bf16 for bf16 pools, fp32 for the FP8 kinds)."""
+        w = self.w
+        ks, vs = [], []
+        for b in range(w.batch):
+            k, v = w.private_kv(b)
+            ctx = int(w.cached_lens[b]) - w.prefix_len
+            ks.append(k[ctx:])
+            vs.append(v[ctx:])
+        return _to_torch(np.stack(ks), w.kv_dtype, "cuda"), _to_torch(np.stack(vs), w.kv_dtype, "cuda")
+
+    def verify_append(self, **kw):
+        """Append the verification tokens and verify them in one call
+        (a pool built with verify_tokens=False)."""
+        kn, vn = self.new_kv()
+        return self.pool.verify_append(range(self.w.batch), self.q, kn, vn, anc_mask=self.anc,
+                                       sm_scale=self.w.sm_scale, **kw)
 
 
 def oracle_sequence_kv(w, b):
@@ -148,3 +169,34 @@ def compare(O, L, O_ref, L_ref, tol):
     assert err_o <= tol, f"max|dO|/rms = {err_o:.3e} > {tol}"
     assert err_l <= tol, f"max|dLSE| = {err_l:.3e} > {tol}"
     return err_o, err_l
+
+
+def check_sequence_pages(pool, pm, seq, kv, d):
+    """GPU pages of `seq` hold exactly the oracle model's values in every
+    slot the sequence can see (codes and scales for FP8 kinds)."""
+    pages, n, _ = pool.table(seq)
+    assert pages == pm.tables[seq] and n == pm.lens[seq]
+    kp = pool.k_pages.cpu().numpy()
+    vp = pool.v_pages.cpu().numpy()
+    if kv != "bf16":
+        ks = pool.k_scale.cpu().numpy()
+        vs = pool.v_scale.cpu().numpy()
+    layout = "bf16" if kv == "bf16" else "fp8"
+    for j, p in enumerate(pages):
+        valid = min(16, n - 16 * j)
+        for h in range(pm.H):
+            if kv == "bf16":
+                K = detile_k(kp[p, h].view(np.uint16), layout, d)[:valid]
+                V = detile_v(vp[p, h].view(np.uint16), layout, d)[:valid]
+                assert np.array_equal(K, bf16_bits(pm.k[p, h, :valid])), (seq, j, h)
+                assert np.array_equal(V, bf16_bits(pm.v[p, h, :valid])), (seq, j, h)
+            else:
+                K = detile_k(kp[p, h], layout, d)[:valid]
+                V = detile_v(vp[p, h], layout, d)[:valid]
+                assert np.array_equal(K, pm.kc[p, h, :valid]), (seq, j, h)
+                assert np.array_equal(V, pm.vc[p, h, :valid]), (seq, j, h)
+        if kv == "fp8":
+            assert np.array_equal(ks[p], pm.ks[p]) and np.array_equal(vs[p], pm.vs[p]), (seq, j)
+        elif kv == "fp8mx":
+            assert np.array_equal(ks[p, :, :valid], pm.kx[p, :, :valid]), (seq, j)
+            assert np.array_equal(vs[p, :, :valid], pm.vx[p, :, :valid]), (seq, j)

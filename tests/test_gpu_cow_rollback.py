@@ -20,7 +20,6 @@ import pytest
 import torch
 
 import harness as H
-from layout_ref import detile_k, detile_v
 from oracle import attention as oa
 from oracle import pool as opool
 from paged_kv_speculative_amd import Pool
@@ -47,37 +46,6 @@ def _page_state(pool, p):
     if pool.k_scale is not None:
         parts += [pool.k_scale[p].clone(), pool.v_scale[p].clone()]
     return parts
-
-
-def _check_sequence_pages(pool, pm, seq, kv, d):
-    """GPU pages of `seq` hold exactly the oracle model's values in every
-    slot the sequence can see (codes and scales for FP8 kinds)."""
-    pages, n, _ = pool.table(seq)
-    assert pages == pm.tables[seq] and n == pm.lens[seq]
-    kp = pool.k_pages.cpu().numpy()
-    vp = pool.v_pages.cpu().numpy()
-    if kv != "bf16":
-        ks = pool.k_scale.cpu().numpy()
-        vs = pool.v_scale.cpu().numpy()
-    layout = "bf16" if kv == "bf16" else "fp8"
-    for j, p in enumerate(pages):
-        valid = min(16, n - 16 * j)
-        for h in range(pm.H):
-            if kv == "bf16":
-                K = detile_k(kp[p, h].view(np.uint16), layout, d)[:valid]
-                V = detile_v(vp[p, h].view(np.uint16), layout, d)[:valid]
-                assert np.array_equal(K, wl.bf16_bits(pm.k[p, h, :valid])), (seq, j, h)
-                assert np.array_equal(V, wl.bf16_bits(pm.v[p, h, :valid])), (seq, j, h)
-            else:
-                K = detile_k(kp[p, h], layout, d)[:valid]
-                V = detile_v(vp[p, h], layout, d)[:valid]
-                assert np.array_equal(K, pm.kc[p, h, :valid]), (seq, j, h)
-                assert np.array_equal(V, pm.vc[p, h, :valid]), (seq, j, h)
-        if kv == "fp8":
-            assert np.array_equal(ks[p], pm.ks[p]) and np.array_equal(vs[p], pm.vs[p]), (seq, j)
-        elif kv == "fp8mx":
-            assert np.array_equal(ks[p, :, :valid], pm.kx[p, :, :valid]), (seq, j)
-            assert np.array_equal(vs[p, :, :valid], pm.vx[p, :, :valid]), (seq, j)
 
 
 @pytest.mark.parametrize("kv,d", [("bf16", 128), ("bf16", 64), ("fp8", 128), ("fp8mx", 128)])
@@ -127,7 +95,7 @@ def test_copy_on_write_append(kv, d):
         assert pool.stats()["cow_copies"] == pm.cow_copies
     assert pm.cow_copies == 2
     for s in pm.tables:
-        _check_sequence_pages(pool, pm, s, kv, d)
+        H.check_sequence_pages(pool, pm, s, kv, d)
     # the three sequences' verification against the oracle's gathered K/V
     n_q = 3
     seqs = sorted(pm.tables)

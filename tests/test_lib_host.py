@@ -281,3 +281,18 @@ def test_argument_checks_of_newer_fields():
         t2.batch, t2.n_nodes, t2.max_children, t2.vocab = 2, 16, 4, 1000
         setattr(t2, field, bad)
         assert lib.spec_accept_tree_workspace_size(C.byref(t2), C.byref(n)) == 1, field
+
+
+def test_fused_append_needs_device_pool():
+    """spec_verify_attention_append on a pool without device memory is refused
+    (PKV_ERR_INVALID_ARG) and changes nothing; a null pool likewise."""
+    p = Pool(8, 1, 64, "bf16")
+    p.alloc(0)
+    p.append([0], [5])
+    snap = (p.table(0), p.stats())
+    a = _lib.VerifyArgs()
+    a.batch, a.n_q = 1, 1
+    seqs = _lib.i64_array([0])
+    assert _lib.lib.spec_verify_attention_append(p._h, 1, seqs, None, None, C.byref(a), None) == 1
+    assert _lib.lib.spec_verify_attention_append(None, 1, seqs, None, None, C.byref(a), None) == 1
+    assert (p.table(0), p.stats()) == snap
