@@ -22,6 +22,7 @@ the launch stream.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
 """
 import argparse
+import ctypes as C
 import json
 import os
 import sys
@@ -322,6 +323,27 @@ def run_gpu(args, w, torch, api):
     torch.cuda.synchronize()
     copy_ms = min(a.elapsed_time(b) for a, b in cev)
     res["copy_gbps"] = 2.0 * (1 << 30) / (copy_ms / 1e3) / 1e9     # bytes read + written
+    # the read-rate reference: a plain read of the same pages (every page of
+    # every (sequence, KV head) the verification call reads, all 16 slots),
+    # same partition over 1024 waves and the same loads, no arithmetic;
+    # timed round-robin over the instances after the steps
+    from paged_kv_speculative_amd import _lib
+    sink = torch.empty(1024, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4 * R)]
+    for I in insts:                       # first launches (code object load) untimed
+        _lib.check(_lib.lib.pkv_page_read_probe(C.byref(I.verify.args), sink.data_ptr(), 1024, stream))
+    for j, (a, b) in enumerate(pev):
+        I = insts[j % R]
+        a.record()
+        _lib.check(_lib.lib.pkv_page_read_probe(C.byref(I.verify.args), sink.data_ptr(), 1024, stream))
+        b.record()
+    torch.cuda.synchronize()
+    probe_ms = np.array([a.elapsed_time(b) for a, b in pev])
+    page_bytes = [int(np.sum((I.lens + 15) // 16)) * w.num_kv_heads * 2 * api.page_bytes(w.kv_dtype, w.head_dim)
+                  for I in insts]
+    res["probe_ms"] = probe_ms
+    res["probe_bytes"] = np.array([page_bytes[j % R] for j in range(len(pev))], dtype=np.float64)
     del src, dst
     return res
 
@@ -495,6 +517,17 @@ def main():
             "frac_of_copy": achieved / r["copy_gbps"],
             "kv_bytes_per_call": float(np.mean(r["attn_bytes"])),
             "query_tokens_per_s": float(B * nq / np.median(attn_s)),
+        },
+        "read_ceiling": {
+            "what": "plain read of the same pages (all slots of every page of every sequence and KV head), "
+                    "same wave partition and 16-byte non-temporal loads, no arithmetic; HIP events, "
+                    "after the timed steps",
+            "us_median": float(np.median(r["probe_ms"]) * 1e3),
+            "bytes_per_call": float(np.mean(r["probe_bytes"])),
+            "gbps": float(np.median(r["probe_bytes"] / (r["probe_ms"] / 1e3)) / 1e9),
+            "frac_of_peak": float(np.median(r["probe_bytes"] / (r["probe_ms"] / 1e3)) / 1e9 / HBM_PEAK_GBPS),
+            "verify_rate_frac": float(np.median(r["attn_bytes"] / (r["attn_ms"] / 1e3))
+                                      / np.median(r["probe_bytes"] / (r["probe_ms"] / 1e3))),
         },
         "roofline": {
             "bound": "hbm",

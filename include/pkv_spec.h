@@ -422,6 +422,21 @@ pkv_status spec_accept_tree_workspace_size(const pkv_tree_accept_args* args, siz
 pkv_status spec_accept_tree(const pkv_tree_accept_args* args, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Measurement aid (not a step of the path; futurestack.online, sections 1.1-1.2:
+ * the roofline of a memory-bound kernel is the rate at which its bytes can be
+ * read).  Reads, once each, the K and V slabs of every (sequence, KV head,
+ * page) position that spec_verify_attention(args) reads -- the same bytes, the
+ * same partition into equal contiguous ranges over n_waves waves, the same
+ * 16-byte non-temporal loads with four pages in flight per wave -- and does no
+ * arithmetic but folding them into one word per wave, written to
+ * sink[n_waves] (device).  Uses args' k_pages, v_pages, block_table,
+ * block_table_stride, seq_lens, batch (1..4096), num_kv_heads, head_dim,
+ * page_size and kv_dtype; the slab must be 1, 2, 4 or 8 KiB.  n_waves: a
+ * positive multiple of 4 (1024 = one wave per SIMD on MI355X).  Errors as for
+ * the other calls; nothing is written but sink. */
+pkv_status pkv_page_read_probe(const pkv_verify_args* args, uint32_t* sink, int32_t n_waves, void* stream);
+
+/* ------------------------------------------------------------------------ */
 const char* pkv_status_string(pkv_status status);
 const char* pkv_last_error(void);
 /* Library version string. */

@@ -106,6 +106,7 @@ EXPORTS = {
     "spec_verify_workspace_size": (C.c_int, [C.POINTER(VerifyArgs), C.POINTER(C.c_size_t)]),
     "spec_verify_attention": (C.c_int, [C.POINTER(VerifyArgs), C.c_void_p]),
     "spec_verify_attention_static": (C.c_int, [C.POINTER(VerifyArgs), C.c_void_p]),
+    "pkv_page_read_probe": (C.c_int, [C.POINTER(VerifyArgs), C.c_void_p, C.c_int32, C.c_void_p]),
     "spec_verify_attention_append": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                                C.POINTER(VerifyArgs), C.c_void_p]),
     "spec_accept_workspace_size": (C.c_int, [C.POINTER(AcceptArgs), C.POINTER(C.c_size_t)]),

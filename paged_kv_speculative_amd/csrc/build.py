@@ -18,7 +18,7 @@ PKG = os.path.dirname(HERE)
 OUT = os.path.join(PKG, "libpkvspec.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["pool.cpp", "kernels/kv_append.hip", "kernels/verify_attn.hip", "kernels/accept.hip",
-           "kernels/tree_accept.hip"]
+           "kernels/tree_accept.hip", "kernels/read_probe.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 VALU ops are kept out of generated code

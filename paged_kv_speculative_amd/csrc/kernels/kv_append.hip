@@ -88,12 +88,10 @@ __device__ void write_f32(const PoolDevice& dev, const PoolTask& t, int h, int H
 #pragma unroll
   for (int u = 0; u < kItemsPerLane; ++u) {
     im[u] = item(t, u, h, H, D);
-    if (im[u].ok) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        kx[u][p] = ks[im[u].src / 4 + p];
-        vx[u][p] = vs[im[u].src / 4 + p];
-      }
+    for (int p = 0; p < 2; ++p) {
+      kx[u][p] = im[u].ok ? ks[im[u].src / 4 + p] : make_float4(0.f, 0.f, 0.f, 0.f);
+      vx[u][p] = im[u].ok ? vs[im[u].src / 4 + p] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
   float4* kslab = reinterpret_cast<float4*>(static_cast<char*>(dev.k_pages) + (long(t.page) * H + h) * pb);
