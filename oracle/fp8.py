@@ -11,9 +11,15 @@ S_V" (atozofsoftwareengineering.blog, section "Custom FP8 Quantized Memory
 Block Layout") but give no rule for the scale or the rounding.  Readings used
 here:
   * scale granularity: one fp32 scale per (page, KV head), separately for K
-    and V, fixed when a page is first written (fresh page);
+    and V, set when a page is first written (fresh page);
   * scale value: s = amax / 448 in fp32 (s = 1 when amax == 0), amax taken over
     the tokens that first write fills into that page-head;
+  * a later append into the page whose values exceed its range
+    (amax > 448 s) doubles s until they fit and encodes the page's codes
+    again with the new scale (value decode(c) * s_old in fp32, then the
+    quantiser below); a power-of-two change leaves every code whose value
+    stays in E4M3's normal range exactly representable.  Without it a page
+    whose first fill is a few decode tokens clips the later ones;
   * code: y = x * (1/s) in fp32 (two IEEE-rounded fp32 operations), then
     round-to-nearest-even onto the E4M3 grid with saturation to +-448.
 The fp32 steps are done in numpy float32 so the integer codes are exactly the
@@ -81,6 +87,34 @@ def page_scale(x_tokens):
     if amax == 0:
         return np.float32(1.0)
     return np.float32(amax / np.float32(FP8_MAX))
+
+
+def needs_growth(x_new, scale):
+    """True when values appended to a page written before exceed the page's
+    range: max |x| > 448 * s (fp32 product and comparison)."""
+    if not np.size(x_new):
+        return False
+    amax = np.float32(np.max(np.abs(np.asarray(x_new, dtype=np.float32))))
+    return bool(amax > np.float32(np.float32(FP8_MAX) * np.float32(scale)))
+
+
+def grown_scale(x_new, scale):
+    """The page's scale times the smallest power of two 2^k (k >= 1) with
+    max |x_new| <= 448 * s * 2^k (fp32).  Codes re-encoded under a power-of-two
+    ratio keep their values except where they fall below the normal range."""
+    amax = np.float32(np.max(np.abs(np.asarray(x_new, dtype=np.float32))))
+    s = np.float32(scale)
+    while True:
+        s = np.float32(s * np.float32(2.0))
+        if not amax > np.float32(np.float32(FP8_MAX) * s):
+            return s
+
+
+def reencode(codes, old_scale, new_scale):
+    """Codes of a page encoded again under a larger scale: the value each code
+    stands for, decode(c) * s_old in fp32, quantised with s_new."""
+    v = (decode(codes).astype(np.float32) * np.float32(old_scale)).astype(np.float32)
+    return quantise(v, new_scale)
 
 
 def quantise(x, scale):

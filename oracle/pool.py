@@ -64,6 +64,7 @@ class PoolModel:
         self.refcount = [0] * num_pages
         self.tables = {}      # seq -> list of page ids
         self.lens = {}        # seq -> length in tokens
+        self.scale_growths = 0
         self.cow_copies = 0
         if self.fp8:
             self.kc = np.zeros((num_pages, self.H, self.S, self.d), dtype=np.uint8)
@@ -159,12 +160,20 @@ class PoolModel:
             elif self.fp8:
                 kx = np.asarray(k_new[src], dtype=np.float32)
                 vx = np.asarray(v_new[src], dtype=np.float32)
+                n_old = t0 - blk * self.S            # slots of the page already holding tokens
                 for h in range(self.H):
-                    if p in fresh:
-                        self.ks[p, h] = fp8.page_scale(kx[:, h])
-                        self.vs[p, h] = fp8.page_scale(vx[:, h])
-                    self.kc[p, h, slots] = fp8.quantise(kx[:, h], self.ks[p, h])
-                    self.vc[p, h, slots] = fp8.quantise(vx[:, h], self.vs[p, h])
+                    for codes, scales, x in ((self.kc, self.ks, kx[:, h]), (self.vc, self.vs, vx[:, h])):
+                        if p in fresh:
+                            scales[p, h] = fp8.page_scale(x)
+                        elif fp8.needs_growth(x, scales[p, h]):
+                            # the new values do not fit the page's range: the
+                            # page's scale doubles until they do and its codes
+                            # are encoded again with it
+                            new_scale = fp8.grown_scale(x, scales[p, h])
+                            self.scale_growths += 1
+                            codes[p, h, :n_old] = fp8.reencode(codes[p, h, :n_old], scales[p, h], new_scale)
+                            scales[p, h] = new_scale
+                        codes[p, h, slots] = fp8.quantise(x, scales[p, h])
             else:
                 for h in range(self.H):
                     self.k[p, h, slots] = np.asarray(k_new[src, h], dtype=np.float64)

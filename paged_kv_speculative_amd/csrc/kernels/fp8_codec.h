@@ -6,8 +6,9 @@
 // Per-page scales (atozofsoftwareengineering.blog, section "Custom FP8
 // Quantized Memory Block Layout", per-block scales S_K, S_V): a page-head
 // written for the first time gets s = amax / 448 of the values written into
-// it by that call (1 when amax is 0).  Codes: y = x * (1/s) in fp32, clamped
-// to +-448, rounded to nearest even.
+// it by that call (1 when amax is 0); a later append whose values exceed
+// 448 s doubles s until they fit and re-encodes the page's codes.  Codes:
+// y = x * (1/s) in fp32, clamped to +-448, rounded to nearest even.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,6 +26,19 @@ __device__ inline unsigned char quant_e4m3(float x, float inv) {
 // Scale of a page-head written for the first time, from the largest
 // magnitude of the values written into it.
 __device__ inline float fresh_page_scale(float amax) { return amax == 0.0f ? 1.0f : amax / 448.0f; }
+
+// Scale of a page-head written before, for newly appended values whose
+// largest magnitude is amax: unchanged when amax <= 448 s, else s doubled
+// until it is (fp32 products and comparisons).  Codes already in the page
+// are then encoded again (reencode_e4m3), a power-of-two change of scale.
+__device__ inline float grown_page_scale(float amax, float s) {
+  for (int i = 0; i < 256 && amax > 448.0f * s; ++i) s *= 2.0f;
+  return s;
+}
+
+// A code of a page whose scale grows from s_old to s_new: the value it
+// stands for, decode(c) * s_old in fp32, encoded with s_new.
+__device__ inline unsigned char reencode_e4m3(unsigned char code, float s_old, float inv_new);
 
 // E8M0 exponent byte of the tile scale 2^k for a tile whose largest magnitude
 // is amax: k the smallest integer with amax / 2^k <= 448 = 0.875 * 2^9
@@ -44,6 +58,10 @@ __device__ inline float dequant_e4m3(unsigned char code) {
   const unsigned s = code >> 7, e = (code >> 3) & 15u, m = code & 7u;
   const float mag = e ? ldexpf(float(8 + m), int(e) - 10) : ldexpf(float(m), -9);
   return s ? -mag : mag;
+}
+
+__device__ inline unsigned char reencode_e4m3(unsigned char code, float s_old, float inv_new) {
+  return quant_e4m3(dequant_e4m3(code) * s_old, inv_new);
 }
 
 }  // namespace pkv

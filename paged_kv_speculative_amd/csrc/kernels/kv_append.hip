@@ -108,7 +108,7 @@ __device__ void write_f32(const PoolDevice& dev, const PoolTask& t, int h, int H
 }
 
 // FP8 pool, fp32 source: the head's values stay in registers while the wave
-// reduces amax for a fresh page; K groups of 8 channels are 8 contiguous
+// reduces their amax for the page's scale; K groups of 8 channels are 8 contiguous
 // bytes of the tiled layout (D/4 is a multiple of 16), V is scattered.
 __device__ void write_fp8(const PoolDevice& dev, const PoolTask& t, int h, int H, int D, long pb) {
   const float4* ks = static_cast<const float4*>(dev.k_src);
@@ -133,23 +133,43 @@ __device__ void write_fp8(const PoolDevice& dev, const PoolTask& t, int h, int H
     }
   }
   const long sidx = long(t.page) * H + h;
-  float sk, sv;
-  if (t.flags & kFresh) {
-    ak = wave_max(ak);
-    av = wave_max(av);
-    sk = fresh_page_scale(ak);
-    sv = fresh_page_scale(av);
-    if ((threadIdx.x & 63) == 0) {
-      static_cast<float*>(dev.k_scale)[sidx] = sk;
-      static_cast<float*>(dev.v_scale)[sidx] = sv;
-    }
-  } else {
-    sk = static_cast<const float*>(dev.k_scale)[sidx];
-    sv = static_cast<const float*>(dev.v_scale)[sidx];
-  }
-  const float ik = 1.0f / sk, iv = 1.0f / sv;
   unsigned char* kslab = static_cast<unsigned char*>(dev.k_pages) + sidx * pb;
   unsigned char* vslab = static_cast<unsigned char*>(dev.v_pages) + sidx * pb;
+  ak = wave_max(ak);
+  av = wave_max(av);
+  float sk, sv;
+  if (t.flags & kFresh) {
+    sk = fresh_page_scale(ak);
+    sv = fresh_page_scale(av);
+  } else {
+    // a page written before keeps its scale unless the new values exceed
+    // its range: then the scale doubles until they fit and the slots
+    // already written (0 .. slot_begin - 1) are encoded again
+    const float sk0 = static_cast<const float*>(dev.k_scale)[sidx];
+    const float sv0 = static_cast<const float*>(dev.v_scale)[sidx];
+    sk = grown_page_scale(ak, sk0);
+    sv = grown_page_scale(av, sv0);
+    const int lane = threadIdx.x & 63, n_old = t.slot_begin * D;
+    if (sk != sk0) {
+      const float inv = 1.0f / sk;
+      for (int e = lane; e < n_old; e += 64) {
+        unsigned char& c = kslab[k_index_fp8(e / D, e % D, D)];
+        c = reencode_e4m3(c, sk0, inv);
+      }
+    }
+    if (sv != sv0) {
+      const float inv = 1.0f / sv;
+      for (int e = lane; e < n_old; e += 64) {
+        unsigned char& c = vslab[v_index_fp8(e / D, e % D)];
+        c = reencode_e4m3(c, sv0, inv);
+      }
+    }
+  }
+  if ((threadIdx.x & 63) == 0) {
+    static_cast<float*>(dev.k_scale)[sidx] = sk;
+    static_cast<float*>(dev.v_scale)[sidx] = sv;
+  }
+  const float ik = 1.0f / sk, iv = 1.0f / sv;
 #pragma unroll
   for (int u = 0; u < kItemsPerLane; ++u) {
     if (!im[u].ok) continue;

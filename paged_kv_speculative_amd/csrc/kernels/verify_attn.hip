@@ -218,6 +218,16 @@ __device__ inline f32x4 mfma_bf16_k16(unsigned a0, unsigned a1, unsigned b0, uns
                                                    __builtin_bit_cast(s16x4, u32x2{b0, b1}), c, 0, 0, 0);
 }
 
+// c + A (b_hi + b_lo) over the 16 tokens of a page, with the hi/lo split of
+// P as the two halves of one K = 32 product: lane group j holds tokens
+// 4j..4j+3 of A twice (elements 0-3 and 4-7) against the same tokens' hi
+// parts (0-3) and lo parts (4-7).  One instruction instead of two K = 16
+// ones, which on gfx950 take as many cycles each.
+__device__ inline f32x4 mfma_bf16_split(unsigned a0, unsigned a1, unsigned h0, unsigned h1, unsigned l0, unsigned l1,
+                                        const f32x4& c) {
+  return mfma_bf16(u32x4{a0, a1, a0, a1}, u32x4{h0, h1, l0, l1}, c);
+}
+
 // Compile-time shape of the streaming kernel for one (head_dim, row tiles, KV type).
 // W2: the variant that runs two waves per SIMD (at most 256 registers each),
 // with two pages in flight per wave.
@@ -621,10 +631,15 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, const int*
     ++units_done;
   };
 
-  // P is split into bf16 high and low parts (two MFMAs) for bf16 KV, whose
-  // accuracy target is 2e-3 of rms(O); FP8 KV (target 2e-2) takes P rounded
-  // to bf16 once (relative error <= 2^-9 per weight).
-  constexpr bool kSplitP = !FP8;
+  // P is split into bf16 high and low parts, the two halves of one K = 32
+  // MFMA, so PV is fp32-accurate: for bf16 KV (target 2e-3 of rms(O)) and for
+  // FP8 KV too, where P rounded once to bf16 (relative error <= 2^-9 per
+  // weight) reached 2.8e-2 of rms(O) against a 2e-2 target on pages with a
+  // wide range of magnitudes.
+#ifndef PKV_FP8_SPLIT_P
+#define PKV_FP8_SPLIT_P 1
+#endif
+  constexpr bool kSplitP = !FP8 || PKV_FP8_SPLIT_P;
   auto compute_page = [&](Regs& R, const PageMeta& M) {
     const int tok0 = (M.page + P.pref) * 16;       // positions past the shared prefix (cascade)
     const int L = (M.n & kLenMask) - (M.n >> kNqShift);
@@ -783,12 +798,11 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, const int*
         if (MX) {
           // channels of tile dt lie in 64-channel tile dt / 4
           const int g = (dt >> 2) % PG;
-          acc[dt][nt] = mfma_bf16_k16(v0, v1, pm[g][nt][0], pm[g][nt][1], acc[dt][nt]);
-          acc[dt][nt] = mfma_bf16_k16(v0, v1, pml[g][nt][0], pml[g][nt][1], acc[dt][nt]);
+          acc[dt][nt] = mfma_bf16_split(v0, v1, pm[g][nt][0], pm[g][nt][1], pml[g][nt][0], pml[g][nt][1], acc[dt][nt]);
           continue;
         }
-        acc[dt][nt] = mfma_bf16_k16(v0, v1, ph[nt][0], ph[nt][1], acc[dt][nt]);
-        if (kSplitP) acc[dt][nt] = mfma_bf16_k16(v0, v1, pl[nt][0], pl[nt][1], acc[dt][nt]);
+        if (kSplitP) acc[dt][nt] = mfma_bf16_split(v0, v1, ph[nt][0], ph[nt][1], pl[nt][0], pl[nt][1], acc[dt][nt]);
+        else acc[dt][nt] = mfma_bf16_k16(v0, v1, ph[nt][0], ph[nt][1], acc[dt][nt]);
       }
     }
   };
@@ -1068,8 +1082,19 @@ __global__ __launch_bounds__(kThreads) void verify_fused_merge_kernel(VerifyPara
   // ---- encode the new tokens ---------------------------------------------------
   const int t = N0 + (ok ? j : 0), pj = t >> 4, slot = t & 15;
   // page-head scales: a page first written by this call takes amax / 448 of
-  // the values written into it (per K and V), an older page keeps its scale
+  // the values written into it (per K and V); the partly filled page pa
+  // keeps its scale unless the new values exceed its range, in which case
+  // the scale doubles until they fit and the page's cached slots are encoded
+  // again.  Its old scales are read before this block's barrier, so before
+  // its writer (this block when y = 0) replaces them; a block y > 0 may read
+  // the replaced value, which yields the same grown scale.
   float sk_pg = 1.0f, sv_pg = 1.0f;
+  float sk_old = 1.0f, sv_old = 1.0f;
+  if (fp8 && (N0 & 15) != 0) {
+    const long sidx = long(page_id(pa)) * P.Hkv + g;
+    sk_old = static_cast<const float*>(P.k_scale)[sidx];
+    sv_old = static_cast<const float*>(P.v_scale)[sidx];
+  }
   if (fp8) {
     float ak = 0.0f, av = 0.0f;
 #pragma unroll
@@ -1096,23 +1121,51 @@ __global__ __launch_bounds__(kThreads) void verify_fused_merge_kernel(VerifyPara
     const int q2 = pj - pa;
     const bool fresh = (pj << 4) >= N0;
     const int id = page_id(pj);
-    if (fresh) {
-      float mk = 0.0f, mv = 0.0f;
+    float mk = 0.0f, mv = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        mk = fmaxf(mk, s_amax[q2][0][w]);
-        mv = fmaxf(mv, s_amax[q2][1][w]);
-      }
+    for (int w = 0; w < kWaves; ++w) {
+      mk = fmaxf(mk, s_amax[q2][0][w]);
+      mv = fmaxf(mv, s_amax[q2][1][w]);
+    }
+    if (fresh) {
       sk_pg = fresh_page_scale(mk);
       sv_pg = fresh_page_scale(mv);
     } else {
-      sk_pg = static_cast<const float*>(P.k_scale)[long(id) * P.Hkv + g];
-      sv_pg = static_cast<const float*>(P.v_scale)[long(id) * P.Hkv + g];
+      sk_pg = grown_page_scale(mk, sk_old);
+      sv_pg = grown_page_scale(mv, sv_old);
     }
-    // the item holding slot 0 of a page this call starts writes its scales
-    if (writer && ok && fresh && slot == 0 && c0 == 0) {
+    // the item holding the call's first token of each page writes its scales
+    if (writer && ok && (slot == 0 || t == N0) && c0 == 0) {
       const_cast<float*>(static_cast<const float*>(P.k_scale))[long(id) * P.Hkv + g] = sk_pg;
       const_cast<float*>(static_cast<const float*>(P.v_scale))[long(id) * P.Hkv + g] = sv_pg;
+    }
+    if (writer && (N0 & 15) != 0) {
+      // the cached slots 0 .. N0 % 16 - 1 of page pa under a grown scale
+      float mk0 = 0.0f, mv0 = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        mk0 = fmaxf(mk0, s_amax[0][0][w]);
+        mv0 = fmaxf(mv0, s_amax[0][1][w]);
+      }
+      const float skn = grown_page_scale(mk0, sk_old), svn = grown_page_scale(mv0, sv_old);
+      const long sidx = long(page_id(pa)) * P.Hkv + g;
+      unsigned char* kp = reinterpret_cast<unsigned char*>(const_cast<char*>(P.k_pages) + sidx * P.slab_bytes);
+      unsigned char* vp = reinterpret_cast<unsigned char*>(const_cast<char*>(P.v_pages) + sidx * P.slab_bytes);
+      const int n_old = (N0 & 15) * D;
+      if (skn != sk_old) {
+        const float inv = 1.0f / skn;
+        for (int e = tid; e < n_old; e += kThreads) {
+          unsigned char& c = kp[k_index_fp8(e / D, e % D, D)];
+          c = reencode_e4m3(c, sk_old, inv);
+        }
+      }
+      if (svn != sv_old) {
+        const float inv = 1.0f / svn;
+        for (int e = tid; e < n_old; e += kThreads) {
+          unsigned char& c = vp[v_index_fp8(e / D, e % D)];
+          c = reencode_e4m3(c, sv_old, inv);
+        }
+      }
     }
   }
   if (ok) {
@@ -1351,8 +1404,7 @@ __global__ __launch_bounds__(kThreads) void verify_prefix_kernel(VerifyParams P)
       const unsigned v0 = vc[dt >> 1][w], v1 = vc[dt >> 1][w + 1];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        acc[dt][nt] = mfma_bf16_k16(v0, v1, ph[nt][0], ph[nt][1], acc[dt][nt]);
-        acc[dt][nt] = mfma_bf16_k16(v0, v1, pl[nt][0], pl[nt][1], acc[dt][nt]);
+        acc[dt][nt] = mfma_bf16_split(v0, v1, ph[nt][0], ph[nt][1], pl[nt][0], pl[nt][1], acc[dt][nt]);
       }
     }
 #pragma unroll

@@ -155,9 +155,56 @@ def test_fp8_pool_scale_rule_and_gather():
         assert p.ks[pg1, h] == fp8.page_scale(k[16:, h])
         assert p.vs[pg1, h] == fp8.page_scale(v[16:, h])
     s_before = p.ks[pg1].copy()
-    p.append(0, 10 * k[:3], v[:3])                  # into the tail page: scale kept, saturates
-    assert np.array_equal(p.ks[pg1], s_before)
-    K, V = p.gather(0)
-    assert np.all(np.abs(K[20:]) <= 448 * s_before.max() * (1 + 1e-6))
-    rel = np.abs(K[:20] - k) / np.maximum(np.abs(k), 1e-3)
+    vs_before = p.vs[pg1].copy()
+    K0, V0 = p.gather(0)
+    # values that fit the tail page's range: its scales are kept
+    p.append(0, 0.5 * k[:2], 0.5 * v[:2])
+    assert np.array_equal(p.ks[pg1], s_before) and np.array_equal(p.vs[pg1], vs_before)
+    K1, _ = p.gather(0)
+    assert np.array_equal(K1[:20], K0)
+    # ten times larger K: the page's K scale doubles until they fit, its
+    # cached tokens keep their values (a power-of-two change of scale moves
+    # a normal E4M3 code's exponent only), the new values are not clipped
+    big = 10 * k[:3]
+    p.append(0, big, v[:3])
+    for h in range(2):
+        amax = np.float32(np.max(np.abs(big[:, h])))
+        ratio = float(p.ks[pg1, h] / s_before[h])
+        kexp = int(round(np.log2(ratio)))
+        assert ratio == 2.0 ** kexp and kexp >= 1
+        assert amax <= np.float32(448) * p.ks[pg1, h] and amax > np.float32(448) * p.ks[pg1, h] / 2
+        assert p.vs[pg1, h] == vs_before[h]
+    K2, V2 = p.gather(0)
+    normal = np.abs(K1[16:22]) >= 2.0 ** -6 * 448 * np.max(p.ks[pg1])   # stays above the subnormal range
+    assert np.array_equal(K2[16:22][normal], K1[16:22][normal])
+    rel = np.abs(K2[22:] - big) / np.maximum(np.abs(big), 1e-3)
+    assert np.max(rel[np.abs(big) > 1.0]) <= 2.0 ** -4 + 1e-6          # half an E4M3 step, no clipping
+    rel = np.abs(K0 - k) / np.maximum(np.abs(k), 1e-3)
     assert np.median(rel) < 0.05
+
+
+def test_fp8_scale_growth_keeps_decode_loop_accuracy():
+    """Pages filled by short appends (a decode loop appends gamma + 1 tokens a
+    step) quantise as well as pages written in one call: with a page scale
+    fixed by its first append, later tokens beyond its range were clipped
+    (relative Frobenius error of attention 8.5% with 5-token and 11.6% with
+    1-token appends against 5.5% one-shot, on this workload at 600 tokens);
+    with power-of-two growth the three agree."""
+    from oracle import attention as oa
+    rng = np.random.default_rng(11)
+    Hkv, d, G, nq, L = 2, 64, 4, 5, 256
+    K = rng.standard_normal((L + nq, Hkv, d)).astype(np.float32)
+    V = rng.standard_normal((L + nq, Hkv, d)).astype(np.float32)
+    q = 2.0 * rng.standard_normal((1, nq, Hkv * G, d))
+    R, _ = oa.verify_attention(q, [K.astype(np.float64)], [V.astype(np.float64)], nq, None, 1 / np.sqrt(d))
+    err = {}
+    for step in (L, 5, 1):
+        p = PoolModel(32, 16, Hkv, d, kv_dtype="fp8")
+        p.alloc(0)
+        for t in range(0, L, step):
+            p.append(0, K[t:min(L, t + step)], V[t:min(L, t + step)])
+        p.append(0, K[L:], V[L:])
+        Kq, Vq = p.gather(0)
+        O, _ = oa.verify_attention(q, [Kq], [Vq], nq, None, 1 / np.sqrt(d))
+        err[step] = np.linalg.norm(O - R) / np.linalg.norm(R)
+    assert err[5] <= 1.1 * err[L] and err[1] <= 1.1 * err[L], err
