@@ -99,12 +99,14 @@ struct VerifyParams {
   float* prefix_part;    // cascade: [batch][n_q][Hq][D + 2] (O, max, sum) over the shared prefix
   int* cum;              // [batch + 1] page prefix sums (written by workgroup 0)
   // fused append (spec_verify_attention_append): the pages hold the cached
-  // tokens only, every one visible; a unit finished by one wave writes its
-  // normalised O to out and its log2-sum-exp to unit_lse [batch][n_q][Hq]
-  // (not lse) for the merge, which adds the new tokens; old_len [batch]
-  // keeps the cached lengths
+  // tokens only, every one visible; the merge adds the new tokens; old_len
+  // [batch] keeps the cached lengths
   int fused;
   int kv_kind;           // pkv_dtype of the pool
+  // fused calls and the cascade: a unit finished by one wave writes its
+  // normalised O to out and its log2-sum-exp to unit_lse [batch][n_q][Hq]
+  // (not lse), and the merge combines it with the rest of the row
+  int defer;
   float* unit_lse;
   int* old_len;
   long slab_bytes;       // bytes of one (page, KV head) slab
@@ -567,19 +569,6 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, const int*
       if (local_ok(nt) && (P.fused || r / P.G < u_nq)) {
         const int i = r / P.G, h = u_g * P.G + r % P.G;
         const long oi = long(u_b * P.n_q + i) * P.Hq + h;
-        // cascade: a unit finished here absorbs the shared prefix's partial
-        // (O, max, sum) of its row, written by the prefix pass (fused calls
-        // leave that to the merge)
-        float sa = 1.0f, sb = 0.0f, m_out = m_run[nt];
-        const float* pp = nullptr;
-        if (!FP8 && full && P.pref > 0 && !P.fused) {
-          pp = P.prefix_part + oi * (D + 2);
-          const float mp = pp[D], lp = pp[D + 1];
-          m_out = fmaxf(m_run[nt], mp);
-          sa = exp2_fast(m_run[nt] - m_out);
-          sb = exp2_fast(mp - m_out);
-          l = l * sa + lp * sb;
-        }
         const float inv = full ? 1.0f / l : 1.0f;
         float* dst = full ? P.out + oi * D : part + long(rl) * D;
         if (FP8) {
@@ -592,19 +581,6 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, const int*
                   make_float4(acc[4 * c][nt][e] * inv, acc[4 * c + 1][nt][e] * inv,
                               acc[4 * c + 2][nt][e] * inv, acc[4 * c + 3][nt][e] * inv);
             }
-        } else if (pp) {
-#pragma unroll
-          for (int c = 0; c < D / 32; ++c) {
-            const int ch = c * 32 + 8 * jg;
-            const float4 p0 = *reinterpret_cast<const float4*>(pp + ch);
-            const float4 p1 = *reinterpret_cast<const float4*>(pp + ch + 4);
-            *reinterpret_cast<float4*>(dst + ch) =
-                make_float4((acc[2 * c][nt][0] * sa + p0.x * sb) * inv, (acc[2 * c + 1][nt][0] * sa + p0.y * sb) * inv,
-                            (acc[2 * c][nt][1] * sa + p0.z * sb) * inv, (acc[2 * c + 1][nt][1] * sa + p0.w * sb) * inv);
-            *reinterpret_cast<float4*>(dst + ch + 4) =
-                make_float4((acc[2 * c][nt][2] * sa + p1.x * sb) * inv, (acc[2 * c + 1][nt][2] * sa + p1.y * sb) * inv,
-                            (acc[2 * c][nt][3] * sa + p1.z * sb) * inv, (acc[2 * c + 1][nt][3] * sa + p1.w * sb) * inv);
-          }
         } else {
 #pragma unroll
           for (int c = 0; c < D / 32; ++c) {
@@ -619,8 +595,8 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, const int*
         }
         if (jg == 0) {
           if (full) {
-            if (P.fused) P.unit_lse[oi] = m_run[nt] + __log2f(l);
-            else if (P.lse) P.lse[oi] = (m_out + __log2f(l)) * kLn2;
+            if (P.defer) P.unit_lse[oi] = m_run[nt] + __log2f(l);
+            else if (P.lse) P.lse[oi] = (m_run[nt] + __log2f(l)) * kLn2;
           } else {
             part[long(P.rows_w) * D + rl] = m_run[nt];
             part[long(P.rows_w) * D + P.rows_w + rl] = l;
@@ -912,8 +888,8 @@ __device__ inline void lse_combine(float& M, float& Ls, float4& o, float m, floa
 // The streamed pieces of unit (b, g), row r (output row oi), channels
 // 4 c4 .. 4 c4 + 3, combined into (M, Ls, o).  Returns false when the unit
 // was finished in place by one worker (nothing to merge; in a fused call
-// that worker left its normalised O in out and its log2-sum-exp in
-// unit_lse, which are then combined and true returned).
+// or with the cascade that worker left its normalised O in out and its
+// log2-sum-exp in unit_lse, which are then combined and true returned).
 // The pieces of a split unit are the slots of the workers whose ranges
 // overlap it, found in closed form; each thread issues the loads of up to
 // eight pieces (their maxima, sums and its float4 of O) before combining
@@ -929,7 +905,7 @@ __device__ bool merge_stream_pieces(const VerifyParams& P, int b, int g, int r, 
   const long u0 = long(P.Hkv) * cum[b] + long(g) * np, u1 = u0 + np;
   const int wf = owner_of(u0, W, n_rng), wl = owner_of(u1 - 1, W, n_rng);
   if (wf == wl) {                                 // finished in place
-    if (!P.fused) return false;
+    if (!P.defer) return false;
     lse_combine(M, Ls, o, P.unit_lse[oi], 1.0f, *reinterpret_cast<const float4*>(P.out + oi * D + 4 * c4));
     return true;
   }
@@ -1304,169 +1280,172 @@ __global__ __launch_bounds__(kThreads) void verify_fused_merge_kernel(VerifyPara
 // Shared-prefix pass of the cascade (bf16 KV): the first P.pref pages are the
 // same physical pages for every sequence of the call, and every query sees
 // all of their tokens, so they are attended once for all sequences.  A
-// workgroup takes 32 query rows of one KV head from the flattened (sequence,
-// slot, head) rows (any mix of sequences); its four waves take a quarter of
-// the prefix pages each (the pages stay in L2 for the other workgroups of
-// the head) and combine their (max, sum, O) through LDS into one
-// unnormalised (O, max, sum) per row, which the streaming kernel or the
-// merge absorbs.  Same tiled layout, MFMA orientation and split-P arithmetic
-// as the streaming kernel, without masks.
-constexpr int kPrefixRows = 32;
+// workgroup takes 64 query rows of one KV head from the flattened (sequence,
+// slot, head) rows (any mix of sequences), 16 per wave.  The four waves walk
+// every prefix page together: each page is read once per workgroup into LDS
+// (double-buffered; the loads of the next kPrefixAhead pages are in flight in
+// registers) and every wave reads its MFMA operands from there, so the prefix
+// is read from L2 once per 64 rows.  The walk has no data-dependent branch
+// around its loads and LDS traffic: it runs over whole groups of kPrefixAhead
+// pages, pages past the prefix (read from the first page's address) enter
+// with scores of -inf, and the Q fragments have landed before the first page
+// load, so the load queue is waited on only as deep as each page needs.  Each
+// wave leaves one unnormalised (O, max, sum) per row, which the streaming
+// kernel or the merge absorbs.  Same tiled layout, MFMA orientation and
+// split-P arithmetic as the streaming kernel, without masks.
+constexpr int kPrefixRows = kWaves * 16;
+constexpr int kPrefixAhead = 4;
+
+// A page slab in LDS holds each 1 KB MFMA tile with its 16-byte chunks in
+// (quarter, token) order instead of the pool's (token, quarter) order, so
+// that lane l of a wave reads its operand at byte 16 l of the tile: the
+// linear pattern is the one gfx950 serves at the full LDS rate for 16-byte
+// reads (the pool's order runs at half of it).  Pool chunk of LDS chunk q:
+__device__ inline int prefix_pool_chunk(int q) {
+  return (q & ~63) | ((q & 15) << 2) | ((q >> 4) & 3);
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void verify_prefix_kernel(VerifyParams P) {
-  constexpr int NT = 2, KS = D / 32, DT = D / 16, VL = D / 32;
-  constexpr int RS = D + 4;                      // LDS floats per (wave, row): O, max, sum (16-byte rows)
-  __shared__ float s_part[kWaves][kPrefixRows][RS];
+  constexpr int KS = D / 32, DT = D / 16, VL = D / 32;
+  constexpr int PB = 64 * D;                     // bytes of one (page, head): K slab then V slab
+  constexpr int NCH = PB / 16 / kThreads;        // 16-byte chunks of a page per thread
+  constexpr int F = kPrefixAhead;
+  static_assert((F & (F - 1)) == 0 && F <= 64, "one id per lane for a group of pages");
+  __shared__ __align__(16) unsigned char s_pg[2][PB];
   const int g = blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m16 = lane & 15, jg = lane >> 4;
-  const unsigned lane_off = unsigned(m16 * 64 + jg * 16);
+  const unsigned lane_off = unsigned(lane * 16);
   const int rows_seq = P.n_q * P.G;
   const long R = long(P.batch) * rows_seq;
-  const long r0 = long(blockIdx.y) * kPrefixRows;
+  const long r_lane = long(blockIdx.y) * kPrefixRows + wave * 16 + m16;   // this lane's query row
   const int row_b0 = P.batch_slots ? P.batch_slots[0] : 0;
   const int* bt = P.block_table + long(row_b0) * P.bt_stride;
   // whole pages of the first sequence only (its table has no other entries)
   const int n_pref = min(P.pref, P.seq_lens[row_b0] >> 4);
-  const int p_lo = int(long(n_pref) * wave / kWaves), p_hi = int(long(n_pref) * (wave + 1) / kWaves);
-  u32x4 qf[NT][KS];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const long r = r0 + nt * 16 + m16;
-    const long rr = r < R ? r : r0;
-    const int b = int(rr / rows_seq), rem = int(rr % rows_seq);
-    const int i = rem / P.G, h = g * P.G + rem % P.G;
-    const long oi = long(b * P.n_q + i) * P.Hq + h;
+  const long rq = r_lane < R ? r_lane : 0;       // rows past the batch read row 0 and are not written
+  const int qb = int(rq / rows_seq), qrem = int(rq % rows_seq);
+  const int qi = qrem / P.G, qh = g * P.G + qrem % P.G;
+  const long oi = long(qb * P.n_q + qi) * P.Hq + qh;
+  u32x4 qf[KS];
+  {
     const unsigned short* qp = static_cast<const unsigned short*>(P.q) + oi * D + (D / 4) * jg;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[nt][s] = load16(qp + 8 * s);
+    for (int s = 0; s < KS; ++s) qf[s] = load16(qp + 8 * s);
   }
-  float m_run[NT], l_run[NT];
-  f32x4 acc[DT][NT];
+  float m_run = kNegInf, l_run = 0.0f;
+  f32x4 acc[DT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m_run[nt] = kNegInf;
-    l_run[nt] = 0.0f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt][nt] = f32x4{0, 0, 0, 0};
-  }
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0, 0, 0, 0};
   const long page_stride = long(P.Hkv) * P.slab_bytes;
-  u32x4 kc[KS], vc[VL], kn[KS], vn[VL];
-  auto load = [&](u32x4 (&k)[KS], u32x4 (&v)[VL], int p) {
-    const int id = bt[p];
+  // page ids a group of F pages at a time: lane i of `ids` holds the id of
+  // page p + (i mod F) (past the prefix: the first page's), read with
+  // readlane.  Each group loads the ids of the group after the next one with
+  // a vector load issued before its page loads, so no wait in the walk is
+  // deeper than the page it needs (a scalar load of the table would make
+  // every LDS wait a full one: its returns are out of order)
+  auto group_ids = [&](int p) {
+    const int q = p + (lane & (F - 1));
+    return bt[q < n_pref ? q : 0];
+  };
+  const int ids0 = group_ids(0);
+  int ids_ahead = group_ids(F);
+  // the Q and id loads stay ahead of every page load (the fences of the
+  // barrier keep them there), so waiting for the first page covers them
+  __syncthreads();
+  u32x4 stg[F][NCH];
+  // this thread's LDS chunks q = tid + j * kThreads of the page with id `id`
+  // into ring slot u (the K slab's chunks, then the V slab's); each wave's
+  // load covers one whole 1 KB tile
+  auto fetch = [&](int u, int id) {
     const char* kb = P.k_pages + long(id) * page_stride + long(g) * P.slab_bytes;
     const char* vb = P.v_pages + long(id) * page_stride + long(g) * P.slab_bytes;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) k[s] = load16(kb + lane_off + s * 1024);
-#pragma unroll
-    for (int c = 0; c < VL; ++c) v[c] = load16(vb + lane_off + c * 1024);
+    for (int j = 0; j < NCH; ++j) {
+      const int q = tid + j * kThreads;
+      stg[u][j] = load16(q < PB / 32 ? kb + prefix_pool_chunk(q) * 16 : vb + prefix_pool_chunk(q - PB / 32) * 16);
+    }
   };
-  if (p_lo < p_hi) load(kc, vc, p_lo);
-  for (int p = p_lo; p < p_hi; ++p) {
-    if (p + 1 < p_hi) load(kn, vn, p + 1);     // next page in flight while this one is computed
-    f32x4 sc[NT];
+  auto stage = [&](int u, int buf) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4 a = f32x4{0, 0, 0, 0};
+    for (int j = 0; j < NCH; ++j) *reinterpret_cast<u32x4*>(&s_pg[buf][(tid + j * kThreads) * 16]) = stg[u][j];
+  };
+  // (n_pref is the same for the whole workgroup; the walk is entered only
+  // through the prologue, so no path reaches it with the Q loads in flight)
+  if (n_pref > 0) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) a = mfma_bf16(kc[s], qf[nt][s], a);
+    for (int u = 0; u < F; ++u) fetch(u, __builtin_amdgcn_readlane(ids0, u));
+    stage(0, 0);
+    __syncthreads();
+    for (int p0 = 0; p0 < n_pref; p0 += F) {
+      const int ids_next = group_ids(p0 + 2 * F);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sc[nt][e] = a[e] * P.scale_log2;
-    }
-    unsigned ph[NT][2], pl[NT][2];
+      for (int u = 0; u < F; ++u) {
+        const int p = p0 + u;
+        const float bias = p < n_pref ? 0.0f : kNegInf;
+        const unsigned char* kl = s_pg[p & 1];
+        const unsigned char* vl = kl + PB / 2;
+        u32x4 kc[KS], vc[VL];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const float mx = row_max4(fmaxf(fmaxf(sc[nt][0], sc[nt][1]), fmaxf(sc[nt][2], sc[nt][3])));
-      const bool grow = mx > m_run[nt] + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = grow ? mx : m_run[nt];
-        const float alpha = grow ? exp2_fast(m_run[nt] - m_new) : 1.0f;
-        l_run[nt] *= alpha;
+        for (int s = 0; s < KS; ++s) kc[s] = *reinterpret_cast<const u32x4*>(kl + lane_off + s * 1024);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[dt][nt] *= alpha;
-        m_run[nt] = m_new;
+        for (int c = 0; c < VL; ++c) vc[c] = *reinterpret_cast<const u32x4*>(vl + lane_off + c * 1024);
+        f32x4 sc = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) sc = mfma_bf16(kc[s], qf[s], sc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[e] = fmaf(sc[e], P.scale_log2, bias);
+        const float mx = row_max4(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+        const bool grow = mx > m_run + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float m_new = grow ? mx : m_run;
+          const float alpha = grow ? exp2_fast(m_run - m_new) : 1.0f;
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+          m_run = m_new;
+        }
+        float pv[4], rv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[e] = exp2_fast(sc[e] - m_run);
+        l_run += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rv[e] = pv[e] - __uint_as_float(__float_as_uint(pv[e]) & 0xFFFF0000u);
+        const unsigned ph0 = pack_hi16(pv[0], pv[1]), ph1 = pack_hi16(pv[2], pv[3]);
+        const unsigned pl0 = pack_rne_bf16(rv[0], rv[1]), pl1 = pack_rne_bf16(rv[2], rv[3]);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int w = (dt & 1) * 2;
+          acc[dt] = mfma_bf16_split(vc[dt >> 1][w], vc[dt >> 1][w + 1], ph0, ph1, pl0, pl1, acc[dt]);
+        }
+        // page p + 1 (fetched F - 1 pages ago) into the other buffer, whose
+        // last readers passed the previous barrier; page p + F into the slot
+        // page p used
+        stage((u + 1) % F, (p + 1) & 1);
+        fetch(u, __builtin_amdgcn_readlane(ids_ahead, u));
+        __syncthreads();
       }
-      float pv[4], rv[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pv[e] = exp2_fast(sc[nt][e] - m_run[nt]);
-      l_run[nt] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) rv[e] = pv[e] - __uint_as_float(__float_as_uint(pv[e]) & 0xFFFF0000u);
-      ph[nt][0] = pack_hi16(pv[0], pv[1]);
-      ph[nt][1] = pack_hi16(pv[2], pv[3]);
-      pl[nt][0] = pack_rne_bf16(rv[0], rv[1]);
-      pl[nt][1] = pack_rne_bf16(rv[2], rv[3]);
-    }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int w = (dt & 1) * 2;
-      const unsigned v0 = vc[dt >> 1][w], v1 = vc[dt >> 1][w + 1];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        acc[dt][nt] = mfma_bf16_split(v0, v1, ph[nt][0], ph[nt][1], pl[nt][0], pl[nt][1], acc[dt][nt]);
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < KS; ++s) kc[s] = kn[s];
-#pragma unroll
-    for (int c = 0; c < VL; ++c) vc[c] = vn[c];
-  }
-  // this wave's (O, max, sum) per row into LDS
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float l = l_run[nt];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    float* dst = s_part[wave][nt * 16 + m16];
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      const int ch = c * 32 + 8 * jg;
-      *reinterpret_cast<float4*>(dst + ch) =
-          make_float4(acc[2 * c][nt][0], acc[2 * c + 1][nt][0], acc[2 * c][nt][1], acc[2 * c + 1][nt][1]);
-      *reinterpret_cast<float4*>(dst + ch + 4) =
-          make_float4(acc[2 * c][nt][2], acc[2 * c + 1][nt][2], acc[2 * c][nt][3], acc[2 * c + 1][nt][3]);
-    }
-    if (jg == 0) {
-      dst[D] = m_run[nt];
-      dst[D + 1] = l;
+      ids_ahead = ids_next;
     }
   }
-  __syncthreads();
-  // the four waves' pieces combined: thread t takes row t / 8 and 16 channels
-  const int row = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * (D / 8);
-  const long r = r0 + row;
-  if (r >= R) return;
-  const int b = int(r / rows_seq), rem = int(r % rows_seq);
-  const int i = rem / P.G, h = g * P.G + rem % P.G;
-  const int nq_b = seq_slots(P, b);
-  if (i >= nq_b) return;
-  float M = kNegInf;
+  // this lane's row: unnormalised O over channels c*32 + 8jg .. +7, max, sum
+  float l = l_run;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (r_lane >= R || qi >= seq_slots(P, qb)) return;
+  float* dst = P.prefix_part + oi * (D + 2);
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_part[w][row][D]);
-  const float ref = M == kNegInf ? 0.0f : M;
-  float sc[kWaves], Ls = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    sc[w] = exp2_fast(s_part[w][row][D] - ref);
-    Ls += s_part[w][row][D + 1] * sc[w];
+  for (int c = 0; c < D / 32; ++c) {
+    const int ch = c * 32 + 8 * jg;
+    *reinterpret_cast<float4*>(dst + ch) =
+        make_float4(acc[2 * c][0], acc[2 * c + 1][0], acc[2 * c][1], acc[2 * c + 1][1]);
+    *reinterpret_cast<float4*>(dst + ch + 4) =
+        make_float4(acc[2 * c][2], acc[2 * c + 1][2], acc[2 * c][3], acc[2 * c + 1][3]);
   }
-  float* dst = P.prefix_part + (long(b * P.n_q + i) * P.Hq + h) * (D + 2);
-  for (int c = c0; c < c0 + D / 8; c += 4) {
-    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float4 v = *reinterpret_cast<const float4*>(&s_part[w][row][c]);
-      o.x += v.x * sc[w];
-      o.y += v.y * sc[w];
-      o.z += v.z * sc[w];
-      o.w += v.w * sc[w];
-    }
-    *reinterpret_cast<float4*>(dst + c) = o;
-  }
-  if ((threadIdx.x & 7) == 0) {
-    dst[D] = M;
-    dst[D + 1] = Ls;
+  if (jg == 0) {
+    dst[D] = m_run;
+    dst[D + 1] = l;
   }
 }
 
@@ -1741,8 +1720,11 @@ pkv_status make_plan(const pkv_verify_args* a, Plan* pl) {
   if (st != PKV_OK) return st;
   pl->cum_bytes = 0;
   pl->part_bytes = 0;
+  // cascade: the prefix partials, then the log2-sum-exp of units finished in place
   pl->prefix_bytes = a->shared_prefix_pages > 0
-                         ? size_t(a->batch) * a->n_q * a->num_q_heads * (a->head_dim + 2) * sizeof(float)
+                         ? ((size_t(a->batch) * a->n_q * a->num_q_heads * (a->head_dim + 2) * sizeof(float) + 255) &
+                            ~size_t(255)) +
+                               ((size_t(a->batch) * a->n_q * a->num_q_heads * sizeof(float) + 255) & ~size_t(255))
                          : 0;
   pl->n_wg = 0;
   // a call that spec_verify_attention_append can take also sizes its
@@ -1858,8 +1840,9 @@ namespace {
 
 // Launches a planned call with its scratch at `ws` (at least the plan's
 // bytes): the page prefix sums, the partial results of split units, the
-// cascade's prefix partials and, for a fused call (f not null), the
-// log2-sum-exp of units finished in place and the cached lengths.  None of
+// cascade's prefix partials and log2-sum-exp of units finished in place and,
+// for a fused call (f not null), its own log2-sum-exp of units finished in
+// place and the cached lengths.  None of
 // it has to start at zero: every word the merge reads is written earlier in
 // the same call.
 pkv_status verify_launch(const pkv_verify_args* a, const Plan& pl, void* ws, void* stream,
@@ -1881,9 +1864,16 @@ pkv_status verify_launch(const pkv_verify_args* a, const Plan& pl, void* ws, voi
   p.cum = reinterpret_cast<int*>(w);
   p.part = reinterpret_cast<float*>(w + pl.cum_bytes);
   p.prefix_part = pl.prefix_bytes ? reinterpret_cast<float*>(w + pl.cum_bytes + pl.part_bytes) : nullptr;
+  if (pl.prefix_bytes) {
+    p.defer = 1;
+    p.unit_lse = reinterpret_cast<float*>(
+        w + pl.cum_bytes + pl.part_bytes +
+        ((size_t(a->batch) * a->n_q * a->num_q_heads * (a->head_dim + 2) * sizeof(float) + 255) & ~size_t(255)));
+  }
   if (f) {
     char* fw = w + pl.cum_bytes + pl.part_bytes + pl.prefix_bytes;
     p.fused = 1;
+    p.defer = 1;
     p.unit_lse = reinterpret_cast<float*>(fw);
     p.old_len = reinterpret_cast<int*>(fw + ((size_t(a->batch) * a->n_q * a->num_q_heads * sizeof(float) + 255) &
                                              ~size_t(255)));
@@ -1914,17 +1904,19 @@ pkv_status verify_launch(const pkv_verify_args* a, const Plan& pl, void* ws, voi
   } else if (pl.mx) {
     e = pl.D == 64 ? dispatch_mx<64>(p, pl.NT, pl.tree, s) : dispatch_mx<128>(p, pl.NT, pl.tree, s);
   } else {
-    e = hipSuccess;
-    if (p.pref > 0) {
-      // cascade: the shared prefix once for all sequences, before the tails
+    e = pl.D == 64 ? dispatch_nt<64>(p, pl.NT, pl.fp8, pl.tree, s) : dispatch_nt<128>(p, pl.NT, pl.fp8, pl.tree, s);
+    if (e == hipSuccess && p.pref > 0) {
+      // cascade: the shared prefix once for all sequences.  Neither kernel
+      // reads what the other writes: the streaming kernel leaves the units it
+      // finishes as (normalised O, log2-sum-exp) and the merge combines every
+      // row with its prefix partial, so no wave of the streaming kernel waits
+      // on prefix results.
       const long rows = long(p.batch) * p.n_q * p.G;
       const dim3 grid(p.Hkv, unsigned((rows + kPrefixRows - 1) / kPrefixRows));
       if (pl.D == 64) hipLaunchKernelGGL(verify_prefix_kernel<64>, grid, dim3(kThreads), 0, s, p);
       else hipLaunchKernelGGL(verify_prefix_kernel<128>, grid, dim3(kThreads), 0, s, p);
       e = hipGetLastError();
     }
-    if (e == hipSuccess) e = pl.D == 64 ? dispatch_nt<64>(p, pl.NT, pl.fp8, pl.tree, s)
-                                        : dispatch_nt<128>(p, pl.NT, pl.fp8, pl.tree, s);
   }
   if (e == hipSuccess && !pl.f32) e = pl.D == 64 ? launch_merge<64>(p, f, s) : launch_merge<128>(p, f, s);
   if (e != hipSuccess) return fail(PKV_ERR_DEVICE, std::string("verify launch: ") + hipGetErrorString(e));
