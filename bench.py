@@ -11,8 +11,11 @@ With --fused, steps 1 and 2 are one spec_verify_attention_append call (the
 verification kernels write the new tokens themselves).
 (the accepted lengths are read back to the host each step, as a serving loop
 must to emit tokens).  Inputs are resident in HBM before the timed region.
-Several independent pool instances are used round-robin so that no step finds
-its KV in the 256 MB last-level cache.
+Several independent pool instances (independent batches) are used round-robin
+so that no step finds its KV in the 256 MB last-level cache.  The host issues
+step s + 1 (the next instance) before it waits for step s's accepted lengths,
+as a serving loop overlaps its host work with the GPU; each instance's commit
+still precedes its next append.  --serial issues one step at a time.
 
 Output: one JSON line.  `value` is whole-step throughput in query tokens per
 second (batch * (gamma+1) / step time); `roofline` is measured on the
@@ -54,6 +57,9 @@ def parse():
     ap.add_argument("--fused", action="store_true",
                     help="append the new tokens inside the verification launch "
                          "(spec_verify_attention_append) instead of a separate paged_kv_append")
+    ap.add_argument("--serial", action="store_true",
+                    help="issue one step at a time (the host reads a step's accepted lengths before it "
+                         "issues the next step) instead of keeping the next instance's step queued")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="kept for the counter commands; the 1 GiB reference copy always runs after the steps")
     return ap.parse_args()
@@ -217,70 +223,93 @@ def run_gpu(args, w, torch, api):
             I.accept_call = api.PreparedTreeAccept(I.T, I.D, I.parents, I.tokens, seed=12345)
     seq_ids = np.arange(B, dtype=np.int64)
     n_new = np.full(B, nq, dtype=np.int32)
+    for I in insts:                    # arguments marshalled once, as a serving loop would
+        I.append_call = I.pool.prepare_append(seq_ids, n_new, I.knew, I.vnew)
+        I.rollback_call = I.pool.prepare_rollback(seq_ids)
+    cur = torch.cuda.current_stream()  # the launch stream, looked up once (each lookup costs ~3 us of host time)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(total_steps)]
     acc_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(total_steps)]
     step_lens, accepted = [], []
-    k_host = torch.empty(B, dtype=torch.int32, pin_memory=True)
-    nodes_host = torch.empty((B, nq), dtype=torch.int32, pin_memory=True)
+    # the accepted lengths (and tree nodes) of a step land in one of two pinned
+    # buffers; `done` marks the end of the step's work on the stream
+    k_host = [torch.empty(B, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    nodes_host = [torch.empty((B, nq), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    done = [torch.cuda.Event() for _ in range(2)]
 
-    def step(s):
+    def launch(s):
+        """Steps 1-3 of step s (its instance's append, verification and
+        acceptance) issued on the stream, ending with the accepted lengths'
+        copy to the host."""
         I = insts[s % R]
         if not args.fused:
-            I.pool.append(seq_ids, n_new, I.knew, I.vnew)
+            I.append_call()
         I.lens += nq
         step_lens.append(I.lens.copy())
-        ev[s][0].record()
+        ev[s][0].record(cur)
         if args.fused:
             I.verify_append()
         elif I.graph_v is not None:
             I.graph_v.replay()
         else:
             I.verify()
-        ev[s][1].record()
-        if I.accept:
+        ev[s][1].record(cur)
+        if I.accept or I.tree_accept:
             timed_acc = s % 4 == 0                    # sampled: every event record costs host time
             if timed_acc:
-                acc_ev[s][0].record()
-            if I.graph_a is not None:
+                acc_ev[s][0].record(cur)
+            if I.tree_accept:
+                k, nodes, _ = I.accept_call(step=s)
+                nodes_host[s % 2].copy_(nodes, non_blocking=True)
+            elif I.graph_a is not None:
                 I.graph_a.replay()                    # increments the step counter, then accepts
                 k = I.accept_graph_call.buffers.accepted_len
             else:
                 k, _ = I.accept_call(step=s)
             if timed_acc:
-                acc_ev[s][1].record()
-            k_host.copy_(k, non_blocking=True)        # host needs k (and the tokens) every step
-            torch.cuda.current_stream().synchronize()
-            k = k_host.numpy()
-        elif I.tree_accept:
-            timed_acc = s % 4 == 0
-            if timed_acc:
-                acc_ev[s][0].record()
-            k, nodes, _ = I.accept_call(step=s)
-            if timed_acc:
-                acc_ev[s][1].record()
-            k_host.copy_(k, non_blocking=True)
-            nodes_host.copy_(nodes, non_blocking=True)
-            torch.cuda.current_stream().synchronize()
-            k = k_host.numpy()
-            nd = nodes_host.numpy()
-            accepted.append(k.copy())
+                acc_ev[s][1].record(cur)
+            k_host[s % 2].copy_(k, non_blocking=True)  # host needs k (and the tokens) every step
+        done[s % 2].record(cur)
+
+    def finish(s):
+        """Step 4 of step s once its accepted lengths are on the host: commit
+        1 + k tokens per sequence (rollback of the rest, or the tree path)."""
+        I = insts[s % R]
+        done[s % 2].synchronize()
+        if I.tree_accept:
+            k = k_host[s % 2].numpy().copy()
+            nd = nodes_host[s % 2].numpy()
+            accepted.append(k)
             # keep each accepted branch, drop the rest of the tree
             I.pool.commit_path(seq_ids, n_new, [nd[b, :k[b]] for b in range(B)])
             I.lens -= (nq - 1) - k
             return
-        else:
-            k = np.full(B, gam, dtype=np.int32)
-            torch.cuda.synchronize()
-        accepted.append(k.copy())
+        k = k_host[s % 2].numpy().copy() if I.accept else np.full(B, gam, dtype=np.int32)
+        accepted.append(k)
         drop = (nq - 1) - k
-        I.pool.rollback(seq_ids, drop)
+        I.rollback_call(drop)
         I.lens -= drop
 
-    for s in range(args.warmup):
-        step(s)
+    def run_steps(first, last):
+        """Steps first..last-1.  By default step s + 1 (the next instance: an
+        independent batch) is issued before the host waits for step s's
+        accepted lengths, so the GPU has the next step queued while the host
+        reads k and commits; each instance's commit still precedes its next
+        append on the stream.  --serial issues one step at a time."""
+        for s in range(first, last):
+            if args.serial:
+                launch(s)
+                finish(s)
+                continue
+            launch(s)
+            if s > first:
+                finish(s - 1)
+        if not args.serial and last > first:
+            finish(last - 1)
+
+    run_steps(0, args.warmup)
     torch.cuda.synchronize()
     if args.graph:
         # verification and acceptance of each instance captured once and
@@ -297,8 +326,7 @@ def run_gpu(args, w, torch, api):
                     I.accept_graph_call(step=0)
         torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.warmup, total_steps):
-        step(s)
+    run_steps(args.warmup, total_steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     timed = range(args.warmup, total_steps)
@@ -493,7 +521,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "launch": ("hip-graph (verification, acceptance)" if args.graph else "eager")
-                  + (", append fused into verification" if args.fused else ""),
+                  + (", append fused into verification" if args.fused else "")
+                  + ("; one step at a time" if args.serial
+                     else "; next instance's step queued while the host reads accepted lengths"),
         "vs_baseline": None,
         "dtype": {"fp8": "fp8-kv/bf16", "fp8mx": "fp8-kv(mx64)/bf16"}.get(w.kv_dtype, "bf16"),
         "data": "synthetic",

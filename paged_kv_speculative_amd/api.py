@@ -141,6 +141,16 @@ class Pool:
         st = _stream(stream) if self.device is not None else None
         check(lib.paged_kv_append(self._h, sa.size, sp, np_, kp, vp, src_dtype, st))
 
+    def prepare_append(self, seqs, n_tokens, k_src, v_src):
+        """paged_kv_append of fixed sequences, counts and source buffers with
+        its arguments marshalled once (a serving loop refills k_src, v_src in
+        place and calls it each step)."""
+        return PreparedAppend(self, seqs, n_tokens, k_src, v_src)
+
+    def prepare_rollback(self, seqs):
+        """paged_kv_rollback of fixed sequences; each call takes the counts."""
+        return PreparedRollback(self, seqs)
+
     def rollback(self, seqs, n_tokens, stream=None):
         sa, sp = _ints(seqs, np.int64)
         na, np_ = _ints(n_tokens, np.int32)
@@ -385,6 +395,52 @@ class PreparedVerifyAppend:
         check(lib.spec_verify_attention_append(self.pool._h, self._seqs.size, self._seqs_p, self._kp, self._vp,
                                                C.byref(self.args), _stream(stream)))
         return self.buffers.out, self.buffers.lse
+
+
+class PreparedAppend:
+    """Pool.append with its arguments marshalled once: each call appends
+    n_tokens[i] tokens to sequence seqs[i] from k_src, v_src (read at call
+    time, laid out as for Pool.append)."""
+
+    def __init__(self, pool, seqs, n_tokens, k_src, v_src):
+        self._seqs, sp = _ints(seqs, np.int64)
+        self._n, np_ = _ints(n_tokens, np.int32)
+        assert self._seqs.size == self._n.size
+        if pool.device is None:
+            raise ValueError("a prepared append needs a pool with device memory")
+        total = int(self._n.sum())
+        for name, t in (("k_src", k_src), ("v_src", v_src)):
+            if not t.is_contiguous() or t.data_ptr() % 16 or t.dtype != k_src.dtype:
+                raise ValueError(f"{name} must be contiguous, 16-byte aligned and of k_src's dtype")
+            if t.numel() < total * pool.num_kv_heads * pool.head_dim:
+                raise ValueError(f"{name} holds fewer than the {total} tokens to append")
+            if t.device != k_src.device:
+                raise ValueError(f"{name} is on {t.device}, k_src on {k_src.device}")
+        self._h = pool._h
+        self._call = (C.c_int32(self._seqs.size), C.c_void_p(sp), C.c_void_p(np_), _ptr(k_src), _ptr(v_src),
+                      C.c_int32(_TORCH_SRC[k_src.dtype]))
+        self._keep = (pool, k_src, v_src)
+
+    def __call__(self, stream=None):
+        check(lib.paged_kv_append(self._h, *self._call, _stream(stream)))
+
+
+class PreparedRollback:
+    """Pool.rollback of fixed sequences: each call drops n_tokens[i] (int32
+    array-like, one per sequence) tokens from sequence seqs[i]."""
+
+    def __init__(self, pool, seqs):
+        self._seqs, sp = _ints(seqs, np.int64)
+        self._h, self._nseq, self._sp = pool._h, C.c_int32(self._seqs.size), C.c_void_p(sp)
+        self._device = pool.device is not None
+        self._keep = pool
+
+    def __call__(self, n_tokens, stream=None):
+        na, np_ = _ints(n_tokens, np.int32)
+        if na.size != self._seqs.size:
+            raise ValueError(f"{na.size} counts for {self._seqs.size} sequences")
+        check(lib.paged_kv_rollback(self._h, self._nseq, self._sp, np_,
+                                    _stream(stream) if self._device else None))
 
 
 def _accept_args(target_logits, draft_logits, draft_tokens, seed, step, gammas=None):

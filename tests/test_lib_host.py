@@ -296,3 +296,29 @@ def test_fused_append_needs_device_pool():
     assert _lib.lib.spec_verify_attention_append(p._h, 1, seqs, None, None, C.byref(a), None) == 1
     assert _lib.lib.spec_verify_attention_append(None, 1, seqs, None, None, C.byref(a), None) == 1
     assert (p.table(0), p.stats()) == snap
+
+
+def test_prepared_rollback_matches_rollback_on_host_pool():
+    """Pool.prepare_rollback marshals the sequences once; each call drops the
+    given counts exactly as Pool.rollback does (tables, lengths, free set).  A
+    prepared append needs device memory and is refused on a host-only pool."""
+    order = np.random.default_rng(7).permutation(48)
+    a = Pool(48, 2, 64, "bf16", max_seqs=4, max_pages_per_seq=16, free_order=order)
+    b = Pool(48, 2, 64, "bf16", max_seqs=4, max_pages_per_seq=16, free_order=order)
+    seqs = [0, 1, 2]
+    for p in (a, b):
+        for s in seqs:
+            p.alloc(s)
+        p.append(seqs, [37, 16, 5])
+    rb = b.prepare_rollback(seqs)
+    for drop in ([5, 0, 3], [16, 16, 2], [0, 0, 0]):
+        a.rollback(seqs, drop)
+        rb(np.asarray(drop, dtype=np.int32))
+        assert [a.table(s) for s in seqs] == [b.table(s) for s in seqs]
+        assert a.stats() == b.stats()
+        a.append(seqs, [1, 2, 3])
+        b.append(seqs, [1, 2, 3])
+    with pytest.raises(ValueError):
+        rb([1, 2])                     # one count per sequence
+    with pytest.raises(ValueError):
+        b.prepare_append(seqs, [1, 1, 1], None, None)
