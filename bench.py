@@ -200,6 +200,24 @@ def cascade_pages(args, w):
     return w.prefix_len // 16
 
 
+def schedule_steps(first, last, launch, finish, serial=False):
+    """Steps first..last-1 as launch(s) (append, verification, acceptance
+    issued on the stream) and finish(s) (wait for the accepted lengths, then
+    commit).  By default step s + 1 -- the next instance, an independent
+    batch -- is issued before the host waits for step s, so the GPU has the
+    next step queued while the host reads k and commits; with two or more
+    instances used round-robin, each instance's commit is still issued before
+    its next append.  serial=True issues one step at a time."""
+    for s in range(first, last):
+        launch(s)
+        if serial:
+            finish(s)
+        elif s > first:
+            finish(s - 1)
+    if not serial and last > first:
+        finish(last - 1)
+
+
 def run_gpu(args, w, torch, api):
     B, nq, gam = w.batch, w.n_q, w.gamma
     total_steps = args.steps + args.warmup
@@ -293,21 +311,7 @@ def run_gpu(args, w, torch, api):
         I.lens -= drop
 
     def run_steps(first, last):
-        """Steps first..last-1.  By default step s + 1 (the next instance: an
-        independent batch) is issued before the host waits for step s's
-        accepted lengths, so the GPU has the next step queued while the host
-        reads k and commits; each instance's commit still precedes its next
-        append on the stream.  --serial issues one step at a time."""
-        for s in range(first, last):
-            if args.serial:
-                launch(s)
-                finish(s)
-                continue
-            launch(s)
-            if s > first:
-                finish(s - 1)
-        if not args.serial and last > first:
-            finish(last - 1)
+        schedule_steps(first, last, launch, finish, args.serial)
 
     run_steps(0, args.warmup)
     torch.cuda.synchronize()
