@@ -180,8 +180,6 @@ __device__ inline float advance_levels(float lp, float lq, const float* lz, int 
 }
 
 // Level j (1-based): residual mass of P_{j-1} - Q per chunk, for nodes with
-// more than j children (their (j+1)-th candidate is tested against P_j).
-// Level j (1-based): residual mass of P_{j-1} - Q per chunk, for nodes with
 // more than j children (their (j+1)-th candidate is tested against P_j).  A
 // tree of n nodes has at most (n-1)/(j+1) such nodes; workgroup (sequence,
 // slot, chunk) takes the slot-th of them in index order, if it exists.
@@ -204,6 +202,12 @@ __global__ __launch_bounds__(kLevelThreads) void tree_level_kernel(TreeParams P,
   const int r = b * P.n + u;
   __shared__ float s_lz[kMaxNodes];
   __shared__ float s_l[2];
+  // the chunk's logits do not depend on the normalisers: their loads go out
+  // first and are in flight while the normalisers are gathered
+  float tv[kLevelQuads][4], dv[kLevelQuads][4];
+  const int q0 = chunk * (kLevelChunk / 4);
+  load_chunk<kAligned, kLevelQuads, false, kLevelThreads>(trow(P, b, u), P.vocab, q0, tv);
+  load_chunk<kAligned, kLevelQuads, false, kLevelThreads>(drow(P, b, u), P.vocab, q0, dv);
   // waves 0 and 1: the row normalisers; the others: the earlier levels' masses
   if (wave < 2) {
     const float l = row_lse(P, b, u, wave);
@@ -216,10 +220,6 @@ __global__ __launch_bounds__(kLevelThreads) void tree_level_kernel(TreeParams P,
   }
   __syncthreads();
   const float lt = s_l[0], ld = s_l[1];
-  float tv[kLevelQuads][4], dv[kLevelQuads][4];
-  const int q0 = chunk * (kLevelChunk / 4);
-  load_chunk<kAligned, kLevelQuads, false, kLevelThreads>(trow(P, b, u), P.vocab, q0, tv);
-  load_chunk<kAligned, kLevelQuads, false, kLevelThreads>(drow(P, b, u), P.vocab, q0, dv);
   float s = 0.0f;
 #pragma unroll
   for (int qq = 0; qq < kLevelQuads; ++qq)
