@@ -1290,9 +1290,9 @@ __global__ __launch_bounds__(kThreads) void verify_fused_merge_kernel(VerifyPara
 // pages, pages past the prefix (read from the first page's address) enter
 // with scores of -inf, and the Q fragments have landed before the first page
 // load, so the load queue is waited on only as deep as each page needs.  Each
-// wave leaves one unnormalised (O, max, sum) per row, which the streaming
-// kernel or the merge absorbs.  Same tiled layout, MFMA orientation and
-// split-P arithmetic as the streaming kernel, without masks.
+// wave leaves one unnormalised (O, max, sum) per row, which the merge (plain
+// or fused) combines with the row's streamed pieces.  Same tiled layout, MFMA
+// orientation and split-P arithmetic as the streaming kernel, without masks.
 constexpr int kPrefixRows = kWaves * 16;
 constexpr int kPrefixAhead = 4;
 
