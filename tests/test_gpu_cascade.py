@@ -3,7 +3,7 @@ pages common to every sequence are attended once for all sequences and merged
 with each sequence's own pages.  Checked against the oracle (which gathers
 every sequence's full K/V and knows nothing of the sharing), for the split
 counts that put units in place and across workers, at full size, with
-per-sequence draft counts, and against the plain call."""
+per-sequence draft counts, through batch_slots, and against the plain call."""
 import numpy as np
 import pytest
 import torch
@@ -72,6 +72,25 @@ def test_cascade_with_per_sequence_counts():
         Or, Lr = oa.verify_attention(qf[b:b + 1, :n_b], [K], [V], n_b, None, float(w.sm_scale))
         H.compare(O[b:b + 1, :n_b], L[b:b + 1, :n_b], Or, Lr, H.TOL["bf16"])
         assert np.all(O[b, n_b:] == 7.0)
+
+
+@pytest.mark.parametrize("splits", [0, 5])
+def test_cascade_with_batch_slots(splits):
+    """A permuted subset of the pool's rows (batch_slots) with the cascade:
+    the prefix pass reads the shared pages through the first listed row (not
+    row 0), and every listed sequence matches the oracle."""
+    w = wl.make(5, small=True)
+    g = H.GpuSide(w)
+    rows = [w.batch - 1, 0, w.batch // 2]
+    slots = torch.tensor(rows, dtype=torch.int32, device="cuda")
+    q = g.q[rows].contiguous()
+    from paged_kv_speculative_amd import spec_verify_attention
+    O, L = spec_verify_attention(q, g.pool.k_pages, g.pool.v_pages, g.pool.block_table, g.pool.seq_lens,
+                                 n_q=w.n_q, num_kv_heads=w.num_kv_heads, kv_dtype="bf16", batch_slots=slots,
+                                 sm_scale=w.sm_scale, num_splits=splits,
+                                 shared_prefix_pages=w.prefix_len // 16)
+    O_ref, L_ref = H.oracle_verify(w, rows)
+    H.compare(O.cpu().numpy(), L.cpu().numpy(), O_ref, L_ref, H.TOL["bf16"])
 
 
 def test_cascade_rejects_fp8():
