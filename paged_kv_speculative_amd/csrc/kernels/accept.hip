@@ -155,9 +155,29 @@ __global__ __launch_bounds__(kThreads) void accept_draw_kernel(AcceptParams P) {
       dx = P.Dl[(long(b) * P.gamma + t) * P.vocab + x];
     }
   }
-  // log normalisers of the sequence's rows from the chunk partials: wave w
-  // takes rows w, w + 4, ... four at a time, lane c chunks c, c + 64, ...
+  // log normalisers of the sequence's rows from the chunk partials.  Up to
+  // 16 partials per row (vocabularies up to 16 stats chunks): each 16-lane
+  // group of a wave reduces one row, lane l16 holding chunk l16, so a wave
+  // covers four rows in four shuffle steps (waves 0.. take rows 4w .. 4w+3).
+  // Otherwise wave w takes rows w, w + 4, ... four at a time, lane c chunks
+  // c, c + 64, ...
   const float2* st = P.stats + long(b) * rows_per_seq * P.schunks;
+  if (P.schunks <= 16) {
+    const int r = 4 * wave + (lane >> 4), c = lane & 15;
+    float2 v = r < rows_per_seq && c < P.schunks ? st[long(r) * P.schunks + c] : make_float2(kNegInf, 0.0f);
+    for (int o = 8; o > 0; o >>= 1) combine_ms(v.x, v.y, __shfl_xor(v.x, o, 64), __shfl_xor(v.y, o, 64));
+    if (c == 0 && r < rows_per_seq) s_lse[r] = v.x + log2_hw(v.y);
+    for (int r1 = 4 * kWaves + wave; r1 < rows_per_seq; r1 += kWaves) {   // rows past 4 per wave
+      float m = kNegInf, sm = 0.0f;
+      if (lane < P.schunks) {
+        const float2 w = st[long(r1) * P.schunks + lane];
+        m = w.x;
+        sm = w.y;
+      }
+      for (int o = 8; o > 0; o >>= 1) combine_ms(m, sm, __shfl_xor(m, o, 64), __shfl_xor(sm, o, 64));
+      if (lane == 0) s_lse[r1] = m + log2_hw(sm);
+    }
+  } else
   for (int r0 = wave; r0 < rows_per_seq; r0 += 4 * kWaves) {
     float m[4], sm[4];
 #pragma unroll
