@@ -194,8 +194,8 @@ class Instance:
 
 def cascade_pages(args, w):
     """Whole pages of the shared prefix attended once for all sequences
-    (bf16 KV; off with --no-cascade)."""
-    if args.no_cascade or not w.prefix_len or w.kv_dtype != "bf16":
+    (bf16 and per-page-scale FP8 KV; off with --no-cascade)."""
+    if args.no_cascade or not w.prefix_len or w.kv_dtype not in ("bf16", "fp8"):
         return 0
     return w.prefix_len // 16
 

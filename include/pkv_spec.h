@@ -275,7 +275,8 @@ typedef struct {
   int32_t num_splits;         /* workgroups sharing the work; 0 = as many as the
                                  GPU keeps resident                              */
   const int32_t* n_q_seq;     /* device [batch] slots per sequence, or NULL (n_q) */
-  int32_t shared_prefix_pages;/* cascade (bf16 KV): the first this-many block-table
+  int32_t shared_prefix_pages;/* cascade (bf16 KV, or FP8_E4M3 with per-page scales;
+                                 FP8_E4M3_MX64 returns PKV_ERR_UNSUPPORTED): the first this-many block-table
                                  entries are the same physical pages for every
                                  sequence of the call (a prefix shared through
                                  paged_kv_alloc) and hold cached tokens only

@@ -1277,9 +1277,10 @@ __global__ __launch_bounds__(kThreads) void verify_fused_merge_kernel(VerifyPara
   }
 }
 
-// Shared-prefix pass of the cascade (bf16 KV): the first P.pref pages are the
-// same physical pages for every sequence of the call, and every query sees
-// all of their tokens, so they are attended once for all sequences.  A
+// Shared-prefix pass of the cascade (bf16 or FP8 KV with per-page scales):
+// the first P.pref pages are the same physical pages for every sequence of
+// the call, and every query sees all of their tokens, so they are attended
+// once for all sequences.  A
 // workgroup takes 64 query rows of one KV head from the flattened (sequence,
 // slot, head) rows (any mix of sequences), 16 per wave.  The four waves walk
 // every prefix page together: each page is read once per workgroup into LDS
@@ -1300,19 +1301,31 @@ constexpr int kPrefixAhead = 4;
 // (quarter, token) order instead of the pool's (token, quarter) order, so
 // that lane l of a wave reads its operand at byte 16 l of the tile: the
 // linear pattern is the one gfx950 serves at the full LDS rate for 16-byte
-// reads (the pool's order runs at half of it).  Pool chunk of LDS chunk q:
+// reads (the pool's order runs at half of it).  Pool chunk of LDS chunk q,
+// and LDS chunk of pool chunk x:
 __device__ inline int prefix_pool_chunk(int q) {
   return (q & ~63) | ((q & 15) << 2) | ((q >> 4) & 3);
 }
+__device__ inline int prefix_lds_chunk(int x) {
+  return (x & ~63) | ((x & 3) << 4) | ((x >> 2) & 15);
+}
 
-template <int D>
+// FP8 pages (per-page scales): each 16-byte group of the pool's FP8 slab is
+// decoded while it is staged, into the two bf16 chunks it makes (in byte
+// order: K group x = 64 s2 + 4 t + j gives bf16 chunks x + 64 s2 and that
+// + 64, V group x = 4 qc + quad gives x + 4 qc and that + 4), so the waves
+// read the same bf16 operand layout as for bf16 pages.  The page's K scale
+// multiplies its scores and its V scale its P, as in the streaming kernel.
+template <int D, bool FP8>
 __global__ __launch_bounds__(kThreads) void verify_prefix_kernel(VerifyParams P) {
   constexpr int KS = D / 32, DT = D / 16, VL = D / 32;
-  constexpr int PB = 64 * D;                     // bytes of one (page, head): K slab then V slab
-  constexpr int NCH = PB / 16 / kThreads;        // 16-byte chunks of a page per thread
+  constexpr int PB = 64 * D;                     // bf16 bytes of one (page, head) in LDS: K slab then V slab
+  constexpr int SB = FP8 ? 32 * D : PB;          // pool bytes of one (page, head)
+  constexpr int NCH = (SB / 16 + kThreads - 1) / kThreads;   // 16-byte pool chunks of a page per thread
   constexpr int F = kPrefixAhead;
   static_assert((F & (F - 1)) == 0 && F <= 64, "one id per lane for a group of pages");
   __shared__ __align__(16) unsigned char s_pg[2][PB];
+  __shared__ float s_sc[2][2];                   // FP8: the staged page's K and V scales
   const int g = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m16 = lane & 15, jg = lane >> 4;
@@ -1355,21 +1368,53 @@ __global__ __launch_bounds__(kThreads) void verify_prefix_kernel(VerifyParams P)
   // barrier keep them there), so waiting for the first page covers them
   __syncthreads();
   u32x4 stg[F][NCH];
-  // this thread's LDS chunks q = tid + j * kThreads of the page with id `id`
-  // into ring slot u (the K slab's chunks, then the V slab's); each wave's
-  // load covers one whole 1 KB tile
+  float sc_k[F], sc_v[F];                        // FP8: ring slot's scales (thread 0)
+  // bf16: this thread's LDS chunks q = tid + j * kThreads of the page with id
+  // `id` into ring slot u (the K slab's chunks, then the V slab's); each
+  // wave's load covers one whole 1 KB tile.  FP8: pool group q of the page
+  // (K slab, then V slab), and thread 0 the page's two scales.
   auto fetch = [&](int u, int id) {
     const char* kb = P.k_pages + long(id) * page_stride + long(g) * P.slab_bytes;
     const char* vb = P.v_pages + long(id) * page_stride + long(g) * P.slab_bytes;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int q = tid + j * kThreads;
-      stg[u][j] = load16(q < PB / 32 ? kb + prefix_pool_chunk(q) * 16 : vb + prefix_pool_chunk(q - PB / 32) * 16);
+      if (FP8) {
+        if (q < SB / 16) stg[u][j] = load16(q < SB / 32 ? kb + q * 16 : vb + (q - SB / 32) * 16);
+      } else {
+        stg[u][j] = load16(q < PB / 32 ? kb + prefix_pool_chunk(q) * 16 : vb + prefix_pool_chunk(q - PB / 32) * 16);
+      }
+    }
+    if (FP8 && tid == 0) {
+      sc_k[u] = static_cast<const float*>(P.k_scale)[long(id) * P.Hkv + g];
+      sc_v[u] = static_cast<const float*>(P.v_scale)[long(id) * P.Hkv + g];
     }
   };
   auto stage = [&](int u, int buf) {
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) *reinterpret_cast<u32x4*>(&s_pg[buf][(tid + j * kThreads) * 16]) = stg[u][j];
+    for (int j = 0; j < NCH; ++j) {
+      const int q = tid + j * kThreads;
+      if (FP8) {
+        if (q < SB / 16) {
+          const u32x4 w = stg[u][j];
+          const Dw2 a0 = fp8x4_to_bf16x4(w[0]), a1 = fp8x4_to_bf16x4(w[1]);
+          const Dw2 a2 = fp8x4_to_bf16x4(w[2]), a3 = fp8x4_to_bf16x4(w[3]);
+          const bool isk = q < SB / 32;
+          const int x = isk ? q : q - SB / 32;                  // group within its slab
+          const int lo = isk ? x + (x >> 6) * 64 : x + (x >> 2) * 4;
+          const int hi = lo + (isk ? 64 : 4);
+          unsigned char* base = &s_pg[buf][isk ? 0 : PB / 2];
+          *reinterpret_cast<u32x4*>(base + prefix_lds_chunk(lo) * 16) = u32x4{a0.lo, a0.hi, a1.lo, a1.hi};
+          *reinterpret_cast<u32x4*>(base + prefix_lds_chunk(hi) * 16) = u32x4{a2.lo, a2.hi, a3.lo, a3.hi};
+        }
+      } else {
+        *reinterpret_cast<u32x4*>(&s_pg[buf][q * 16]) = stg[u][j];
+      }
+    }
+    if (FP8 && tid == 0) {
+      s_sc[buf][0] = sc_k[u];
+      s_sc[buf][1] = sc_v[u];
+    }
   };
   // (n_pref is the same for the whole workgroup; the walk is entered only
   // through the prologue, so no path reaches it with the Q loads in flight)
@@ -1394,8 +1439,9 @@ __global__ __launch_bounds__(kThreads) void verify_prefix_kernel(VerifyParams P)
         f32x4 sc = f32x4{0, 0, 0, 0};
 #pragma unroll
         for (int s = 0; s < KS; ++s) sc = mfma_bf16(kc[s], qf[s], sc);
+        const float ksc = FP8 ? P.scale_log2 * s_sc[p & 1][0] : P.scale_log2;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sc[e] = fmaf(sc[e], P.scale_log2, bias);
+        for (int e = 0; e < 4; ++e) sc[e] = fmaf(sc[e], ksc, bias);
         const float mx = row_max4(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
         const bool grow = mx > m_run + kRescaleSlack;
         if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -1410,6 +1456,11 @@ __global__ __launch_bounds__(kThreads) void verify_prefix_kernel(VerifyParams P)
 #pragma unroll
         for (int e = 0; e < 4; ++e) pv[e] = exp2_fast(sc[e] - m_run);
         l_run += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+        if (FP8) {
+          const float vsc = s_sc[p & 1][1];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pv[e] *= vsc;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) rv[e] = pv[e] - __uint_as_float(__float_as_uint(pv[e]) & 0xFFFF0000u);
         const unsigned ph0 = pack_hi16(pv[0], pv[1]), ph1 = pack_hi16(pv[2], pv[3]);
@@ -1595,8 +1646,8 @@ pkv_status check_args(const pkv_verify_args* a, Plan* pl) {
   if (!a->q || !a->k_pages || !a->v_pages || !a->block_table || !a->seq_lens)
     return fail(PKV_ERR_INVALID_ARG, "null device pointer");
   if (a->shared_prefix_pages < 0) return fail(PKV_ERR_INVALID_ARG, "shared_prefix_pages must be >= 0");
-  if (a->shared_prefix_pages > 0 && a->kv_dtype != PKV_BF16)
-    return fail(PKV_ERR_UNSUPPORTED, "the shared-prefix pass supports bf16 KV");
+  if (a->shared_prefix_pages > 0 && a->kv_dtype != PKV_BF16 && a->kv_dtype != PKV_FP8_E4M3)
+    return fail(PKV_ERR_UNSUPPORTED, "the shared-prefix pass supports bf16 and per-page-scale FP8 KV");
   if (a->num_splits < 0 || a->num_splits > 1024)
     return fail(PKV_ERR_INVALID_ARG, "num_splits must be in [0, 1024]");
   const int G = a->num_q_heads / a->num_kv_heads;
@@ -1913,8 +1964,13 @@ pkv_status verify_launch(const pkv_verify_args* a, const Plan& pl, void* ws, voi
       // on prefix results.
       const long rows = long(p.batch) * p.n_q * p.G;
       const dim3 grid(p.Hkv, unsigned((rows + kPrefixRows - 1) / kPrefixRows));
-      if (pl.D == 64) hipLaunchKernelGGL(verify_prefix_kernel<64>, grid, dim3(kThreads), 0, s, p);
-      else hipLaunchKernelGGL(verify_prefix_kernel<128>, grid, dim3(kThreads), 0, s, p);
+      if (pl.D == 64) {
+        if (pl.fp8) hipLaunchKernelGGL((verify_prefix_kernel<64, true>), grid, dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((verify_prefix_kernel<64, false>), grid, dim3(kThreads), 0, s, p);
+      } else {
+        if (pl.fp8) hipLaunchKernelGGL((verify_prefix_kernel<128, true>), grid, dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((verify_prefix_kernel<128, false>), grid, dim3(kThreads), 0, s, p);
+      }
       e = hipGetLastError();
     }
   }

@@ -3,7 +3,8 @@ pages common to every sequence are attended once for all sequences and merged
 with each sequence's own pages.  Checked against the oracle (which gathers
 every sequence's full K/V and knows nothing of the sharing), for the split
 counts that put units in place and across workers, at full size, with
-per-sequence draft counts, through batch_slots, and against the plain call."""
+per-sequence draft counts, through batch_slots, and against the plain call;
+for bf16 KV and for FP8 KV with per-page scales."""
 import numpy as np
 import pytest
 import torch
@@ -93,8 +94,56 @@ def test_cascade_with_batch_slots(splits):
     H.compare(O.cpu().numpy(), L.cpu().numpy(), O_ref, L_ref, H.TOL["bf16"])
 
 
-def test_cascade_rejects_fp8():
-    w = wl.make(4, small=True, batch=2)
+def _fp8(w, kv="fp8"):
+    w.kv_dtype = kv
+    return w
+
+
+@pytest.mark.parametrize("splits", [0, 1, 7])
+def test_cascade_fp8_matches_oracle(splits):
+    """FP8 KV with per-page scales: the prefix pass decodes each page while
+    staging it and applies the page's K and V scales; against the oracle's
+    replay of the same quantised appends."""
+    w = _fp8(wl.make(5, small=True))
+    g = H.GpuSide(w)
+    O, L = g.verify(shared_prefix_pages=w.prefix_len // 16, num_splits=splits)
+    O_ref, L_ref = H.oracle_verify(w, range(w.batch))
+    H.compare(O.cpu().numpy(), L.cpu().numpy(), O_ref, L_ref, H.TOL["fp8"])
+
+
+def test_cascade_fp8_equals_plain_call():
+    """Same FP8 pool with and without the cascade: the same decoded values and
+    scales, combined in another order.  Both passes feed each weight p to the
+    bf16 products as a truncated high half plus a rounded remainder, which
+    keeps p to 2^-16 of itself, so each side's O is within 2^-16 max|V| of
+    the exact combination of the same decoded pages, and the two sides within
+    twice that (plus fp32 reordering, far below it)."""
+    w = _fp8(wl.make(5, small=True, batch=9))
+    g = H.GpuSide(w)
+    O1, L1 = (x.clone() for x in g.verify())
+    O2, L2 = g.verify(shared_prefix_pages=w.prefix_len // 16)
+    O1, L1, O2, L2 = (x.cpu().numpy() for x in (O1, L1, O2, L2))
+    vmax = max([float(np.abs(w.prefix_kv()[1]).max())] +
+               [float(np.abs(w.private_kv(b)[1]).max()) for b in range(w.batch)])
+    tol = 2.0 ** -15 * vmax * 1.1                 # 1.1: FP8 rounding may round a value up
+    assert np.max(np.abs(O1 - O2)) <= tol and np.max(np.abs(L1 - L2)) <= 1e-4
+
+
+def test_cascade_fp8_full_size_sampled():
+    w = _fp8(wl.make(5))
+    print(f"cascade fp8 full: B={w.batch} prefix={w.prefix_len}", flush=True)
+    g = H.GpuSide(w)
+    O, L = g.verify(shared_prefix_pages=w.prefix_len // 16)
+    O, L = O.cpu().numpy(), L.cpu().numpy()
+    rng = np.random.default_rng(6)
+    sample = sorted(set([0, w.batch - 1, int(np.argmax(w.seq_lens))] + list(rng.choice(w.batch, 2, replace=False))))
+    O_ref, L_ref = H.oracle_verify(w, sample)
+    H.compare(O[sample], L[sample], O_ref, L_ref, H.TOL["fp8"])
+
+
+def test_cascade_rejects_fp8mx():
+    """Per-64-channel FP8 scales are not supported by the prefix pass."""
+    w = _fp8(wl.make(5, small=True, batch=2), "fp8mx")
     g = H.GpuSide(w)
     with pytest.raises(PkvError):
-        g.verify(shared_prefix_pages=1)
+        g.verify(shared_prefix_pages=w.prefix_len // 16)

@@ -48,7 +48,7 @@ def _workload(cfg, kv=None, small=True):
 
 @pytest.mark.parametrize("cfg,kv,splits", [(2, "bf16", 0), (2, "fp8", 0), (2, "fp8mx", 0), (2, "bf16", 11),
                                            (4, "fp8", 0), (4, "fp8mx", 0), (4, "bf16", 5), (5, "bf16", 0),
-                                           (3, "bf16", 0)])
+                                           (5, "fp8", 0), (5, "fp8", 7), (3, "bf16", 0)])
 def test_fused_equals_append_then_verify(cfg, kv, splits):
     w = _workload(cfg, kv)
     print(f"fused cfg {cfg} kv={kv} splits={splits} B={w.batch} n_q={w.n_q}", flush=True)

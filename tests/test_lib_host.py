@@ -269,7 +269,9 @@ def test_argument_checks_of_newer_fields():
     a.block_table_stride = 8
     n = C.c_size_t()
     a.shared_prefix_pages = 1
-    assert lib.spec_verify_workspace_size(C.byref(a), C.byref(n)) == 5       # cascade needs bf16 KV
+    assert lib.spec_verify_workspace_size(C.byref(a), C.byref(n)) == 0       # per-page FP8 scales: accepted
+    a.kv_dtype = _lib.FP8_E4M3_MX64
+    assert lib.spec_verify_workspace_size(C.byref(a), C.byref(n)) == 5       # per-64-channel scales: not
     a.kv_dtype, a.shared_prefix_pages = _lib.BF16, -1
     assert lib.spec_verify_workspace_size(C.byref(a), C.byref(n)) == 1
     t = _lib.TreeAcceptArgs()
