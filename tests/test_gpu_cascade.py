@@ -111,6 +111,19 @@ def test_cascade_fp8_matches_oracle(splits):
     H.compare(O.cpu().numpy(), L.cpu().numpy(), O_ref, L_ref, H.TOL["fp8"])
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("splits", [0, 7])
+def test_cascade_head_dim_64(kv, splits):
+    """The d = 64 prefix pass (half the tiles per page; for FP8 half the
+    threads stage a page) against the oracle."""
+    w = _fp8(wl.make(5, small=True), kv)
+    w.head_dim = 64
+    g = H.GpuSide(w)
+    O, L = g.verify(shared_prefix_pages=w.prefix_len // 16, num_splits=splits)
+    O_ref, L_ref = H.oracle_verify(w, range(w.batch))
+    H.compare(O.cpu().numpy(), L.cpu().numpy(), O_ref, L_ref, H.TOL[kv])
+
+
 def test_cascade_fp8_equals_plain_call():
     """Same FP8 pool with and without the cascade: the same decoded values and
     scales, combined in another order.  Both passes feed each weight p to the
