@@ -33,6 +33,10 @@ __device__ inline float wave_max(float v) {
 
 
 // Item it of a task (token it / G, channel group it % G) for the calling lane.
+// An item past the task's tokens reads the task's first source row instead
+// (valid whenever the task has tokens) and stores nothing: every source load
+// is then issued unconditionally, all of a lane's loads back to back (loads
+// behind a branch were issued one at a time, each waited for).
 struct Item {
   bool ok;
   int slot, c0;
@@ -44,7 +48,7 @@ __device__ inline Item item(const PoolTask& t, int u, int h, int H, int D) {
   const int it = u * 64 + int(threadIdx.x & 63);
   Item r;
   r.ok = it < t.n * G;
-  const int tok = it / G;
+  const int tok = r.ok ? it / G : 0;
   r.c0 = (it % G) * 8;
   r.slot = t.slot_begin + tok;
   r.src = (long(t.src_row) + tok) * H * D + long(h) * D + r.c0;
@@ -53,58 +57,63 @@ __device__ inline Item item(const PoolTask& t, int u, int h, int H, int D) {
 
 // bf16 pool, bf16 source: 16-byte loads; K groups of 8 channels are
 // contiguous in the tiled layout (D/4 is a multiple of 8), V is scattered.
+// The items are named values, not arrays: arrays indexed in these loops were
+// placed in LDS by the compiler (before the loops are unrolled), and every
+// source load then waited for its LDS copy.
 __device__ void write_bf16(const PoolDevice& dev, const PoolTask& t, int h, int H, int D, long pb) {
+  static_assert(kItemsPerLane == 4, "four named items per lane");
   const uint4* ks = static_cast<const uint4*>(dev.k_src);
   const uint4* vs = static_cast<const uint4*>(dev.v_src);
-  uint4 kx[kItemsPerLane], vx[kItemsPerLane];
-  Item im[kItemsPerLane];
-#pragma unroll
-  for (int u = 0; u < kItemsPerLane; ++u) {
-    im[u] = item(t, u, h, H, D);
-    if (im[u].ok) {
-      kx[u] = ks[im[u].src / 8];
-      vx[u] = vs[im[u].src / 8];
-    }
-  }
+  const Item i0 = item(t, 0, h, H, D), i1 = item(t, 1, h, H, D), i2 = item(t, 2, h, H, D),
+             i3 = item(t, 3, h, H, D);
+  const uint4 k0 = ks[i0.src / 8], k1 = ks[i1.src / 8], k2 = ks[i2.src / 8], k3 = ks[i3.src / 8];
+  const uint4 v0 = vs[i0.src / 8], v1 = vs[i1.src / 8], v2 = vs[i2.src / 8], v3 = vs[i3.src / 8];
   char* kslab = static_cast<char*>(dev.k_pages) + (long(t.page) * H + h) * pb;
   unsigned short* vslab = reinterpret_cast<unsigned short*>(static_cast<char*>(dev.v_pages) + (long(t.page) * H + h) * pb);
-#pragma unroll
-  for (int u = 0; u < kItemsPerLane; ++u) {
-    if (!im[u].ok) continue;
-    *reinterpret_cast<uint4*>(kslab + 2 * k_index_bf16(im[u].slot, im[u].c0, D)) = kx[u];
-    const unsigned w[4] = {vx[u].x, vx[u].y, vx[u].z, vx[u].w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      vslab[v_index_bf16(im[u].slot, im[u].c0 + i)] = static_cast<unsigned short>(w[i / 2] >> (16 * (i % 2)));
-  }
+  auto put = [&](const Item& im, const uint4& kx, const uint4& vx) {
+    if (!im.ok) return;
+    *reinterpret_cast<uint4*>(kslab + 2 * k_index_bf16(im.slot, im.c0, D)) = kx;
+    auto v2 = [&](int i, unsigned w) {           // channels c0 + i, c0 + i + 1
+      vslab[v_index_bf16(im.slot, im.c0 + i)] = static_cast<unsigned short>(w);
+      vslab[v_index_bf16(im.slot, im.c0 + i + 1)] = static_cast<unsigned short>(w >> 16);
+    };
+    v2(0, vx.x);
+    v2(2, vx.y);
+    v2(4, vx.z);
+    v2(6, vx.w);
+  };
+  put(i0, k0, v0);
+  put(i1, k1, v1);
+  put(i2, k2, v2);
+  put(i3, k3, v3);
 }
 
-// fp32 pool, fp32 source: row-major slab, two 16-byte moves per group.
+// fp32 pool, fp32 source: row-major slab, two 16-byte moves per group (named
+// values, as for bf16).
 __device__ void write_f32(const PoolDevice& dev, const PoolTask& t, int h, int H, int D, long pb) {
+  static_assert(kItemsPerLane == 4, "four named items per lane");
   const float4* ks = static_cast<const float4*>(dev.k_src);
   const float4* vs = static_cast<const float4*>(dev.v_src);
-  float4 kx[kItemsPerLane][2], vx[kItemsPerLane][2];
-  Item im[kItemsPerLane];
-#pragma unroll
-  for (int u = 0; u < kItemsPerLane; ++u) {
-    im[u] = item(t, u, h, H, D);
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      kx[u][p] = im[u].ok ? ks[im[u].src / 4 + p] : make_float4(0.f, 0.f, 0.f, 0.f);
-      vx[u][p] = im[u].ok ? vs[im[u].src / 4 + p] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
+  const Item i0 = item(t, 0, h, H, D), i1 = item(t, 1, h, H, D), i2 = item(t, 2, h, H, D),
+             i3 = item(t, 3, h, H, D);
+  const float4 k0a = ks[i0.src / 4], k0b = ks[i0.src / 4 + 1], k1a = ks[i1.src / 4], k1b = ks[i1.src / 4 + 1];
+  const float4 k2a = ks[i2.src / 4], k2b = ks[i2.src / 4 + 1], k3a = ks[i3.src / 4], k3b = ks[i3.src / 4 + 1];
+  const float4 v0a = vs[i0.src / 4], v0b = vs[i0.src / 4 + 1], v1a = vs[i1.src / 4], v1b = vs[i1.src / 4 + 1];
+  const float4 v2a = vs[i2.src / 4], v2b = vs[i2.src / 4 + 1], v3a = vs[i3.src / 4], v3b = vs[i3.src / 4 + 1];
   float4* kslab = reinterpret_cast<float4*>(static_cast<char*>(dev.k_pages) + (long(t.page) * H + h) * pb);
   float4* vslab = reinterpret_cast<float4*>(static_cast<char*>(dev.v_pages) + (long(t.page) * H + h) * pb);
-#pragma unroll
-  for (int u = 0; u < kItemsPerLane; ++u) {
-    if (!im[u].ok) continue;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      kslab[index_f32(im[u].slot, im[u].c0, D) / 4 + p] = kx[u][p];
-      vslab[index_f32(im[u].slot, im[u].c0, D) / 4 + p] = vx[u][p];
-    }
-  }
+  auto put = [&](const Item& im, const float4& ka, const float4& kb, const float4& va, const float4& vb) {
+    if (!im.ok) return;
+    const long o = index_f32(im.slot, im.c0, D) / 4;
+    kslab[o] = ka;
+    kslab[o + 1] = kb;
+    vslab[o] = va;
+    vslab[o + 1] = vb;
+  };
+  put(i0, k0a, k0b, v0a, v0b);
+  put(i1, k1a, k1b, v1a, v1b);
+  put(i2, k2a, k2b, v2a, v2b);
+  put(i3, k3a, k3b, v3a, v3b);
 }
 
 // FP8 pool, fp32 source: the head's values stay in registers while the wave
@@ -121,15 +130,16 @@ __device__ void write_fp8(const PoolDevice& dev, const PoolTask& t, int h, int H
     im[u] = item(t, u, h, H, D);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const float4 a = im[u].ok ? ks[im[u].src / 4 + p] : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 b = im[u].ok ? vs[im[u].src / 4 + p] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 a = ks[im[u].src / 4 + p];
+      const float4 b = vs[im[u].src / 4 + p];
       kx[u][4 * p + 0] = a.x; kx[u][4 * p + 1] = a.y; kx[u][4 * p + 2] = a.z; kx[u][4 * p + 3] = a.w;
       vx[u][4 * p + 0] = b.x; vx[u][4 * p + 1] = b.y; vx[u][4 * p + 2] = b.z; vx[u][4 * p + 3] = b.w;
     }
+    // items past the task's tokens hold another item's values: not in the amax
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      ak = fmaxf(ak, fabsf(kx[u][i]));
-      av = fmaxf(av, fabsf(vx[u][i]));
+      ak = fmaxf(ak, im[u].ok ? fabsf(kx[u][i]) : 0.0f);
+      av = fmaxf(av, im[u].ok ? fabsf(vx[u][i]) : 0.0f);
     }
   }
   const long sidx = long(t.page) * H + h;
@@ -203,16 +213,16 @@ __device__ void write_fp8mx(const PoolDevice& dev, const PoolTask& t, int h, int
     float kx[8], vx[8];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const float4 a = im.ok ? ks[im.src / 4 + p] : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 b = im.ok ? vs[im.src / 4 + p] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 a = ks[im.src / 4 + p];
+      const float4 b = vs[im.src / 4 + p];
       kx[4 * p + 0] = a.x; kx[4 * p + 1] = a.y; kx[4 * p + 2] = a.z; kx[4 * p + 3] = a.w;
       vx[4 * p + 0] = b.x; vx[4 * p + 1] = b.y; vx[4 * p + 2] = b.z; vx[4 * p + 3] = b.w;
     }
     float ak = 0.0f, av = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      ak = fmaxf(ak, fabsf(kx[i]));
-      av = fmaxf(av, fabsf(vx[i]));
+      ak = fmaxf(ak, im.ok ? fabsf(kx[i]) : 0.0f);
+      av = fmaxf(av, im.ok ? fabsf(vx[i]) : 0.0f);
     }
 #pragma unroll
     for (int o = 1; o < 8; o <<= 1) {
