@@ -200,6 +200,7 @@ __device__ void write_fp8(const PoolDevice& dev, const PoolTask& t, int h, int H
 // 64-channel tile (consecutive items, 8-aligned) reduce its amax by
 // shuffles, and the tile's first lane writes the exponent byte.
 __device__ void write_fp8mx(const PoolDevice& dev, const PoolTask& t, int h, int H, int D, long pb) {
+  static_assert(kItemsPerLane == 4, "four named items per lane");
   const float4* ks = static_cast<const float4*>(dev.k_src);
   const float4* vs = static_cast<const float4*>(dev.v_src);
   const int G = D / 64;
@@ -207,17 +208,18 @@ __device__ void write_fp8mx(const PoolDevice& dev, const PoolTask& t, int h, int
   unsigned char* vslab = static_cast<unsigned char*>(dev.v_pages) + (long(t.page) * H + h) * pb;
   unsigned char* kexp = static_cast<unsigned char*>(dev.k_scale) + (long(t.page) * H + h) * 16 * G;
   unsigned char* vexp = static_cast<unsigned char*>(dev.v_scale) + (long(t.page) * H + h) * 16 * G;
-#pragma unroll
-  for (int u = 0; u < kItemsPerLane; ++u) {
-    const Item im = item(t, u, h, H, D);
-    float kx[8], vx[8];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const float4 a = ks[im.src / 4 + p];
-      const float4 b = vs[im.src / 4 + p];
-      kx[4 * p + 0] = a.x; kx[4 * p + 1] = a.y; kx[4 * p + 2] = a.z; kx[4 * p + 3] = a.w;
-      vx[4 * p + 0] = b.x; vx[4 * p + 1] = b.y; vx[4 * p + 2] = b.z; vx[4 * p + 3] = b.w;
-    }
+  // every item's source values are loaded before the first one is encoded
+  // (encoding an item before the next item's loads issued made each lane's
+  // loads wait for one another)
+  const Item i0 = item(t, 0, h, H, D), i1 = item(t, 1, h, H, D), i2 = item(t, 2, h, H, D),
+             i3 = item(t, 3, h, H, D);
+  const float4 k0a = ks[i0.src / 4], k0b = ks[i0.src / 4 + 1], k1a = ks[i1.src / 4], k1b = ks[i1.src / 4 + 1];
+  const float4 k2a = ks[i2.src / 4], k2b = ks[i2.src / 4 + 1], k3a = ks[i3.src / 4], k3b = ks[i3.src / 4 + 1];
+  const float4 v0a = vs[i0.src / 4], v0b = vs[i0.src / 4 + 1], v1a = vs[i1.src / 4], v1b = vs[i1.src / 4 + 1];
+  const float4 v2a = vs[i2.src / 4], v2b = vs[i2.src / 4 + 1], v3a = vs[i3.src / 4], v3b = vs[i3.src / 4 + 1];
+  auto put = [&](const Item& im, const float4& ka, const float4& kb, const float4& va, const float4& vb) {
+    const float kx[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+    const float vx[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
     float ak = 0.0f, av = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -229,7 +231,7 @@ __device__ void write_fp8mx(const PoolDevice& dev, const PoolTask& t, int h, int
       ak = fmaxf(ak, __shfl_xor(ak, o, 64));
       av = fmaxf(av, __shfl_xor(av, o, 64));
     }
-    if (!im.ok) continue;
+    if (!im.ok) return;
     const int ek = tile_exponent_byte(ak), ev = tile_exponent_byte(av);
     const float ik = ldexpf(1.0f, 127 - ek), iv = ldexpf(1.0f, 127 - ev);
     unsigned lo = 0, hi = 0;
@@ -245,7 +247,11 @@ __device__ void write_fp8mx(const PoolDevice& dev, const PoolTask& t, int h, int
       kexp[im.slot * G + im.c0 / 64] = static_cast<unsigned char>(ek);
       vexp[im.slot * G + im.c0 / 64] = static_cast<unsigned char>(ev);
     }
-  }
+  };
+  put(i0, k0a, k0b, v0a, v0b);
+  put(i1, k1a, k1b, v1a, v1b);
+  put(i2, k2a, k2b, v2a, v2b);
+  put(i3, k3a, k3b, v3a, v3b);
 }
 
 // Block (task, y) handles KV heads 4y .. 4y+3 of its task, one wave per head.
