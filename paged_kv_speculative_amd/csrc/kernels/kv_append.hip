@@ -269,9 +269,26 @@ __global__ __launch_bounds__(kThreads) void pool_update_kernel(PoolDevice dev, P
     const uint4* sv = reinterpret_cast<const uint4*>(static_cast<const char*>(dev.v_pages) + so);
     uint4* dk = reinterpret_cast<uint4*>(static_cast<char*>(dev.k_pages) + dO);
     uint4* dv = reinterpret_cast<uint4*>(static_cast<char*>(dev.v_pages) + dO);
-    for (long i = threadIdx.x; i < n16; i += kThreads) {
-      dk[i] = sk[i];
-      dv[i] = sv[i];
+    // four 16-byte chunks of K and of V per thread per round, all loaded
+    // before any is stored (named values: see write_bf16)
+    for (long i0 = threadIdx.x; i0 < n16; i0 += 4 * kThreads) {
+      const long i1 = i0 + kThreads, i2 = i0 + 2 * kThreads, i3 = i0 + 3 * kThreads, last = n16 - 1;
+      const uint4 k0 = sk[i0], k1 = sk[min(i1, last)], k2 = sk[min(i2, last)], k3 = sk[min(i3, last)];
+      const uint4 v0 = sv[i0], v1 = sv[min(i1, last)], v2 = sv[min(i2, last)], v3 = sv[min(i3, last)];
+      dk[i0] = k0;
+      dv[i0] = v0;
+      if (i1 < n16) {
+        dk[i1] = k1;
+        dv[i1] = v1;
+      }
+      if (i2 < n16) {
+        dk[i2] = k2;
+        dv[i2] = v2;
+      }
+      if (i3 < n16) {
+        dk[i3] = k3;
+        dv[i3] = v3;
+      }
     }
     if (batch.kv_dtype == PKV_FP8_E4M3 && int(threadIdx.x) < nh) {
       const int h = h0 + threadIdx.x;
