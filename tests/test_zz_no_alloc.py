@@ -32,9 +32,11 @@ def _static(g, outputs=None, **kw):
                                         anc_mask=g.anc, sm_scale=w.sm_scale, **kw)
 
 
-def _case(cfg, small=True, batch=None, **kw):
+def _case(cfg, small=True, batch=None, kv=None, **kw):
     w = wl.make(cfg, small=small, batch=batch)
-    print(f"no-alloc cfg {cfg} small={small} B={w.batch} {kw}", flush=True)
+    if kv is not None:
+        w.kv_dtype = kv
+    print(f"no-alloc cfg {cfg} small={small} B={w.batch} kv={w.kv_dtype} {kw}", flush=True)
     g = H.GpuSide(w)
     O_ws, L_ws = (x.clone() for x in g.verify(**kw))
     O_st, L_st = _static(g, **kw)
@@ -53,6 +55,18 @@ def test_static_scratch_matches_workspace_on_shrinking_calls():
         if c["cfg"] == 5:
             kw["shared_prefix_pages"] = wl.make(5, small=True).prefix_len // 16
         w, O, L = _case(c["cfg"], batch=c.get("batch"), **kw)
+        O_ref, L_ref = H.oracle_verify(w, range(w.batch))
+        H.compare(O, L, O_ref, L_ref, H.TOL[w.kv_dtype])
+
+
+def test_static_scratch_fp8_cascade():
+    """The cascade over FP8 pages (per-page scales) through the static
+    scratch, then a smaller plain call that finds its partials there."""
+    pages = wl.make(5, small=True).prefix_len // 16
+    for c in (dict(cfg=5, kv="fp8", shared_prefix_pages=pages),
+              dict(cfg=5, kv="fp8", shared_prefix_pages=pages, num_splits=7),
+              dict(cfg=2, batch=2)):
+        w, O, L = _case(**c)
         O_ref, L_ref = H.oracle_verify(w, range(w.batch))
         H.compare(O, L, O_ref, L_ref, H.TOL[w.kv_dtype])
 
