@@ -51,10 +51,12 @@ def test_cascade_full_size_sampled():
     H.compare(O[sample], L[sample], O_ref, L_ref, H.TOL["bf16"])
 
 
-def test_cascade_with_per_sequence_counts():
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_cascade_with_per_sequence_counts(kv):
     """Per-sequence slot counts with the cascade: only slots i < n_b are
     computed and written."""
     w = wl.make(5, small=True)
+    w.kv_dtype = kv
     g = H.GpuSide(w)
     nq = torch.tensor([5, 1, 3, 5, 2, 4][:w.batch], dtype=torch.int32, device="cuda")
     from paged_kv_speculative_amd import VerifyBuffers
@@ -71,27 +73,30 @@ def test_cascade_with_per_sequence_counts():
         n_b = int(nq[b])
         K, V = H.oracle_sequence_kv(w, b)
         Or, Lr = oa.verify_attention(qf[b:b + 1, :n_b], [K], [V], n_b, None, float(w.sm_scale))
-        H.compare(O[b:b + 1, :n_b], L[b:b + 1, :n_b], Or, Lr, H.TOL["bf16"])
+        H.compare(O[b:b + 1, :n_b], L[b:b + 1, :n_b], Or, Lr, H.TOL[kv])
         assert np.all(O[b, n_b:] == 7.0)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
 @pytest.mark.parametrize("splits", [0, 5])
-def test_cascade_with_batch_slots(splits):
+def test_cascade_with_batch_slots(splits, kv):
     """A permuted subset of the pool's rows (batch_slots) with the cascade:
     the prefix pass reads the shared pages through the first listed row (not
     row 0), and every listed sequence matches the oracle."""
     w = wl.make(5, small=True)
+    w.kv_dtype = kv
     g = H.GpuSide(w)
     rows = [w.batch - 1, 0, w.batch // 2]
     slots = torch.tensor(rows, dtype=torch.int32, device="cuda")
     q = g.q[rows].contiguous()
     from paged_kv_speculative_amd import spec_verify_attention
     O, L = spec_verify_attention(q, g.pool.k_pages, g.pool.v_pages, g.pool.block_table, g.pool.seq_lens,
-                                 n_q=w.n_q, num_kv_heads=w.num_kv_heads, kv_dtype="bf16", batch_slots=slots,
+                                 n_q=w.n_q, num_kv_heads=w.num_kv_heads, kv_dtype=kv, batch_slots=slots,
+                                 k_scale=g.pool.k_scale, v_scale=g.pool.v_scale,
                                  sm_scale=w.sm_scale, num_splits=splits,
                                  shared_prefix_pages=w.prefix_len // 16)
     O_ref, L_ref = H.oracle_verify(w, rows)
-    H.compare(O.cpu().numpy(), L.cpu().numpy(), O_ref, L_ref, H.TOL["bf16"])
+    H.compare(O.cpu().numpy(), L.cpu().numpy(), O_ref, L_ref, H.TOL[kv])
 
 
 def _fp8(w, kv="fp8"):
