@@ -34,9 +34,8 @@ __device__ inline float wave_max(float v) {
 
 // Item it of a task (token it / G, channel group it % G) for the calling lane.
 // An item past the task's tokens reads the task's first source row instead
-// (valid whenever the task has tokens) and stores nothing: every source load
-// is then issued unconditionally, all of a lane's loads back to back (loads
-// behind a branch were issued one at a time, each waited for).
+// (valid whenever the task has tokens) and stores nothing, so every source
+// load is unconditional and a lane's loads can all be in flight at once.
 struct Item {
   bool ok;
   int slot, c0;
@@ -73,14 +72,14 @@ __device__ void write_bf16(const PoolDevice& dev, const PoolTask& t, int h, int 
   auto put = [&](const Item& im, const uint4& kx, const uint4& vx) {
     if (!im.ok) return;
     *reinterpret_cast<uint4*>(kslab + 2 * k_index_bf16(im.slot, im.c0, D)) = kx;
-    auto v2 = [&](int i, unsigned w) {           // channels c0 + i, c0 + i + 1
+    auto put_pair = [&](int i, unsigned w) {     // channels c0 + i, c0 + i + 1
       vslab[v_index_bf16(im.slot, im.c0 + i)] = static_cast<unsigned short>(w);
       vslab[v_index_bf16(im.slot, im.c0 + i + 1)] = static_cast<unsigned short>(w >> 16);
     };
-    v2(0, vx.x);
-    v2(2, vx.y);
-    v2(4, vx.z);
-    v2(6, vx.w);
+    put_pair(0, vx.x);
+    put_pair(2, vx.y);
+    put_pair(4, vx.z);
+    put_pair(6, vx.w);
   };
   put(i0, k0, v0);
   put(i1, k1, v1);
