@@ -69,6 +69,9 @@ TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "prof
                                "verify_traffic_llama3-8b-layer.md")
 
 
+SAMPLE_EVERY = 4          # timed steps per sampled verification (and acceptance) timing
+
+
 def kernel_build_digest(sources):
     """sha256 over the given source files (repository-relative) followed by
     the hipcc flags the build script compiles the first of them with."""
@@ -257,6 +260,19 @@ def run_gpu(args, w, torch, api):
     nodes_host = [torch.empty((B, nq), dtype=torch.int32, pin_memory=True) for _ in range(2)]
     done = [torch.cuda.Event() for _ in range(2)]
 
+    # HIP events around the verification and the acceptance on every
+    # SAMPLE_EVERY-th timed step (each record holds the launch stream ~5 us and
+    # costs host time, which would otherwise be counted in every step): the
+    # verification on steps 0, 4, 8, ... after the warmup, the acceptance two
+    # steps later (on the first step when there are fewer than three)
+    acc_phase = min(SAMPLE_EVERY // 2, args.steps - 1)
+
+    def sampled_verify(s):
+        return s >= args.warmup and (s - args.warmup) % SAMPLE_EVERY == 0
+
+    def sampled_accept(s):
+        return s >= args.warmup and (s - args.warmup) % SAMPLE_EVERY == acc_phase
+
     def launch(s):
         """Steps 1-3 of step s (its instance's append, verification and
         acceptance) issued on the stream, ending with the accepted lengths'
@@ -266,7 +282,7 @@ def run_gpu(args, w, torch, api):
             I.append_call()
         I.lens += nq
         step_lens.append(I.lens.copy())
-        timed_v = (s - args.warmup) % 2 == 0         # sampled: each record holds the stream ~5 us
+        timed_v = sampled_verify(s)                   # sampled: each record holds the stream ~5 us
         if timed_v:
             ev[s][0].record(cur)
         if args.fused:
@@ -278,7 +294,7 @@ def run_gpu(args, w, torch, api):
         if timed_v:
             ev[s][1].record(cur)
         if I.accept or I.tree_accept:
-            timed_acc = s % 4 == 0                    # sampled: every event record costs host time
+            timed_acc = sampled_accept(s)
             if timed_acc:
                 acc_ev[s][0].record(cur)
             if I.tree_accept:
@@ -337,10 +353,10 @@ def run_gpu(args, w, torch, api):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     timed = range(args.warmup, total_steps)
-    attn_ms = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in timed if (s - args.warmup) % 2 == 0])
-    attn_bytes = np.array([kv_bytes(step_lens[s], w) for s in timed if (s - args.warmup) % 2 == 0],
+    attn_ms = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in timed if sampled_verify(s)])
+    attn_bytes = np.array([kv_bytes(step_lens[s], w) for s in timed if sampled_verify(s)],
                           dtype=np.float64)
-    acc_ms = (np.array([acc_ev[s][0].elapsed_time(acc_ev[s][1]) for s in timed if s % 4 == 0])
+    acc_ms = (np.array([acc_ev[s][0].elapsed_time(acc_ev[s][1]) for s in timed if sampled_accept(s)])
               if insts[0].accept or insts[0].tree_accept else None)
     res = {
         "wall_s": wall, "steps": args.steps, "instances": R,
