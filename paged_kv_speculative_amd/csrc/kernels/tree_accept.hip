@@ -248,8 +248,11 @@ __global__ __launch_bounds__(kThreads) void tree_decide_kernel(TreeParams P) {
   __shared__ float s_lt[kMaxNodes], s_ld[kMaxNodes];
   __shared__ float s_lz[kMaxNodes][kMaxNodes];   // [node][level - 1]
   __shared__ int s_bad;
-  // tree shape: parents and child counts
+  // tree shape: parents and child counts; wave 0 also loads lane c's draft
+  // token with its parent (independent loads, one round trip)
+  int x = -1;
   if (wave == 0) {
+    x = lane >= 1 && lane < P.n ? P.tokens[long(b) * P.n + lane] : -1;
     const int par = lane < P.n ? (lane == 0 ? -1 : P.parents[long(b) * P.n + lane]) : -2;
     const bool bad_par = lane < P.n && (lane == 0 ? P.parents[long(b) * P.n] != -1 : (par < 0 || par >= lane));
     s_par[lane] = par;
@@ -268,6 +271,20 @@ __global__ __launch_bounds__(kThreads) void tree_decide_kernel(TreeParams P) {
       dec[0] = -1;
     }
     return;
+  }
+  // wave 0, lane c: candidate c's parent, sibling rank and the two logits of
+  // its token, loaded before the normalisers are gathered (they depend on
+  // nothing else)
+  int u_c = 0, rank = 0;
+  float tx = 0.0f, dx = 0.0f;
+  const bool cand = wave == 0 && lane >= 1 && lane < P.n;
+  if (cand) {
+    u_c = s_par[lane];
+    for (int c = 1; c < lane; ++c) rank += s_par[c] == u_c;
+    if (x >= 0 && x < P.vocab) {
+      dx = drow(P, b, u_c)[x];
+      tx = trow(P, b, u_c)[x];
+    }
   }
   // normalisers of internal nodes and their residual masses: item
   // (u, 0) and (u, 1) are the target and draft rows, (u, 1 + j) level j;
@@ -288,14 +305,11 @@ __global__ __launch_bounds__(kThreads) void tree_decide_kernel(TreeParams P) {
   __syncthreads();
   if (wave != 0) return;
   bool acc = false;
-  if (lane >= 1 && lane < P.n) {
-    const int u = s_par[lane];
-    int rank = 0;
-    for (int c = 1; c < lane; ++c) rank += s_par[c] == u;
-    const int x = P.tokens[long(b) * P.n + lane];
+  if (cand) {
+    const int u = u_c;
     if (x >= 0 && x < P.vocab) {
-      const float lq = __builtin_fmaf(drow(P, b, u)[x], kLog2e, -s_ld[u]);
-      const float lp = advance_levels(__builtin_fmaf(trow(P, b, u)[x], kLog2e, -s_lt[u]), lq, s_lz[u], rank);
+      const float lq = __builtin_fmaf(dx, kLog2e, -s_ld[u]);
+      const float lp = advance_levels(__builtin_fmaf(tx, kLog2e, -s_lt[u]), lq, s_lz[u], rank);
       const float d = lp - lq;
       const float a = d >= 0.0f ? 1.0f : exp2_hw(d);
       const Philox4 r = philox4x32_10(0u, unsigned(b), step, unsigned(lane - 1) | (kPurposeAccept << 16),
