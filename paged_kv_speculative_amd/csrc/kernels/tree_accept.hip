@@ -248,6 +248,8 @@ __global__ __launch_bounds__(kThreads) void tree_decide_kernel(TreeParams P) {
   __shared__ float s_lt[kMaxNodes], s_ld[kMaxNodes];
   __shared__ float s_lz[kMaxNodes][kMaxNodes];   // [node][level - 1]
   __shared__ int s_bad;
+  __shared__ int s_items[2 * kMaxNodes];
+  __shared__ int s_nitems;
   // tree shape: parents and child counts; wave 0 also loads lane c's draft
   // token with its parent (independent loads, one round trip)
   int x = -1;
@@ -289,18 +291,63 @@ __global__ __launch_bounds__(kThreads) void tree_decide_kernel(TreeParams P) {
   // normalisers of internal nodes and their residual masses: item
   // (u, 0) and (u, 1) are the target and draft rows, (u, 1 + j) level j;
   // wave w takes items w, w + 4, ... (each a wave reduction)
-  const int items = P.n * (P.levels + 2);
-  for (int i = wave; i < items; i += kWaves) {
-    const int u = i / (P.levels + 2), q = i % (P.levels + 2);
+  const int per = P.levels + 2, items = P.n * per;
+  // an item is needed for internal nodes only, and a level only below the
+  // node's child count
+  auto needed = [&](int i) {
+    const int u = i / per, q = i % per;
+    return i < items && (q < 2 ? s_nkids[u] > 0 : q - 1 < s_nkids[u]);
+  };
+  // the first 64 partials of an item, every lane one: (max, sum) of a row's
+  // chunk or the mass of a level's chunk.  Loaded for two items before
+  // either is reduced, without branches (a loaded value copied at a branch
+  // merge was waited for there): lanes past the chunk count read a valid
+  // element and drop it afterwards.
+  auto raw_part = [&](int i) {
+    const int u = i / per, q = i % per;
+    const bool row = q < 2;
+    const int c = lane < (row ? P.chunks : P.zchunks) ? lane : 0;
+    const float* src = row ? reinterpret_cast<const float*>(P.stats + (long(b * P.n + u) * 2 + q) * P.chunks + c)
+                           : P.zpart + (long(b * P.n + u) * P.levels + (q - 2)) * P.zchunks + c;
+    return make_float2(src[0], src[row ? 1 : 0]);
+  };
+  auto finish_item = [&](int i, float2 r) {
+    const int u = i / per, q = i % per;
     if (q < 2) {
-      if (s_nkids[u] > 0) {
-        const float l = row_lse(P, b, u, q);
-        if (lane == 0) (q ? s_ld : s_lt)[u] = l;
-      }
-    } else if (q - 1 < s_nkids[u]) {
-      const float l = level_lz(P, b, u, q - 1);
-      if (lane == 0) s_lz[u][q - 2] = l;
+      const bool has = lane < P.chunks;
+      float m = has ? r.x : kNegInf, sm = has ? r.y : 0.0f;
+      const float2* st = P.stats + (long(b * P.n + u) * 2 + q) * P.chunks;
+      for (int c = lane + 64; c < P.chunks; c += 64) combine_ms(m, sm, st[c].x, st[c].y);
+      for (int o = 32; o > 0; o >>= 1) combine_ms(m, sm, __shfl_xor(m, o, 64), __shfl_xor(sm, o, 64));
+      if (lane == 0) (q ? s_ld : s_lt)[u] = m + log2_hw(sm);
+    } else {
+      float z = lane < P.zchunks ? r.x : 0.0f;
+      const float* zp = P.zpart + (long(b * P.n + u) * P.levels + (q - 2)) * P.zchunks;
+      for (int c = lane + 64; c < P.zchunks; c += 64) z += zp[c];
+      for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, 64);
+      if (lane == 0) s_lz[u][q - 2] = z > 0.0f ? log2_hw(z) : kNegInf;
     }
+  };
+  // wave 0 lists the needed items (at most 2n - 2: two rows per internal
+  // node and one level per extra child), then the waves take them two at a time
+  if (wave == 0) {
+    int cnt = 0;
+    for (int base = 0; base < items; base += 64) {
+      const bool pred = needed(base + lane);
+      const unsigned long long mask = __ballot(pred);
+      if (pred) s_items[cnt + __popcll(mask & ((1ull << lane) - 1ull))] = base + lane;
+      cnt += __popcll(mask);
+    }
+    if (lane == 0) s_nitems = cnt;
+  }
+  __syncthreads();
+  const int nit = s_nitems;
+  for (int k = wave; k < nit; k += 2 * kWaves) {
+    const int k2 = k + kWaves;
+    const int i1 = s_items[k], i2 = s_items[min(k2, nit - 1)];
+    const float2 r1 = raw_part(i1), r2 = raw_part(i2);
+    finish_item(i1, r1);
+    if (k2 < nit) finish_item(i2, r2);
   }
   __syncthreads();
   if (wave != 0) return;
