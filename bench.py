@@ -228,6 +228,11 @@ def run_gpu(args, w, torch, api):
     R = args.instances or max(2, int(np.ceil(1.2e9 / max(one, 1))))
     R = min(R, 8)
     insts = [Instance(w, -(-total_steps // R) + 1, torch, api, r) for r in range(R)]
+    # the accepted lengths (and tree nodes) of a step land in one of two pinned
+    # host buffers: the chain acceptance writes its lengths there itself
+    # (one prepared call per buffer), the tree acceptance's are copied
+    k_host = [torch.empty(B, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    nodes_host = [torch.empty((B, nq), dtype=torch.int32, pin_memory=True) for _ in range(2)]
     for I in insts:
         I.verify = I.pool.prepare_verify(I.q, nq, anc_mask=I.anc, sm_scale=w.sm_scale,
                                          shared_prefix_pages=cascade_pages(args, w))
@@ -237,7 +242,8 @@ def run_gpu(args, w, torch, api):
                 np.arange(B), I.q, I.knew.view(shp), I.vnew.view(shp), anc_mask=I.anc, sm_scale=w.sm_scale,
                 buffers=I.verify.buffers, shared_prefix_pages=cascade_pages(args, w))
         if I.accept:
-            I.accept_call = api.PreparedAccept(I.T, I.D, I.x, seed=12345)
+            I.accept_calls = [api.PreparedAccept(I.T, I.D, I.x, seed=12345, accepted_len_out=k_host[j])
+                              for j in range(2)]
             if args.graph:       # the captured launch reads its step counter from device memory
                 I.accept_graph_call = api.PreparedAccept(I.T, I.D, I.x, seed=12345, step_tensor=I.step_t)
         if I.tree_accept:
@@ -254,10 +260,7 @@ def run_gpu(args, w, torch, api):
     acc_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(total_steps)]
     step_lens, accepted = [], []
-    # the accepted lengths (and tree nodes) of a step land in one of two pinned
-    # buffers; `done` marks the end of the step's work on the stream
-    k_host = [torch.empty(B, dtype=torch.int32, pin_memory=True) for _ in range(2)]
-    nodes_host = [torch.empty((B, nq), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    # `done` marks the end of a step's work on the stream
     done = [torch.cuda.Event() for _ in range(2)]
 
     # HIP events around the verification and the acceptance on every
@@ -297,6 +300,7 @@ def run_gpu(args, w, torch, api):
             timed_acc = sampled_accept(s)
             if timed_acc:
                 acc_ev[s][0].record(cur)
+            k = None                                  # set where the lengths stay on the device
             if I.tree_accept:
                 k, nodes, _ = I.accept_call(step=s)
                 nodes_host[s % 2].copy_(nodes, non_blocking=True)
@@ -304,10 +308,11 @@ def run_gpu(args, w, torch, api):
                 I.graph_a.replay()                    # increments the step counter, then accepts
                 k = I.accept_graph_call.buffers.accepted_len
             else:
-                k, _ = I.accept_call(step=s)
+                I.accept_calls[s % 2](step=s)         # writes the lengths into k_host[s % 2]
             if timed_acc:
                 acc_ev[s][1].record(cur)
-            k_host[s % 2].copy_(k, non_blocking=True)  # host needs k (and the tokens) every step
+            if k is not None:
+                k_host[s % 2].copy_(k, non_blocking=True)  # host needs k every step
         done[s % 2].record(cur)
 
     def finish(s):
@@ -361,6 +366,7 @@ def run_gpu(args, w, torch, api):
     res = {
         "wall_s": wall, "steps": args.steps, "instances": R,
         "attn_ms": attn_ms, "attn_bytes": attn_bytes, "acc_ms": acc_ms,
+        "accept_direct": bool(insts[0].accept and not args.graph),
         "mean_k": float(np.mean([a.mean() for a in accepted[args.warmup:]])),
     }
     # a plain 1 GiB device-to-device copy, timed after the steps (outside the
@@ -546,6 +552,8 @@ def main():
         "scaling": "weak",
         "launch": ("hip-graph (verification, acceptance)" if args.graph else "eager")
                   + (", append fused into verification" if args.fused else "")
+                  + (", accepted lengths written to pinned host memory by the acceptance"
+                     if r["accept_direct"] else "")
                   + ("; one step at a time" if args.serial
                      else "; next instance's step queued while the host reads accepted lengths"),
         "vs_baseline": None,

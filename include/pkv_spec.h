@@ -357,7 +357,9 @@ typedef struct {
   const int32_t* draft_tokens;/* device [batch][gamma], values in [0, vocab)     */
   uint64_t seed;
   uint32_t step;
-  int32_t* accepted_len;      /* device [batch]                                  */
+  int32_t* accepted_len;      /* [batch]: device memory, or pinned host memory
+                                 (hipHostMalloc) that the kernels write directly;
+                                 each entry is stored once and never read back  */
   int32_t* next_token;        /* device [batch]                                  */
   void* workspace;            /* device, >= spec_accept_workspace_size bytes,
                                  16-byte aligned; scratch for per-chunk partial

@@ -496,7 +496,11 @@ class PreparedAccept:
     step from it when they run, so the launch can be captured in a graph."""
 
     def __init__(self, target_logits, draft_logits, draft_tokens, seed, buffers=None, gammas=None,
-                 step_tensor=None):
+                 step_tensor=None, accepted_len_out=None):
+        """accepted_len_out: optional int32 [batch] tensor the accepted lengths
+        are written to instead of buffers.accepted_len: device memory, or
+        pinned host memory, which the kernel then writes directly (no copy to
+        the host needed once the stream has passed the call)."""
         a = _accept_args(target_logits, draft_logits, draft_tokens, seed, 0, gammas)
         if step_tensor is not None:
             assert step_tensor.numel() == 1 and step_tensor.element_size() == 4
@@ -505,6 +509,14 @@ class PreparedAccept:
         if buffers is None:
             buffers = AcceptBuffers(a.batch, ws, target_logits.device)
         assert buffers.workspace.numel() >= ws
+        if accepted_len_out is not None:
+            if accepted_len_out.dtype != torch.int32 or accepted_len_out.numel() != a.batch:
+                raise ValueError("accepted_len_out must be int32 with one entry per sequence")
+            if not accepted_len_out.is_contiguous():
+                raise ValueError("accepted_len_out must be contiguous")
+            if not (accepted_len_out.is_cuda or accepted_len_out.is_pinned()):
+                raise ValueError("accepted_len_out must be device memory or pinned host memory")
+            buffers.accepted_len = accepted_len_out
         a.accepted_len, a.next_token = buffers.accepted_len.data_ptr(), buffers.next_token.data_ptr()
         a.workspace, a.workspace_bytes = buffers.workspace.data_ptr(), buffers.workspace.numel()
         self.args, self.buffers = a, buffers

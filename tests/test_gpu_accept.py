@@ -171,3 +171,24 @@ def test_prepared_accept_matches():
         k1, t1 = (a.clone() for a in call(step))
         k2, t2 = spec_accept(Tt, Dt, xt, 99, step)
         assert torch.equal(k1, k2) and torch.equal(t1, t2)
+
+
+def test_accepted_lengths_written_to_pinned_host_memory():
+    """accepted_len in pinned host memory: the kernels store the lengths there
+    directly; after the stream passes the call they equal the device-buffer
+    call's on several steps (workload-5 shapes, small)."""
+    from paged_kv_speculative_amd import PreparedAccept
+    w = wl.make(5, small=True)
+    T, D, x = w.accept_inputs(step=0)
+    Tt, Dt, xt = (torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (T, D, x))
+    host = torch.full((w.batch,), -7, dtype=torch.int32, pin_memory=True)
+    direct = PreparedAccept(Tt, Dt, xt, seed=4321, accepted_len_out=host)
+    plain = PreparedAccept(Tt, Dt, xt, seed=4321)
+    for step in (0, 3, 17):
+        direct(step)
+        k_dev, t_dev = (a.clone() for a in plain(step))
+        torch.cuda.synchronize()
+        assert torch.equal(host, k_dev.cpu())
+        assert torch.equal(direct.buffers.next_token, t_dev)
+    with pytest.raises(ValueError):
+        PreparedAccept(Tt, Dt, xt, seed=1, accepted_len_out=torch.zeros(w.batch, dtype=torch.int32))
