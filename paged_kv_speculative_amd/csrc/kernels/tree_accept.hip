@@ -201,6 +201,7 @@ __global__ __launch_bounds__(kLevelThreads) void tree_level_kernel(TreeParams P,
   const int u = __builtin_ctzll(rest);
   const int r = b * P.n + u;
   __shared__ float s_lz[kMaxNodes];
+  __shared__ float s_iz[kMaxNodes];              // 1 / Z_i of the earlier levels
   __shared__ float s_l[2];
   // the chunk's logits do not depend on the normalisers: their loads go out
   // first and are in flight while the normalisers are gathered
@@ -215,7 +216,10 @@ __global__ __launch_bounds__(kLevelThreads) void tree_level_kernel(TreeParams P,
   } else {
     for (int i = wave - 2; i < j - 1; i += kLevelWaves - 2) {
       const float l = level_lz(P, b, u, i + 1);
-      if (lane == 0) s_lz[i] = l;
+      if (lane == 0) {
+        s_lz[i] = l;
+        s_iz[i] = l > kNegInf ? exp2_hw(-l) : 1.0f;
+      }
     }
   }
   __syncthreads();
@@ -225,10 +229,13 @@ __global__ __launch_bounds__(kLevelThreads) void tree_level_kernel(TreeParams P,
   for (int qq = 0; qq < kLevelQuads; ++qq)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float lq = __builtin_fmaf(dv[qq][e], kLog2e, -ld);
-      const float lp = advance_levels(__builtin_fmaf(tv[qq][e], kLog2e, -lt), lq, s_lz, j - 1);
-      const float lr = residual_log(lp, lq);
-      s += lr > kNegInf ? exp2_hw(lr) : 0.0f;     // past the row: -inf
+      // in linear terms: P_0 and Q, P_i = max(0, P_{i-1} - Q) / Z_i through
+      // the earlier levels (unchanged where Z_i = 0), then this level's term
+      // max(0, P_{j-1} - Q); past the row both are 0
+      const float qv = exp2_hw(__builtin_fmaf(dv[qq][e], kLog2e, -ld));
+      float pv = exp2_hw(__builtin_fmaf(tv[qq][e], kLog2e, -lt));
+      for (int i = 0; i < j - 1; ++i) pv = s_lz[i] > kNegInf ? fmaxf(pv - qv, 0.0f) * s_iz[i] : pv;
+      s += fmaxf(pv - qv, 0.0f);
     }
   s = block_sum<kLevelWaves>(s);
   if (t == 0) P.zpart[(long(r) * P.levels + (j - 1)) * P.zchunks + chunk] = s;
