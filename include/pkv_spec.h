@@ -264,7 +264,8 @@ typedef struct {
   const int32_t* seq_lens;    /* device, total length N incl. the n_q tokens     */
   const int32_t* batch_slots; /* device [batch] rows to use, or NULL (row = b)   */
   const uint64_t* anc_mask;   /* device [batch][n_q] or NULL (chain)             */
-  float sm_scale;             /* usually 1/sqrt(head_dim)                        */
+  float sm_scale;             /* usually 1/sqrt(head_dim); positive and finite,
+                                 else PKV_ERR_INVALID_ARG                        */
   float* out;                 /* device [batch][n_q][Hq][head_dim] fp32          */
   float* lse;                 /* device [batch][n_q][Hq] fp32, may be NULL       */
   void* workspace;            /* device, >= spec_verify_workspace_size bytes;

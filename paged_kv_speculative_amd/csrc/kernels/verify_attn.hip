@@ -647,10 +647,8 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, const int*
       ksc *= M.ks;
       vsc = M.vs;
     }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sc[nt][e] *= ksc;
+    // the scores stay unscaled: ksc > 0, so the row maximum is taken on them
+    // and scaled once, and each weight is exp2(fma(score, ksc, -m))
 
     if (tok0 + 16 > L) {                         // page reaches the verification slots or the end
       const int N = M.n & kLenMask;
@@ -704,7 +702,7 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, const int*
     unsigned ph[NT][2], pl[NT][2], pm[PG][NT][2], pml[PG][NT][2];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const float mx = row_max4(fmaxf(fmaxf(sc[nt][0], sc[nt][1]), fmaxf(sc[nt][2], sc[nt][3])));
+      const float mx = row_max4(fmaxf(fmaxf(sc[nt][0], sc[nt][1]), fmaxf(sc[nt][2], sc[nt][3]))) * ksc;
       const bool grow = mx > m_run[nt] + kRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(grow)) {
         const float m_new = grow ? mx : m_run[nt];
@@ -717,7 +715,7 @@ __device__ void stream_range(const VerifyParams& P, const int* s_cum, const int*
       const float m_ref = m_run[nt] == kNegInf ? 0.0f : m_run[nt];
       float p[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = exp2_fast(sc[nt][e] - m_ref);
+      for (int e = 0; e < 4; ++e) p[e] = exp2_fast(fmaf(sc[nt][e], ksc, -m_ref));
       l_run[nt] += (p[0] + p[1]) + (p[2] + p[3]);
       if (MX) {
         // P = hi + lo as for bf16 KV; scaling by a power of two is exact, so
@@ -1643,6 +1641,8 @@ pkv_status check_args(const pkv_verify_args* a, Plan* pl) {
   if (a->page_size != kPageSize) return fail(PKV_ERR_UNSUPPORTED, "page_size must be 16");
   if (a->head_dim != 64 && a->head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (a->block_table_stride < 1) return fail(PKV_ERR_INVALID_ARG, "block_table_stride must be >= 1");
+  if (!(a->sm_scale > 0.0f) || !(a->sm_scale < INFINITY))
+    return fail(PKV_ERR_INVALID_ARG, "sm_scale must be positive and finite");
   if (!a->q || !a->k_pages || !a->v_pages || !a->block_table || !a->seq_lens)
     return fail(PKV_ERR_INVALID_ARG, "null device pointer");
   if (a->shared_prefix_pages < 0) return fail(PKV_ERR_INVALID_ARG, "shared_prefix_pages must be >= 0");

@@ -265,6 +265,7 @@ def test_argument_checks_of_newer_fields():
     a = _lib.VerifyArgs()
     a.batch, a.n_q, a.num_q_heads, a.num_kv_heads, a.head_dim, a.page_size = 2, 5, 8, 2, 128, 16
     a.q_dtype, a.kv_dtype = _lib.BF16, _lib.FP8_E4M3
+    a.sm_scale = 0.125
     a.q = a.k_pages = a.v_pages = a.block_table = a.seq_lens = a.k_scale = a.v_scale = 16
     a.block_table_stride = 8
     n = C.c_size_t()
@@ -274,6 +275,11 @@ def test_argument_checks_of_newer_fields():
     assert lib.spec_verify_workspace_size(C.byref(a), C.byref(n)) == 5       # per-64-channel scales: not
     a.kv_dtype, a.shared_prefix_pages = _lib.BF16, -1
     assert lib.spec_verify_workspace_size(C.byref(a), C.byref(n)) == 1
+    a.shared_prefix_pages, a.sm_scale = 0, 0.125
+    assert lib.spec_verify_workspace_size(C.byref(a), C.byref(n)) == 0
+    for bad in (0.0, -0.125, float("inf"), float("nan")):   # the softmax scale must be positive
+        a.sm_scale = bad
+        assert lib.spec_verify_workspace_size(C.byref(a), C.byref(n)) == 1, bad
     t = _lib.TreeAcceptArgs()
     t.batch, t.n_nodes, t.max_children, t.vocab = 2, 16, 4, 1000
     assert lib.spec_accept_tree_workspace_size(C.byref(t), C.byref(n)) == 0 and n.value > 0
